@@ -1,0 +1,322 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 hot path on one MI355X.
+
+One step = one pass over every row of the path, each on its own seeded
+synthetic workload:
+  decode_b1   the 27B-class dense layer at batch 1: five GEMVs (gate, up 5120->17408,
+              down 17408->5120, QKV 5120->7168, O 5120->5120), fp32 outputs
+  decode_b32  the same layer's weights at 32 decode tokens: five skinny GEMMs, bf16 outputs
+  moe         32 tokens through a 512-expert, top-10 MoE layer (hidden 2048, expert
+              width 512): route, group, gate/up + SwiGLU, down, scatter
+  prefill     a 512-token prompt through gate, up (5120->17408) and down (17408->5120)
+The headline `value` is the batch-1 layer's weight-stream rate in GB/s
+(algorithmic bytes: NVFP4 weights + x + y).  Weights are rotated over several
+device copies so that no copy is re-read before > 1 GiB of other traffic:
+the 256 MB Infinity Cache cannot serve repeats.
+
+Prints ONE JSON line on stdout; details go to stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
+MODEL_27B_BYTES_PER_TOKEN = 27e9 * 0.5625  # weights-only stream of a 27B NVFP4 model
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="target length of the oracle sample")
+    p.add_argument("--rows", default="decode_b1,decode_b32,moe,prefill")
+    p.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path runs on a single "
+              f"MI355X; see the multi-GPU design notes)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from bit_quantized_decode_amd import binding as B
+    from bit_quantized_decode_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    B.lib()
+    rows = set(args.rows.split(","))
+    t_setup = time.time()
+
+    def u8(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    # ---- the dense layer (batch 1 and batch 32 share weights) ----------------
+    layer = I.DENSE_LAYER
+    dense_copies = 4
+    packed = [[None] * len(layer) for _ in range(dense_copies)]
+    for j, mat in enumerate(layer):
+        c, s = I.nvfp4_matrix(I.DECODE_B1, mat.matrix_id, mat.n, mat.k)
+        p0 = B.pack(u8(c), u8(s))
+        for cp in range(dense_copies):
+            packed[cp][j] = p0 if cp == 0 else p0.clone()
+    x1 = [bf16(I.activations(I.DECODE_B1, m.matrix_id, 1, m.k)[0]) for m in layer]
+    y1 = [torch.empty(m.n, dtype=torch.float32, device=dev) for m in layer]
+    x32 = [bf16(I.activations(I.DECODE_B32, m.matrix_id, 32, m.k)) for m in layer]
+    y32 = [torch.empty((32, m.n), dtype=torch.bfloat16, device=dev) for m in layer]
+    ws_split = B.workspace(max(max(B.gemv_workspace_bytes(m.n, m.k), B.gemm_workspace_bytes(32, m.n, m.k))
+                               for m in layer), dev)
+    b1_bytes = sum(B.packed_bytes(m.n, m.k) + 2 * m.k + 4 * m.n for m in layer)
+    b1_weight_bytes = sum(B.packed_bytes(m.n, m.k) for m in layer)
+    b32_bytes = sum(B.packed_bytes(m.n, m.k) + 2 * 32 * m.k + 2 * 32 * m.n for m in layer)
+    b32_flops = sum(2 * 32 * m.n * m.k for m in layer)
+
+    # ---- MoE --------------------------------------------------------------
+    shape = I.MoeShape()
+    moe_pools = []
+    if "moe" in rows:
+        w = I.moe_weights(I.MOE_32T, shape)
+        stride_gu = B.packed_bytes(shape.inter, shape.hidden)
+        stride_d = B.packed_bytes(shape.hidden, shape.inter)
+
+        def pool(codes, scales, stride):
+            out = torch.empty(shape.experts * stride, dtype=torch.uint8, device=dev)
+            for e in range(shape.experts):
+                out[e * stride:(e + 1) * stride].copy_(B.pack(u8(codes[e]), u8(scales[e])))
+            return out
+
+        pg, pu, pd = (pool(w.gate_codes, w.gate_scales, stride_gu), pool(w.up_codes, w.up_scales, stride_gu),
+                      pool(w.down_codes, w.down_scales, stride_d))
+        moe_pools = [(pg, pu, pd), (pg.clone(), pu.clone(), pd.clone())]
+        moe_x = bf16(I.activations(I.MOE_32T, 0, shape.tokens, shape.hidden))
+        moe_logits = torch.from_numpy(I.router_logits(I.MOE_32T, shape.tokens, shape.experts, shape.zipf_s)).to(dev)
+        sts = [torch.from_numpy(a).to(dev) for a in (w.gate_st, w.up_st, w.down_st)]
+        moe_out = {}
+        moe_ws = B.workspace(B.moe_workspace_bytes(shape.tokens, shape.experts, shape.top_k, shape.hidden,
+                                                   shape.inter), dev, kind="moe")
+        del w
+
+    def run_moe(cp):
+        pg_, pu_, pd_ = moe_pools[cp]
+        return B.moe_grouped(moe_x, moe_logits, shape.top_k, pg_, pu_, pd_, stride_gu, stride_gu, stride_d,
+                             sts[0], sts[1], sts[2], shape.inter, y_dtype=torch.float32, ws=moe_ws,
+                             outputs=moe_out)
+
+    # ---- prefill ----------------------------------------------------------
+    pre = I.PREFILL_MATRICES
+    pre_copies = 2
+    pre_packed = [[None] * len(pre) for _ in range(pre_copies)]
+    pre_x, pre_y = [], []
+    if "prefill" in rows:
+        for j, mat in enumerate(pre):
+            c, s = I.nvfp4_matrix(I.PREFILL_512, mat.matrix_id, mat.n, mat.k)
+            p0 = B.pack(u8(c), u8(s))
+            for cp in range(pre_copies):
+                pre_packed[cp][j] = p0 if cp == 0 else p0.clone()
+            pre_x.append(bf16(I.activations(I.PREFILL_512, mat.matrix_id, 512, mat.k)))
+            pre_y.append(torch.empty((512, mat.n), dtype=torch.bfloat16, device=dev))
+    pre_flops = sum(2 * 512 * m.n * m.k for m in pre)
+    pre_bytes = sum(B.packed_bytes(m.n, m.k) + 2 * 512 * m.k + 2 * 512 * m.n for m in pre)
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t_setup:.1f}s")
+
+    # ---- one step: each row's launches, captured once per weight copy as a
+    # HIP graph and replayed (the launch cost stays off the GPU timeline) ------
+    def row_b1(cp):
+        for j, mat in enumerate(layer):
+            B.gemv(packed[cp][j], mat.n, mat.k, I.TENSOR_SCALE, x1[j], y=y1[j], ws=ws_split)
+
+    def row_b32(cp):
+        for j, mat in enumerate(layer):
+            B.gemm(packed[cp][j], mat.n, mat.k, I.TENSOR_SCALE, x32[j], y=y32[j], ws=ws_split)
+
+    def row_pre(cp):
+        for j, mat in enumerate(pre):
+            B.gemm(pre_packed[cp][j], mat.n, mat.k, I.TENSOR_SCALE, pre_x[j], y=pre_y[j], ws=ws_split)
+
+    plan = []   # (row name, callable(copy), copies, copy for step i, outputs to check)
+    if "decode_b1" in rows:
+        plan.append(("decode_b1", row_b1, dense_copies, lambda i: (2 * i) % dense_copies, y1))
+    if "decode_b32" in rows:
+        plan.append(("decode_b32", row_b32, dense_copies, lambda i: (2 * i + 1) % dense_copies, y32))
+    if "moe" in rows:
+        plan.append(("moe", run_moe, 2, lambda i: i % 2, None))
+    if "prefill" in rows:
+        plan.append(("prefill", row_pre, pre_copies, lambda i: i % pre_copies, pre_y))
+
+    # Eager reference outputs (copy 0), then capture.
+    eager = {}
+    for name, fn, ncp, _, outs in plan:
+        fn(0)
+        torch.cuda.synchronize()
+        eager[name] = [o.clone() for o in outs] if outs is not None else [moe_out["y"].clone()]
+    graphs = {}
+    if not args.eager:
+        for name, fn, ncp, _, _ in plan:
+            for cp in range(ncp):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    fn(cp)
+                graphs[(name, cp)] = g
+        torch.cuda.synchronize()
+        # Every graph's replay must reproduce the eager result bit for bit.
+        for name, fn, ncp, _, outs in plan:
+            for cp in range(ncp):
+                graphs[(name, cp)].replay()
+                torch.cuda.synchronize()
+                got = [o for o in outs] if outs is not None else [moe_out["y"]]
+                for a_, b_ in zip(got, eager[name]):
+                    if not torch.equal(a_.view(torch.uint8), b_.view(torch.uint8)):
+                        raise SystemExit(f"graph replay of {name} (copy {cp}) differs from the eager run")
+        log(f"captured {len(graphs)} graphs; replays match the eager runs")
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(i):
+        marks = {}
+        for name, fn, ncp, pick, _ in plan:
+            a = ev()
+            b = ev()
+            a.record()
+            if args.eager:
+                fn(pick(i))
+            else:
+                graphs[(name, pick(i))].replay()
+            b.record()
+            marks[name] = (a, b)
+        return marks
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log("warmup done")
+    all_marks = []
+    t0 = ev(); t1 = ev()
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(args.steps):
+        all_marks.append(step(args.warmup + i))
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms_per_step = total_ms / args.steps
+    seg = {}
+    for name in all_marks[0]:
+        seg[name] = sum(m[name][0].elapsed_time(m[name][1]) for m in all_marks) / args.steps
+    gemv_launches = args.steps * len(layer) if "decode_b1" in seg else 0
+    gemv_ms = seg.get("decode_b1", 0.0) * args.steps
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step; segments (ms): "
+        + ", ".join(f"{k}={v:.4f}" for k, v in seg.items()))
+
+    # ---- per-row results --------------------------------------------------
+    result_rows = {}
+    if "decode_b1" in seg:
+        s = seg["decode_b1"] * 1e-3
+        result_rows["decode_b1"] = {"GB/s": b1_bytes / s / 1e9, "weight_GB/s": b1_weight_bytes / s / 1e9,
+                                    "us": s * 1e6, "frac_hbm": b1_bytes / s / 1e9 / HBM_PEAK_GBS,
+                                    "equiv_tok_s": b1_bytes / s / MODEL_27B_BYTES_PER_TOKEN}
+    if "decode_b32" in seg:
+        s = seg["decode_b32"] * 1e-3
+        result_rows["decode_b32"] = {"GB/s": b32_bytes / s / 1e9, "TFLOP/s": b32_flops / s / 1e12, "us": s * 1e6,
+                                     "frac_hbm": b32_bytes / s / 1e9 / HBM_PEAK_GBS,
+                                     "equiv_tok_s": 32 * b32_bytes / s / MODEL_27B_BYTES_PER_TOKEN}
+    if "moe" in seg:
+        s = seg["moe"] * 1e-3
+        counts = moe_out["expert_counts"].cpu().numpy()
+        active = int((counts > 0).sum())
+        per_expert = 3 * B.packed_bytes(shape.inter, shape.hidden)
+        moe_bytes = (active * per_expert + 2 * shape.tokens * shape.hidden + 4 * shape.tokens * shape.experts
+                     + 4 * shape.tokens * shape.hidden + 8 * shape.tokens * shape.top_k)
+        result_rows["moe"] = {"GB/s": moe_bytes / s / 1e9, "us": s * 1e6, "active_experts": active,
+                              "algorithmic_bytes": moe_bytes, "frac_hbm": moe_bytes / s / 1e9 / HBM_PEAK_GBS,
+                              "layer_tok_s": shape.tokens / s, "max_tokens_per_expert": int(counts.max())}
+    if "prefill" in seg:
+        s = seg["prefill"] * 1e-3
+        result_rows["prefill"] = {"TFLOP/s": pre_flops / s / 1e12, "us": s * 1e6,
+                                  "frac_mfma_bf16": pre_flops / s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                                  "GB/s": pre_bytes / s / 1e9, "equiv_tok_s": pre_flops / s / (2 * 27e9)}
+
+    roofline = None
+    if gemv_launches:
+        bytes_per_launch = b1_bytes * args.steps / gemv_launches
+        avg_launch_s = gemv_ms * 1e-3 / gemv_launches
+        achieved = bytes_per_launch / avg_launch_s / 1e9
+        roofline = {"kernel": "gemv_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": None, "avg_launch_us": round(avg_launch_s * 1e6, 3),
+                    "bytes_per_launch": int(bytes_per_launch)}
+
+    cpu = None
+    if not args.no_cpu_baseline and "decode_b1" in rows:
+        cpu = cpu_baseline(args.cpu_seconds)
+
+    value = result_rows.get("decode_b1", {}).get("GB/s")
+    out = {
+        "metric": "NVFP4 GEMV weight GB/s (% HBM peak) at B=1/32; MoE GB/s; prefill TFLOP/s",
+        "value": round(value, 1) if value else None,
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "nvfp4 weights x bf16 activations, fp32 accumulate",
+        "data": "synthetic (seeded NVFP4 codes/scales, N(0,1) bf16 activations, Zipf-biased router logits)",
+        "config": {"workload": "27B-class dense decode layer, batch 1: NVFP4 GEMVs gate/up 5120->17408, "
+                               "down 17408->5120, QKV 5120->7168, O 5120->5120",
+                   "batch": 1, "algorithmic_bytes_per_step": b1_bytes},
+        "rows": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                 for k, v in result_rows.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(target_s):
+    """The oracle, untuned, on this host's cores: the batch-1 layer's five GEMVs, repeated
+    until about `target_s` seconds of work, reported in the same unit (GB/s)."""
+    import numpy as np
+
+    import oracle
+    from bit_quantized_decode_amd import inputs as I
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    mats = [(m, *I.nvfp4_matrix(I.DECODE_B1, m.matrix_id, m.n, m.k)) for m in I.DENSE_LAYER]
+    xs = [I.activations(I.DECODE_B1, m.matrix_id, 1, m.k) for m in I.DENSE_LAYER]
+    layer_bytes = sum(m.n * m.k * 9 // 16 + 2 * m.k + 4 * m.n for m in I.DENSE_LAYER)
+    oracle.gemm(mats[4][1], mats[4][2], I.TENSOR_SCALE, xs[4], nthreads=cores)  # warm-up
+    reps, t0 = 0, time.time()
+    while True:
+        for (m, c, s), x in zip(mats, xs):
+            oracle.gemm(c, s, I.TENSOR_SCALE, x, nthreads=cores)
+        reps += 1
+        if time.time() - t0 >= target_s or reps >= 200:
+            break
+    dt = time.time() - t0
+    log(f"cpu baseline: {reps} passes of the layer in {dt:.1f}s on {cores} threads")
+    return {"value": round(reps * layer_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} full passes of the batch-1 layer (5 GEMVs, 330,301,440 weights) in fp64, "
+                      f"{dt:.1f} s wall"}
+
+
+if __name__ == "__main__":
+    main()

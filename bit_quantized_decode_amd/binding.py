@@ -1,0 +1,238 @@
+"""Python binding of libnvfp4.so: the functions of include/nvfp4.h, same names.
+
+Argument marshalling only: torch tensors supply device memory and the current
+stream; every step of the computation runs in the library's HIP kernels.  If
+the library is not built, every call raises -- there is no fallback path.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+NVFP4_OK = 0
+NVFP4_ERR_NULL = 1
+NVFP4_ERR_SHAPE = 2
+NVFP4_ERR_ALIGN = 3
+NVFP4_ERR_DTYPE = 4
+NVFP4_ERR_WORKSPACE = 5
+NVFP4_ERR_ARG = 6
+NVFP4_ERR_HIP = 7
+NVFP4_F32 = 0
+NVFP4_BF16 = 1
+
+EXPORTED = (
+    "nvfp4_abi_version", "nvfp4_status_str", "nvfp4_last_error", "nvfp4_packed_bytes", "nvfp4_pack",
+    "nvfp4_unpack", "nvfp4_gemv_workspace_bytes", "nvfp4_gemv", "nvfp4_gemm_workspace_bytes", "nvfp4_gemm",
+    "nvfp4_moe_workspace_bytes", "nvfp4_moe_grouped",
+)
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(message)
+        self.status = status
+
+
+class MoeArgs(ctypes.Structure):
+    """Mirror of struct nvfp4_moe_args."""
+    _fields_ = [
+        ("tokens", ctypes.c_int64), ("experts", ctypes.c_int64), ("top_k", ctypes.c_int64),
+        ("hidden", ctypes.c_int64), ("inter", ctypes.c_int64),
+        ("x", ctypes.c_void_p), ("router_logits", ctypes.c_void_p),
+        ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+        ("stride_gate", ctypes.c_size_t), ("stride_up", ctypes.c_size_t), ("stride_down", ctypes.c_size_t),
+        ("scale_gate", ctypes.c_void_p), ("scale_up", ctypes.c_void_p), ("scale_down", ctypes.c_void_p),
+        ("y", ctypes.c_void_p), ("y_dtype", ctypes.c_int),
+        ("topk_ids", ctypes.c_void_p), ("topk_weights", ctypes.c_void_p),
+        ("expert_counts", ctypes.c_void_p), ("expert_offsets", ctypes.c_void_p), ("perm", ctypes.c_void_p),
+        ("dbg_gate", ctypes.c_void_p), ("dbg_up", ctypes.c_void_p), ("dbg_h", ctypes.c_void_p),
+        ("dbg_down", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m bit_quantized_decode_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i64, sz, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+    sig = {
+        "nvfp4_abi_version": (I, []),
+        "nvfp4_status_str": (ctypes.c_char_p, [I]),
+        "nvfp4_last_error": (ctypes.c_char_p, []),
+        "nvfp4_packed_bytes": (I, [i64, i64, ctypes.POINTER(sz)]),
+        "nvfp4_pack": (I, [P, P, i64, i64, P, P]),
+        "nvfp4_unpack": (I, [P, i64, i64, P, P, P]),
+        "nvfp4_gemv_workspace_bytes": (I, [i64, i64, ctypes.POINTER(sz)]),
+        "nvfp4_gemv": (I, [P, i64, i64, ctypes.c_float, P, P, P, sz, P]),
+        "nvfp4_gemm_workspace_bytes": (I, [i64, i64, i64, ctypes.POINTER(sz)]),
+        "nvfp4_gemm": (I, [P, i64, i64, ctypes.c_float, P, i64, i64, P, i64, I, P, sz, P]),
+        "nvfp4_moe_workspace_bytes": (I, [ctypes.POINTER(MoeArgs), ctypes.POINTER(sz)]),
+        "nvfp4_moe_grouped": (I, [ctypes.POINTER(MoeArgs), P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def check(status):
+    if status != NVFP4_OK:
+        L = lib()
+        raise Nvfp4Error(status, f"{L.nvfp4_status_str(status).decode()}: {L.nvfp4_last_error().decode()}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# Zero-initialised workspaces, one per (device, kind), reused across calls in
+# stream order.  "split" serves the GEMV / GEMM split-K reductions, whose
+# counters every call leaves at zero; "moe" holds the MoE intermediates.  The
+# two kinds never share memory, so MoE scratch cannot disturb the counters.
+_workspaces = {}
+
+
+def workspace(nbytes, device, kind="split"):
+    if nbytes == 0:
+        return None
+    key = (str(device), kind)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def abi_version():
+    return lib().nvfp4_abi_version()
+
+
+def packed_bytes(n, k):
+    out = ctypes.c_size_t()
+    check(lib().nvfp4_packed_bytes(n, k, ctypes.byref(out)))
+    return out.value
+
+
+def pack(codes, scales, stream=None):
+    """codes uint8 [n][k/2], scales uint8 [n][k/16] (device) -> packed uint8 buffer."""
+    n, kh = codes.shape
+    k = 2 * kh
+    packed = torch.empty(packed_bytes(n, k), dtype=torch.uint8, device=codes.device)
+    check(lib().nvfp4_pack(_ptr(codes), _ptr(scales), n, k, _ptr(packed), _stream(stream)))
+    return packed
+
+
+def unpack(packed, n, k, stream=None):
+    codes = torch.empty((n, k // 2), dtype=torch.uint8, device=packed.device)
+    scales = torch.empty((n, k // 16), dtype=torch.uint8, device=packed.device)
+    check(lib().nvfp4_unpack(_ptr(packed), n, k, _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def gemv_workspace_bytes(n, k):
+    out = ctypes.c_size_t()
+    check(lib().nvfp4_gemv_workspace_bytes(n, k, ctypes.byref(out)))
+    return out.value
+
+
+def gemv(packed, n, k, tensor_scale, x, y=None, ws=None, stream=None):
+    """y[n] fp32 = s_t * W x, x bf16 [k] (device)."""
+    if y is None:
+        y = torch.empty(n, dtype=torch.float32, device=x.device)
+    need = gemv_workspace_bytes(n, k)
+    if ws is None:
+        ws = workspace(need, x.device)
+    check(lib().nvfp4_gemv(_ptr(packed), n, k, float(tensor_scale), _ptr(x), _ptr(y), _ptr(ws),
+                           0 if ws is None else ws.numel(), _stream(stream)))
+    return y
+
+
+def gemm_workspace_bytes(m, n, k):
+    out = ctypes.c_size_t()
+    check(lib().nvfp4_gemm_workspace_bytes(m, n, k, ctypes.byref(out)))
+    return out.value
+
+
+def gemm(packed, n, k, tensor_scale, x, y=None, y_dtype=torch.bfloat16, ws=None, stream=None):
+    """y[m][n] = s_t * x W^T, x bf16 [m][ldx] (device, row stride x.stride(0))."""
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=y_dtype, device=x.device)
+    dt = NVFP4_BF16 if y.dtype == torch.bfloat16 else NVFP4_F32
+    need = gemm_workspace_bytes(m, n, k)
+    if ws is None:
+        ws = workspace(need, x.device)
+    check(lib().nvfp4_gemm(_ptr(packed), n, k, float(tensor_scale), _ptr(x), m, x.stride(0), _ptr(y), y.stride(0),
+                           dt, _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    return y
+
+
+def moe_args(**kw):
+    a = MoeArgs()
+    for key, val in kw.items():
+        if isinstance(val, torch.Tensor):
+            val = val.data_ptr()
+        setattr(a, key, val)
+    return a
+
+
+def moe_workspace_bytes(tokens, experts, top_k, hidden, inter):
+    a = moe_args(tokens=tokens, experts=experts, top_k=top_k, hidden=hidden, inter=inter)
+    out = ctypes.c_size_t()
+    check(lib().nvfp4_moe_workspace_bytes(ctypes.byref(a), ctypes.byref(out)))
+    return out.value
+
+
+def moe_grouped(x, logits, top_k, w_gate, w_up, w_down, stride_gate, stride_up, stride_down,
+                scale_gate, scale_up, scale_down, inter, y_dtype=torch.float32, debug=False, ws=None,
+                outputs=None, stream=None):
+    """The routed expert layer.  Returns a dict of the outputs (see nvfp4_moe_grouped)."""
+    tokens, hidden = x.shape
+    experts = logits.shape[1]
+    dev = x.device
+    o = outputs if outputs is not None else {}
+    flat = tokens * top_k
+    o.setdefault("y", torch.empty((tokens, hidden), dtype=y_dtype, device=dev))
+    o.setdefault("topk_ids", torch.empty((tokens, top_k), dtype=torch.int32, device=dev))
+    o.setdefault("topk_weights", torch.empty((tokens, top_k), dtype=torch.float32, device=dev))
+    o.setdefault("expert_counts", torch.empty(experts, dtype=torch.int32, device=dev))
+    o.setdefault("expert_offsets", torch.empty(experts + 1, dtype=torch.int32, device=dev))
+    o.setdefault("perm", torch.empty(flat, dtype=torch.int32, device=dev))
+    if debug:
+        o.setdefault("dbg_gate", torch.empty((flat, inter), dtype=torch.float32, device=dev))
+        o.setdefault("dbg_up", torch.empty((flat, inter), dtype=torch.float32, device=dev))
+        o.setdefault("dbg_h", torch.empty((flat, inter), dtype=torch.bfloat16, device=dev))
+        o.setdefault("dbg_down", torch.empty((flat, hidden), dtype=torch.float32, device=dev))
+    if ws is None:
+        ws = workspace(moe_workspace_bytes(tokens, experts, top_k, hidden, inter), dev, kind="moe")
+    a = moe_args(
+        tokens=tokens, experts=experts, top_k=top_k, hidden=hidden, inter=inter, x=x, router_logits=logits,
+        w_gate=w_gate, w_up=w_up, w_down=w_down, stride_gate=stride_gate, stride_up=stride_up,
+        stride_down=stride_down, scale_gate=scale_gate, scale_up=scale_up, scale_down=scale_down,
+        y=o["y"], y_dtype=NVFP4_BF16 if o["y"].dtype == torch.bfloat16 else NVFP4_F32,
+        topk_ids=o["topk_ids"], topk_weights=o["topk_weights"], expert_counts=o["expert_counts"],
+        expert_offsets=o["expert_offsets"], perm=o["perm"],
+        dbg_gate=o.get("dbg_gate"), dbg_up=o.get("dbg_up"), dbg_h=o.get("dbg_h"), dbg_down=o.get("dbg_down"),
+        workspace=ws, workspace_bytes=0 if ws is None else ws.numel(),
+    )
+    check(lib().nvfp4_moe_grouped(ctypes.byref(a), _stream(stream)))
+    return o

@@ -1,0 +1,262 @@
+// The C ABI of libnvfp4.so (declared in include/nvfp4.h): argument
+// validation, status codes and dispatch to the kernel launchers.  Nothing here
+// allocates, frees or synchronises, and no exception leaves this file.
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "../../include/nvfp4.h"
+#include "launchers.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return NVFP4_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(NVFP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+
+int check_shape(int64_t n, int64_t k) {
+  if (n < 0 || k < 0) return fail(NVFP4_ERR_SHAPE, "negative size (n=%lld, k=%lld)", (long long)n, (long long)k);
+  if (k % 16 != 0) return fail(NVFP4_ERR_SHAPE, "k=%lld is not a multiple of 16 (one E4M3 scale per 16 k)", (long long)k);
+  if (n > kMaxDim || k > kMaxDim) return fail(NVFP4_ERR_SHAPE, "size above 2^30 (n=%lld, k=%lld)", (long long)n, (long long)k);
+  const nvfp4::Geometry g = nvfp4::geometry(n, k);
+  if (g.nkt > 0 && g.nrt > (int64_t(1) << 40) / (g.nkt * 9216)) return fail(NVFP4_ERR_SHAPE, "packed matrix too large");
+  return NVFP4_OK;
+}
+
+int check_rows(int64_t n) {
+  if (n > nvfp4::kMaxSplitRows)
+    return fail(NVFP4_ERR_SHAPE, "n=%lld above the %lld rows a product call supports", (long long)n,
+                (long long)nvfp4::kMaxSplitRows);
+  return NVFP4_OK;
+}
+
+#define NVFP4_TRY(expr)              \
+  do {                               \
+    int s_ = (expr);                 \
+    if (s_ != NVFP4_OK) return s_;   \
+  } while (0)
+
+#define NVFP4_GUARD_BEGIN try {
+#define NVFP4_GUARD_END                                                    \
+  }                                                                        \
+  catch (...) {                                                            \
+    return fail(NVFP4_ERR_ARG, "internal error: unexpected C++ exception"); \
+  }
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
+
+const char* nvfp4_status_str(int status) {
+  switch (status) {
+    case NVFP4_OK: return "NVFP4_OK";
+    case NVFP4_ERR_NULL: return "NVFP4_ERR_NULL";
+    case NVFP4_ERR_SHAPE: return "NVFP4_ERR_SHAPE";
+    case NVFP4_ERR_ALIGN: return "NVFP4_ERR_ALIGN";
+    case NVFP4_ERR_DTYPE: return "NVFP4_ERR_DTYPE";
+    case NVFP4_ERR_WORKSPACE: return "NVFP4_ERR_WORKSPACE";
+    case NVFP4_ERR_ARG: return "NVFP4_ERR_ARG";
+    case NVFP4_ERR_HIP: return "NVFP4_ERR_HIP";
+    default: return "unknown status";
+  }
+}
+
+const char* nvfp4_last_error(void) { return g_last_error; }
+
+int nvfp4_packed_bytes(int64_t n, int64_t k, size_t* bytes) {
+  NVFP4_GUARD_BEGIN
+  if (!bytes) return fail(NVFP4_ERR_NULL, "bytes is NULL");
+  NVFP4_TRY(check_shape(n, k));
+  *bytes = nvfp4::packed_bytes(nvfp4::geometry(n, k));
+  return ok();
+  NVFP4_GUARD_END
+}
+
+int nvfp4_pack(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k, void* packed, void* stream) {
+  NVFP4_GUARD_BEGIN
+  NVFP4_TRY(check_shape(n, k));
+  if (n == 0 || k == 0) return ok();
+  if (!codes || !scales || !packed) return fail(NVFP4_ERR_NULL, "codes, scales and packed must be non-NULL");
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(packed))
+    return fail(NVFP4_ERR_ALIGN, "codes, scales and packed must be 16-byte aligned");
+  return hip_status(nvfp4::launch_pack(codes, scales, nvfp4::geometry(n, k), packed, (hipStream_t)stream), "pack launch");
+  NVFP4_GUARD_END
+}
+
+int nvfp4_unpack(const void* packed, int64_t n, int64_t k, uint8_t* codes, uint8_t* scales, void* stream) {
+  NVFP4_GUARD_BEGIN
+  NVFP4_TRY(check_shape(n, k));
+  if (n == 0 || k == 0) return ok();
+  if (!codes || !scales || !packed) return fail(NVFP4_ERR_NULL, "codes, scales and packed must be non-NULL");
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(packed))
+    return fail(NVFP4_ERR_ALIGN, "codes, scales and packed must be 16-byte aligned");
+  return hip_status(nvfp4::launch_unpack(packed, nvfp4::geometry(n, k), codes, scales, (hipStream_t)stream),
+                    "unpack launch");
+  NVFP4_GUARD_END
+}
+
+int nvfp4_gemv_workspace_bytes(int64_t n, int64_t k, size_t* bytes) {
+  NVFP4_GUARD_BEGIN
+  if (!bytes) return fail(NVFP4_ERR_NULL, "bytes is NULL");
+  NVFP4_TRY(check_shape(n, k));
+  NVFP4_TRY(check_rows(n));
+  *bytes = nvfp4::gemv_workspace_bytes(nvfp4::geometry(n, k));
+  return ok();
+  NVFP4_GUARD_END
+}
+
+int nvfp4_gemv(const void* packed, int64_t n, int64_t k, float tensor_scale, const uint16_t* x, float* y,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  NVFP4_GUARD_BEGIN
+  NVFP4_TRY(check_shape(n, k));
+  NVFP4_TRY(check_rows(n));
+  if (n == 0) return ok();
+  if (!y || (k > 0 && (!packed || !x))) return fail(NVFP4_ERR_NULL, "packed, x and y must be non-NULL");
+  if (!aligned16(y) || (k > 0 && (!aligned16(packed) || !aligned16(x))))
+    return fail(NVFP4_ERR_ALIGN, "packed, x and y must be 16-byte aligned");
+  const nvfp4::Geometry g = nvfp4::geometry(n, k);
+  const size_t need = nvfp4::gemv_workspace_bytes(g);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace ? workspace_bytes : 0);
+  if (need > 0 && !aligned16(workspace)) return fail(NVFP4_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return hip_status(nvfp4::launch_gemv(packed, g, tensor_scale, x, y, workspace, (hipStream_t)stream), "gemv launch");
+  NVFP4_GUARD_END
+}
+
+int nvfp4_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, size_t* bytes) {
+  NVFP4_GUARD_BEGIN
+  if (!bytes) return fail(NVFP4_ERR_NULL, "bytes is NULL");
+  NVFP4_TRY(check_shape(n, k));
+  NVFP4_TRY(check_rows(n));
+  if (m < 0 || m > kMaxDim) return fail(NVFP4_ERR_SHAPE, "m=%lld out of range", (long long)m);
+  const nvfp4::Geometry g = nvfp4::geometry(n, k);
+  *bytes = m <= 32 ? nvfp4::skinny_workspace_bytes(g) : nvfp4::prefill_workspace_bytes(m, g);
+  return ok();
+  NVFP4_GUARD_END
+}
+
+int nvfp4_gemm(const void* packed, int64_t n, int64_t k, float tensor_scale, const uint16_t* x, int64_t m,
+               int64_t ldx, void* y, int64_t ldy, int y_dtype, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  NVFP4_GUARD_BEGIN
+  NVFP4_TRY(check_shape(n, k));
+  NVFP4_TRY(check_rows(n));
+  if (m < 0 || m > kMaxDim) return fail(NVFP4_ERR_SHAPE, "m=%lld out of range", (long long)m);
+  if (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16) return fail(NVFP4_ERR_DTYPE, "unknown y_dtype %d", y_dtype);
+  if (m == 0 || n == 0) return ok();
+  if (ldx < k || ldx % 8 != 0) return fail(NVFP4_ERR_SHAPE, "ldx=%lld must be >= k=%lld and a multiple of 8", (long long)ldx, (long long)k);
+  if (ldy < n) return fail(NVFP4_ERR_SHAPE, "ldy=%lld must be >= n=%lld", (long long)ldy, (long long)n);
+  if (!y || (k > 0 && (!packed || !x))) return fail(NVFP4_ERR_NULL, "packed, x and y must be non-NULL");
+  if (!aligned16(y) || (k > 0 && (!aligned16(packed) || !aligned16(x))))
+    return fail(NVFP4_ERR_ALIGN, "packed, x and y must be 16-byte aligned");
+  const nvfp4::Geometry g = nvfp4::geometry(n, k);
+  const bool skinny = m <= 32;
+  const size_t need = skinny ? nvfp4::skinny_workspace_bytes(g) : nvfp4::prefill_workspace_bytes(m, g);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace ? workspace_bytes : 0);
+  if (need > 0 && !aligned16(workspace)) return fail(NVFP4_ERR_ALIGN, "workspace must be 16-byte aligned");
+  const bool bf16 = y_dtype == NVFP4_BF16;
+  hipError_t e = skinny ? nvfp4::launch_skinny(packed, g, tensor_scale, x, m, ldx, y, ldy, bf16, workspace, (hipStream_t)stream)
+                        : nvfp4::launch_prefill(packed, g, tensor_scale, x, m, ldx, y, ldy, bf16, workspace, (hipStream_t)stream);
+  return hip_status(e, skinny ? "skinny gemm launch" : "prefill gemm launch");
+  NVFP4_GUARD_END
+}
+
+static int check_moe(const nvfp4_moe_args* a, bool need_buffers) {
+  if (!a) return fail(NVFP4_ERR_NULL, "args is NULL");
+  if (a->tokens < 0 || a->hidden <= 0 || a->inter <= 0 || a->experts <= 0)
+    return fail(NVFP4_ERR_SHAPE, "tokens must be >= 0; experts, hidden and inter > 0");
+  if (a->hidden % 16 != 0 || a->inter % 16 != 0)
+    return fail(NVFP4_ERR_SHAPE, "hidden=%lld and inter=%lld must be multiples of 16", (long long)a->hidden, (long long)a->inter);
+  if (a->tokens > kMaxDim || a->hidden > kMaxDim || a->inter > kMaxDim)
+    return fail(NVFP4_ERR_SHAPE, "size above 2^30");
+  if (a->experts > nvfp4::moe_max_experts())
+    return fail(NVFP4_ERR_ARG, "experts=%lld above the supported %lld", (long long)a->experts, (long long)nvfp4::moe_max_experts());
+  if (a->top_k < 1 || a->top_k > a->experts || a->top_k > 64)
+    return fail(NVFP4_ERR_ARG, "top_k=%lld must be in [1, min(experts, 64)]", (long long)a->top_k);
+  if (a->tokens * a->top_k > (int64_t(1) << 30)) return fail(NVFP4_ERR_SHAPE, "tokens*top_k too large");
+  if (!need_buffers) return NVFP4_OK;
+  if (a->y_dtype != NVFP4_F32 && a->y_dtype != NVFP4_BF16) return fail(NVFP4_ERR_DTYPE, "unknown y_dtype %d", a->y_dtype);
+  if (!a->x || !a->router_logits || !a->w_gate || !a->w_up || !a->w_down || !a->scale_gate || !a->scale_up ||
+      !a->scale_down || !a->y || !a->topk_ids || !a->topk_weights || !a->expert_counts || !a->expert_offsets ||
+      !a->perm || !a->workspace)
+    return fail(NVFP4_ERR_NULL, "a required MoE pointer is NULL");
+  if (!aligned16(a->x) || !aligned16(a->w_gate) || !aligned16(a->w_up) || !aligned16(a->w_down) ||
+      !aligned16(a->workspace) || !aligned16(a->y) || (a->dbg_gate && !aligned16(a->dbg_gate)) ||
+      (a->dbg_up && !aligned16(a->dbg_up)) || (a->dbg_h && !aligned16(a->dbg_h)) ||
+      (a->dbg_down && !aligned16(a->dbg_down)))
+    return fail(NVFP4_ERR_ALIGN, "x, weight pools, y, workspace and debug outputs must be 16-byte aligned");
+  if (!aligned4(a->router_logits) || !aligned4(a->scale_gate) || !aligned4(a->scale_up) || !aligned4(a->scale_down) ||
+      !aligned4(a->topk_ids) || !aligned4(a->topk_weights) || !aligned4(a->expert_counts) ||
+      !aligned4(a->expert_offsets) || !aligned4(a->perm))
+    return fail(NVFP4_ERR_ALIGN, "logits, scales and index outputs must be 4-byte aligned");
+  const size_t gu = nvfp4::packed_bytes(nvfp4::geometry(a->inter, a->hidden));
+  const size_t dn = nvfp4::packed_bytes(nvfp4::geometry(a->hidden, a->inter));
+  if (a->stride_gate < gu || a->stride_up < gu || a->stride_down < dn)
+    return fail(NVFP4_ERR_ARG, "expert strides must be at least the packed matrix size (%zu / %zu bytes)", gu, dn);
+  if (a->stride_gate % 16 || a->stride_up % 16 || a->stride_down % 16)
+    return fail(NVFP4_ERR_ALIGN, "expert strides must be multiples of 16 bytes");
+  const size_t need = nvfp4::moe_workspace_bytes(a->tokens, a->experts, a->top_k, a->hidden, a->inter);
+  if (a->workspace_bytes < need) return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, a->workspace_bytes);
+  return NVFP4_OK;
+}
+
+int nvfp4_moe_workspace_bytes(const nvfp4_moe_args* args, size_t* bytes) {
+  NVFP4_GUARD_BEGIN
+  if (!bytes) return fail(NVFP4_ERR_NULL, "bytes is NULL");
+  NVFP4_TRY(check_moe(args, false));
+  *bytes = nvfp4::moe_workspace_bytes(args->tokens, args->experts, args->top_k, args->hidden, args->inter);
+  return ok();
+  NVFP4_GUARD_END
+}
+
+int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
+  NVFP4_GUARD_BEGIN
+  if (a && a->tokens == 0) {
+    NVFP4_TRY(check_moe(a, false));
+    return ok();
+  }
+  NVFP4_TRY(check_moe(a, true));
+  nvfp4::MoeLaunch l;
+  l.tokens = a->tokens; l.experts = a->experts; l.top_k = a->top_k; l.hidden = a->hidden; l.inter = a->inter;
+  l.x = a->x; l.logits = a->router_logits;
+  l.w_gate = static_cast<const uint8_t*>(a->w_gate);
+  l.w_up = static_cast<const uint8_t*>(a->w_up);
+  l.w_down = static_cast<const uint8_t*>(a->w_down);
+  l.stride_gate = a->stride_gate; l.stride_up = a->stride_up; l.stride_down = a->stride_down;
+  l.scale_gate = a->scale_gate; l.scale_up = a->scale_up; l.scale_down = a->scale_down;
+  l.y = a->y; l.y_bf16 = a->y_dtype == NVFP4_BF16;
+  l.ids = a->topk_ids; l.g = a->topk_weights; l.counts = a->expert_counts; l.offsets = a->expert_offsets;
+  l.perm = a->perm;
+  l.dbg_gate = a->dbg_gate; l.dbg_up = a->dbg_up; l.dbg_h = a->dbg_h; l.dbg_down = a->dbg_down;
+  l.ws = a->workspace;
+  return hip_status(nvfp4::launch_moe(l, (hipStream_t)stream), "moe launch");
+  NVFP4_GUARD_END
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+// Device-side helpers shared by the NVFP4 kernels (gfx950 / CDNA4 only).
+//
+// Packed layout (the one form every product kernel reads).  An [N][K] NVFP4
+// matrix is padded to Np = ceil(N/64)*64 rows and Kp = ceil(K/256)*256 columns
+// (padding: code 0, scale byte 0x00, i.e. weight 0) and cut into tiles of
+// 64 rows x 256 k, stored row-tile-major: tile (rt, kt) starts at
+// (rt * (Kp/256) + kt) * 9216 bytes.  Inside a tile:
+//   bytes [1024*c + 16*l, +16), c = 0..7 : the 32 codes of row 64*rt + l for
+//        k = 256*kt + 32*c + [0, 32), in canonical order (k even in the low
+//        nibble) -- one coalesced 1 KB wavefront load per chunk, lane l = row l;
+//   bytes [8192 + 16*l, +16) : the 16 E4M3 scale bytes of row 64*rt + l for
+//        blocks 16*kt + [0, 16) -- one 16-byte load per lane per tile.
+// 9216 bytes per 16384 weights = 0.5625 bytes per weight, the format's own size.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+constexpr int kTileRows = 64;
+constexpr int kTileK = 256;
+constexpr int kTileCodeBytes = 8192;
+constexpr int kTileBytes = 9216;
+constexpr int kChunkK = 32;          // k per 16-byte lane load
+constexpr int kChunksPerTile = 8;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two E2M1 codes (byte `SEL` of w: low nibble -> .x, high nibble -> .y) to fp32.
+// The conversion's scale operand only contributes its exponent, so 1.0f gives
+// the plain E2M1 values.
+template <int SEL>
+__device__ __forceinline__ f32x2 e2m1x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+}
+
+// E4M3FN byte `SEL` of w to fp32 (exact; NaN for 0x7F / 0xFF).
+template <int SEL>
+__device__ __forceinline__ float e4m3(uint32_t w) {
+  return __builtin_amdgcn_cvt_f32_fp8(w, SEL);
+}
+
+// Round-to-nearest-even fp32 -> bf16 of a pair, packed low/high.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float v) {
+  __bf16 a = (__bf16)v;
+  return __builtin_bit_cast(uint16_t, a);
+}
+
+// Exchange between the wavefront halves: afterwards lanes 32..63 of `hi_dst`
+// hold what lanes 0..31 of `lo_src` held, and lanes 0..31 of `lo_src` hold what
+// lanes 32..63 of `hi_dst` held; the other lanes keep their values.
+__device__ __forceinline__ void swap_halves(uint32_t& hi_dst, uint32_t& lo_src) {
+  auto r = __builtin_amdgcn_permlane32_swap(hi_dst, lo_src, false, false);
+  hi_dst = r[0];
+  lo_src = r[1];
+}
+
+// Split-K handoff between workgroups without floating-point atomics.
+//
+// Each workgroup writes its partial sums with store_coherent, then calls
+// arrive_last; the workgroup that arrives last sees true and reads every
+// partial with load_coherent, adding them in index order -- so the result does
+// not depend on arrival order.  It also returns the counter to zero.
+//
+// Coherence without cache maintenance: the L2 of each XCD is not coherent with
+// the others, and a device-scope fence would write back and invalidate the
+// whole L2 (slow, and it evicts the weight stream of every other workgroup on
+// that XCD).  Instead every partial is stored and loaded as a device-scope
+// relaxed atomic (write-through / L2-bypassing accesses), each thread waits
+// for its own stores to complete before the workgroup barrier, and only then
+// does one thread bump the device-scope counter.  The reader's loads are
+// issued after it has observed the final count.
+// Must be called by every thread of the workgroup (contains barriers).
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned expected) {
+  __shared__ unsigned s_last;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);  // keep the partial stores above the wait
+  __builtin_amdgcn_s_waitcnt(0);            // this thread's partial stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned last = (prev == expected - 1u) ? 1u : 0u;
+    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = last;
+  }
+  __syncthreads();
+  return s_last != 0u;
+}
+
+}  // namespace nvfp4

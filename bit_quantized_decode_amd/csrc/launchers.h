@@ -1,0 +1,88 @@
+// Host-side launchers of the HIP kernels; called only by abi.cpp after it has
+// validated every argument.  Each returns the hipError_t of its launch(es).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+struct Geometry {
+  int64_t n, k;      // logical shape
+  int64_t nrt, nkt;  // row tiles (64 rows), k tiles (256 k)
+};
+
+inline Geometry geometry(int64_t n, int64_t k) {
+  Geometry g;
+  g.n = n;
+  g.k = k;
+  g.nrt = (n + 63) / 64;
+  g.nkt = (k + 255) / 256;
+  return g;
+}
+
+inline size_t packed_bytes(const Geometry& g) { return (size_t)g.nrt * (size_t)g.nkt * 9216u; }
+
+// Split workspaces (GEMV and skinny GEMM) start with a fixed counter area of
+// kCounterSlots zero-initialised uint32 counters -- one per row tile or row
+// group -- followed by the partial sums.  Because the counter area never moves,
+// calls of different shapes can share one workspace: one call's partials can
+// never land on another call's counters.
+constexpr int64_t kCounterSlots = 65536;
+constexpr size_t kCounterBytes = (size_t)kCounterSlots * 4;
+constexpr int64_t kMaxSplitRows = kCounterSlots * 64;
+
+// Split-K plan shared by the GEMV and the skinny GEMM: `groups` workgroups per
+// row tile, 4 wavefronts each, so the K tiles are cut into 4*groups parts.
+struct SplitPlan {
+  int groups;
+  int parts;
+};
+SplitPlan gemv_plan(const Geometry& g);
+SplitPlan skinny_plan(const Geometry& g);
+size_t gemv_workspace_bytes(const Geometry& g);
+size_t skinny_workspace_bytes(const Geometry& g);
+size_t prefill_workspace_bytes(int64_t m, const Geometry& g);
+
+hipError_t launch_pack(const uint8_t* codes, const uint8_t* scales, const Geometry& g, void* packed,
+                       hipStream_t s);
+hipError_t launch_unpack(const void* packed, const Geometry& g, uint8_t* codes, uint8_t* scales,
+                         hipStream_t s);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_gemv(const void* packed, const Geometry& g, float st, const uint16_t* x, float* y,
+                       void* ws, hipStream_t s);
+hipError_t launch_skinny(const void* packed, const Geometry& g, float st, const uint16_t* x, int64_t m,
+                         int64_t ldx, void* y, int64_t ldy, bool y_bf16, void* ws, hipStream_t s);
+hipError_t launch_prefill(const void* packed, const Geometry& g, float st, const uint16_t* x, int64_t m,
+                          int64_t ldx, void* y, int64_t ldy, bool y_bf16, void* ws, hipStream_t s);
+
+struct MoeLaunch {
+  int64_t tokens, experts, top_k, hidden, inter;
+  const uint16_t* x;
+  const float* logits;
+  const uint8_t* w_gate;
+  const uint8_t* w_up;
+  const uint8_t* w_down;
+  size_t stride_gate, stride_up, stride_down;
+  const float* scale_gate;
+  const float* scale_up;
+  const float* scale_down;
+  void* y;
+  bool y_bf16;
+  int32_t* ids;
+  float* g;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  float* dbg_gate;
+  float* dbg_up;
+  uint16_t* dbg_h;
+  float* dbg_down;
+  void* ws;
+};
+size_t moe_workspace_bytes(int64_t tokens, int64_t experts, int64_t top_k, int64_t hidden, int64_t inter);
+int64_t moe_max_experts();
+hipError_t launch_moe(const MoeLaunch& a, hipStream_t s);
+
+}  // namespace nvfp4

@@ -1,0 +1,196 @@
+/*
+ * nvfp4.h -- NVFP4 weight x bf16 activation products on AMD Instinct MI355X (gfx950).
+ *
+ * The only way into the library (libnvfp4.so).  A flat C boundary with plain
+ * pointers and sizes, as the Ignis README's introduction describes for its own
+ * kernel library ("a flat, device-resident step-level C ABI" under the Rust
+ * host) and as the imp README's "Using it" section offers its C library.
+ *
+ * ---- The weight format (NVFP4) ----------------------------------------------
+ * An [N][K] weight matrix W (N output rows, K inputs, K a multiple of 16) is
+ *   codes   uint8 [N][K/2]   two 4-bit E2M1 codes per byte, element k = 2i in
+ *                            the low nibble of byte i, k = 2i+1 in the high nibble
+ *   scales  uint8 [N][K/16]  one FP8 E4M3FN scale per 16 consecutive K of a row
+ *   s_t     float            one fp32 per-tensor scale
+ * and W[n][k] = s_t * e2m1(code) * e4m3(scale[n][k/16]).  E2M1 takes the 16
+ * values {0, +-0.5, +-1, +-1.5, +-2, +-3, +-4, +-6} (OCP MX v1.0); E4M3FN has no
+ * infinities, 0x7F/0xFF are NaN (a NaN scale makes its block NaN), subnormals
+ * are m * 2^-9.  The imp README ("How does it work?") keeps weights in this
+ * 4-bit format and computes on it directly instead of unpacking to 16 bits.
+ *
+ * ---- Conventions for every call ---------------------------------------------
+ *  - Pointers are DEVICE memory unless marked (host).  The caller owns all
+ *    memory; the library never allocates, frees or synchronises.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued on
+ *    it and runs asynchronously; results are ready after the caller
+ *    synchronises with the stream.
+ *  - Arguments are validated on the host before anything is enqueued.  A
+ *    failed check returns its status and enqueues nothing, in the spirit of the
+ *    imp README's "Will it fit?" (refuse rather than run wrong).
+ *  - Device pointers to bulk data (codes, scales, packed buffers, activations,
+ *    outputs, workspaces) must be 16-byte aligned; the small per-token and
+ *    per-expert arrays of the MoE call (logits, tensor scales, ids, weights,
+ *    counts, offsets, perm) 4-byte aligned (NVFP4_ERR_ALIGN otherwise).
+ *  - A launch failure returns NVFP4_ERR_HIP; nvfp4_last_error() then holds the
+ *    HIP error text.  Faults during execution surface at the caller's next
+ *    synchronisation.
+ *  - No C++ exception crosses this boundary.  The library keeps no mutable
+ *    global state apart from the thread-local error text.
+ *  - Workspaces: calls that split a reduction across workgroups take a caller
+ *    workspace of at least the size the matching *_workspace_bytes() returns.
+ *    For nvfp4_gemv / nvfp4_gemm its first 262144 bytes are counters that must
+ *    be all zero before the first use (allocate it zeroed); every call leaves
+ *    them zero again, so one workspace serves calls of any shape in stream
+ *    order.  Calls that share one workspace must not run concurrently.
+ *    nvfp4_gemv / nvfp4_gemm accept n up to 4194304 rows.
+ *  - Products accumulate in fp32.  Every product of a weight and a bf16
+ *    activation is exact in fp32; the per-tensor scale is applied after
+ *    accumulation.  The sum order is fixed, so repeated calls give
+ *    bit-identical results (no floating-point atomics anywhere).
+ */
+#ifndef NVFP4_H_
+#define NVFP4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_ABI_VERSION 1
+
+typedef enum nvfp4_status {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = 1,       /* a required pointer is NULL */
+  NVFP4_ERR_SHAPE = 2,      /* a size is negative, K % 16 != 0, a leading dimension too small, ... */
+  NVFP4_ERR_ALIGN = 3,      /* a device pointer (or a byte stride) is not 16-byte aligned */
+  NVFP4_ERR_DTYPE = 4,      /* unknown nvfp4_dtype */
+  NVFP4_ERR_WORKSPACE = 5,  /* workspace missing or smaller than required */
+  NVFP4_ERR_ARG = 6,        /* other invalid argument (top_k > experts, stride too small, ...) */
+  NVFP4_ERR_HIP = 7         /* a HIP launch failed; see nvfp4_last_error() */
+} nvfp4_status;
+
+typedef enum nvfp4_dtype {
+  NVFP4_F32 = 0,            /* float32 */
+  NVFP4_BF16 = 1            /* bfloat16, rounded to nearest even */
+} nvfp4_dtype;
+
+/* NVFP4_ABI_VERSION of the built library. */
+int nvfp4_abi_version(void);
+
+/* A static string naming `status` ("NVFP4_OK", ...); "unknown status" otherwise. */
+const char* nvfp4_status_str(int status);
+
+/* Thread-local text describing this thread's last failed call ("" if none). */
+const char* nvfp4_last_error(void);
+
+/* ---- a1: offline repack -------------------------------------------------------
+ * The packed buffer is the only form the product kernels read.  Its layout is
+ * private to the library (a gfx950 tile layout); only nvfp4_packed_bytes() and
+ * nvfp4_unpack() expose it.  It holds exactly the NVFP4 information (0.5625
+ * bytes per weight) plus zero padding of N to a multiple of 64 and of K to a
+ * multiple of 256.  imp converts weights once at first load and caches the
+ * result (imp README, "Install"); packing is likewise a one-off step outside
+ * the timed path.
+ */
+
+/* (host) *bytes = size of the packed buffer for an [n][k] matrix.
+ * n >= 0, k >= 0, k % 16 == 0. */
+int nvfp4_packed_bytes(int64_t n, int64_t k, size_t* bytes);
+
+/* Repack canonical codes [n][k/2] and scales [n][k/16] (both row-major,
+ * contiguous) into `packed` (nvfp4_packed_bytes() bytes, fully written,
+ * padding included).  n == 0 or k == 0 is a no-op. */
+int nvfp4_pack(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
+               void* packed, void* stream);
+
+/* The inverse of nvfp4_pack (a test hook): writes codes [n][k/2] and scales [n][k/16]. */
+int nvfp4_unpack(const void* packed, int64_t n, int64_t k, uint8_t* codes, uint8_t* scales,
+                 void* stream);
+
+/* ---- a2: GEMV, one activation vector ----------------------------------------
+ * y[j] = s_t * sum_k e2m1(c[j][k]) * e4m3(sigma[j][k/16]) * x[k],   j < n.
+ * x: bf16 bit patterns [k];  y: float32 [n].
+ * The memory-bound decode product: the Ignis README ("The decode round")
+ * measures its decode round as weight streaming at the card's bandwidth, the
+ * backbone GEMM at full roofline.  n == 0 or k == 0: y is zero-filled (k == 0)
+ * or nothing is done (n == 0).
+ */
+int nvfp4_gemv_workspace_bytes(int64_t n, int64_t k, size_t* bytes /* host */);
+int nvfp4_gemv(const void* packed, int64_t n, int64_t k, float tensor_scale,
+               const uint16_t* x, float* y, void* workspace, size_t workspace_bytes,
+               void* stream);
+
+/* ---- a3 / a9: GEMM, m activation rows -----------------------------------------
+ * y[i][j] = s_t * sum_k W[j][k] * x[i][k],   i < m, j < n.
+ * x: bf16 bit patterns, row i at x + i*ldx (ldx >= k, ldx % 8 == 0);
+ * y: y_dtype, row i at y + i*ldy elements (ldy >= n).
+ * m <= 32 runs the skinny (decode-batch) kernel: the imp README's 32-users
+ * table and the Ignis README's batch-wide decode round.  Larger m runs the
+ * prefill kernel, which dequantises each weight x block-scale exactly to bf16
+ * in LDS and runs bf16 MFMA.  m == 0 or n == 0 is a no-op.
+ */
+int nvfp4_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, size_t* bytes /* host */);
+int nvfp4_gemm(const void* packed, int64_t n, int64_t k, float tensor_scale,
+               const uint16_t* x, int64_t m, int64_t ldx,
+               void* y, int64_t ldy, int y_dtype,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- a4-a8: top-k routed mixture-of-experts layer ----------------------------
+ * Per token t (CHImp-Alpha-v1.0 model card, "How it fits on one GPU": each
+ * token is routed to 10 of 512 experts and only those experts' weights are read):
+ *   ids[t][0..top_k)  the top_k experts by router logit, descending, equal
+ *                     logits ranked by smaller expert id (logits must not be NaN);
+ *   g[t][j]           exp(l_j - l_0) / sum_j' exp(l_j' - l_0)  (softmax over the
+ *                     selected logits, fp32);
+ *   for each j, with e = ids[t][j]:
+ *     h_j = bf16( silu(Wg_e x_t) * (Wu_e x_t) ),  silu(z) = z / (1 + exp(-z)),
+ *     d_j = Wd_e h_j                                (fp32)
+ *   y[t] = sum_{j = 0..top_k-1} g[t][j] * d_j      (summed in j order).
+ * Wg_e, Wu_e are [inter][hidden], Wd_e is [hidden][inter], each packed with
+ * nvfp4_pack(); expert e's packed matrix starts e*stride bytes into its pool.
+ * Grouping outputs (bit-exact, deterministic):
+ *   expert_counts[e]   number of (t, j) with ids[t][j] == e
+ *   expert_offsets[e]  exclusive prefix sum of the counts (offsets[E] = tokens*top_k)
+ *   perm[p]            the flat indices f = t*top_k + j ordered by expert, and by f
+ *                      within an expert (a stable sort by expert id)
+ * Optional stage outputs (NULL to skip), rows in perm order p:
+ *   dbg_gate, dbg_up  fp32 [tokens*top_k][inter]   Wg_e x_t, Wu_e x_t (tensor scale applied)
+ *   dbg_h             bf16 [tokens*top_k][inter]
+ *   dbg_down          fp32 [tokens*top_k][hidden]  d_j
+ * tokens == 0 is a no-op.  Experts with no tokens are never read.
+ */
+typedef struct nvfp4_moe_args {
+  int64_t tokens, experts, top_k, hidden, inter;
+  const uint16_t* x;              /* bf16 [tokens][hidden] */
+  const float* router_logits;     /* fp32 [tokens][experts] */
+  const void* w_gate;             /* packed pools */
+  const void* w_up;
+  const void* w_down;
+  size_t stride_gate, stride_up, stride_down;   /* bytes between experts in each pool */
+  const float* scale_gate;        /* per-expert tensor scales, device fp32 [experts] */
+  const float* scale_up;
+  const float* scale_down;
+  void* y;                        /* [tokens][hidden], y_dtype */
+  int y_dtype;
+  int32_t* topk_ids;              /* [tokens][top_k] (out) */
+  float* topk_weights;            /* [tokens][top_k] (out) */
+  int32_t* expert_counts;         /* [experts] (out) */
+  int32_t* expert_offsets;        /* [experts + 1] (out) */
+  int32_t* perm;                  /* [tokens * top_k] (out) */
+  float* dbg_gate;                /* optional, see above */
+  float* dbg_up;
+  uint16_t* dbg_h;
+  float* dbg_down;
+  void* workspace;
+  size_t workspace_bytes;
+} nvfp4_moe_args;
+
+int nvfp4_moe_workspace_bytes(const nvfp4_moe_args* args /* host */, size_t* bytes /* host */);
+int nvfp4_moe_grouped(const nvfp4_moe_args* args /* host */, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NVFP4_H_ */

@@ -1,0 +1,85 @@
+"""Shared test helpers: device transfer, bf16 views and the parity bounds."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from bit_quantized_decode_amd import inputs as I
+
+TOL = 1e-5  # |y - y_ref| <= TOL * sum_k |w_k x_k| per output
+
+
+def device():
+    if not torch.cuda.is_available():
+        pytest.fail("a GPU test ran without a visible GPU (these tests fail rather than skip)")
+    from bit_quantized_decode_amd import binding as B
+    B.lib()  # raises if the HIP library is not built
+    return torch.device("cuda:0")
+
+
+def to_dev_u8(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def to_dev_bf16(bits, dev):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev)
+    return t.view(torch.bfloat16)
+
+
+def bf16_to_f64(t):
+    """torch bf16 tensor (any device) -> numpy float64."""
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def bf16_bits(t):
+    return t.detach().to("cpu").view(torch.int16).numpy().view(np.uint16)
+
+
+def ulp_bf16(v):
+    """Spacing of bf16 at |v| (smallest subnormal spacing at 0)."""
+    v = np.abs(np.asarray(v, dtype=np.float64))
+    _, e = np.frexp(v)
+    u = np.ldexp(1.0, e - 8)
+    return np.where(v > 0, np.maximum(u, 2.0 ** -133), 2.0 ** -133)
+
+
+def assert_within(y, y_ref, s, extra=0.0, what=""):
+    """Per-output bound |y - y_ref| <= TOL * s + extra; reports the worst ratio."""
+    y = np.asarray(y, dtype=np.float64)
+    err = np.abs(y - y_ref)
+    bound = TOL * s + extra
+    bad = ~(err <= bound)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        ratio = np.max(np.where(s > 0, err / np.maximum(s, 1e-300), np.inf))
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outputs outside the bound; "
+                             f"worst err/S = {ratio:.3e}; first at {idx.tolist()}: "
+                             f"y={y[tuple(idx[0])]!r} ref={y_ref[tuple(idx[0])]!r} S={s[tuple(idx[0])]!r}")
+    return float(np.max(err / np.maximum(s, 1e-300))) if s.size else 0.0
+
+
+def oracle_threads():
+    try:
+        return min(len(os.sched_getaffinity(0)), 16)
+    except AttributeError:
+        return 8
+
+
+def pack_to_device(codes, scales, dev):
+    from bit_quantized_decode_amd import binding as B
+    return B.pack(to_dev_u8(codes, dev), to_dev_u8(scales, dev))
+
+
+def sample_rows(n, count, seed):
+    """First, last and random rows (sorted, unique)."""
+    rng = np.random.default_rng(seed)
+    rows = set(range(min(n, 8))) | set(range(max(0, n - 8), n))
+    rows |= set(rng.choice(n, size=min(n, count), replace=False).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def random_matrix(rng, n, k):
+    codes = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    scales = I.e4m3_round(np.exp2(rng.uniform(-6, 2, size=(n, k // 16))))
+    return codes, scales

