@@ -4,12 +4,20 @@
 // matrix is padded to Np = ceil(N/64)*64 rows and Kp = ceil(K/256)*256 columns
 // (padding: code 0, scale byte 0x00, i.e. weight 0) and cut into tiles of
 // 64 rows x 256 k, stored row-tile-major: tile (rt, kt) starts at
-// (rt * (Kp/256) + kt) * 9216 bytes.  Inside a tile:
-//   bytes [1024*c + 16*l, +16), c = 0..7 : the 32 codes of row 64*rt + l for
-//        k = 256*kt + 32*c + [0, 32), in canonical order (k even in the low
-//        nibble) -- one coalesced 1 KB wavefront load per chunk, lane l = row l;
-//   bytes [8192 + 16*l, +16) : the 16 E4M3 scale bytes of row 64*rt + l for
-//        blocks 16*kt + [0, 16) -- one 16-byte load per lane per tile.
+// (rt * (Kp/256) + kt) * 9216 bytes.  Inside a tile, with r = l % 32 and
+// h = l / 32 for lane l of a wavefront:
+//   bytes [1024*c + 16*l, +16), c = 0..7 (k = 256*kt + 32*c + [0, 32)):
+//        dword 0: row r,      k offsets 8h + [0, 8)
+//        dword 1: row 32 + r, k offsets 8h + [0, 8)
+//        dword 2: row r,      k offsets 16 + 8h + [0, 8)
+//        dword 3: row 32 + r, k offsets 16 + 8h + [0, 8)
+//        (rows relative to the tile, k offsets relative to the chunk; 8 codes
+//        per dword in canonical order, k even in the low nibble).  This is
+//        the A-operand layout of v_mfma_f32_32x32x16_bf16 for two 32-row
+//        halves and two k steps, so a 1 KB coalesced wavefront load feeds four
+//        matrix instructions without any lane exchange;
+//   bytes [8192 + 32*r, +16): the 16 E4M3 scale bytes of row r for blocks
+//        16*kt + [0, 16); bytes [8192 + 32*r + 16, +16): the same for row 32 + r.
 // 9216 bytes per 16384 weights = 0.5625 bytes per weight, the format's own size.
 #pragma once
 
@@ -22,8 +30,9 @@ constexpr int kTileRows = 64;
 constexpr int kTileK = 256;
 constexpr int kTileCodeBytes = 8192;
 constexpr int kTileBytes = 9216;
-constexpr int kChunkK = 32;          // k per 16-byte lane load
+constexpr int kChunkK = 32;          // k per 1 KB wavefront chunk
 constexpr int kChunksPerTile = 8;
+constexpr int kScaleOffset = 8192;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -50,6 +59,13 @@ __device__ __forceinline__ f32x2 e2m1x2(uint32_t w) {
 template <int SEL>
 __device__ __forceinline__ float e4m3(uint32_t w) {
   return __builtin_amdgcn_cvt_f32_fp8(w, SEL);
+}
+
+// Pack two fp32 values whose low 16 bits are zero (at most 8 significant
+// bits: every dequantised weight qualifies) into a bf16 pair: truncation is
+// exact for them, and one byte permute does it.
+__device__ __forceinline__ uint32_t pack_exact_bf16x2(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
 // Round-to-nearest-even fp32 -> bf16 of a pair, packed low/high.
@@ -94,6 +110,54 @@ __device__ __forceinline__ void store_coherent(float* p, float v) {
 
 __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// sum_{i < count} p[i * stride], added in index order.  The loads are issued
+// in batches of eight so that their memory latencies overlap; padding lanes of
+// a batch re-read the last element and are not added.
+__device__ __forceinline__ float sum_coherent(const float* p, size_t stride, int count) {
+  float s = 0.0f;
+  for (int i = 0; i < count; i += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int idx = i + j < count ? i + j : count - 1;
+      v[j] = load_coherent(p + (size_t)idx * stride);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s = (i + j < count) ? s + v[j] : s;
+  }
+  return s;
+}
+
+// Sixteen 16-byte loads that bypass the non-coherent caches, issued together;
+// the wait for them sits in the same asm statement, so no load is still in
+// flight when the statement ends.
+__device__ __forceinline__ void load16x4_coherent(const float* const (&p)[16], f32x4 (&v)[16]) {
+  asm volatile(
+      "global_load_dwordx4 %0, %16, off sc1\n"
+      "global_load_dwordx4 %1, %17, off sc1\n"
+      "global_load_dwordx4 %2, %18, off sc1\n"
+      "global_load_dwordx4 %3, %19, off sc1\n"
+      "global_load_dwordx4 %4, %20, off sc1\n"
+      "global_load_dwordx4 %5, %21, off sc1\n"
+      "global_load_dwordx4 %6, %22, off sc1\n"
+      "global_load_dwordx4 %7, %23, off sc1\n"
+      "global_load_dwordx4 %8, %24, off sc1\n"
+      "global_load_dwordx4 %9, %25, off sc1\n"
+      "global_load_dwordx4 %10, %26, off sc1\n"
+      "global_load_dwordx4 %11, %27, off sc1\n"
+      "global_load_dwordx4 %12, %28, off sc1\n"
+      "global_load_dwordx4 %13, %29, off sc1\n"
+      "global_load_dwordx4 %14, %30, off sc1\n"
+      "global_load_dwordx4 %15, %31, off sc1\n"
+      "s_waitcnt vmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
+        "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]),
+        "=&v"(v[15])
+      : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7]), "v"(p[8]),
+        "v"(p[9]), "v"(p[10]), "v"(p[11]), "v"(p[12]), "v"(p[13]), "v"(p[14]), "v"(p[15])
+      : "memory");
 }
 
 __device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned expected) {

@@ -4,19 +4,24 @@
 //
 // The memory-bound decode product (the Ignis README's decode round is weight
 // streaming at the card's bandwidth).  Mapping on gfx950:
-//  - a wavefront owns one 64-row tile and a range of its 256-k tiles; lane l
-//    owns row l, so every lane reads the same activations: x comes in through
-//    scalar loads (wave-uniform) and never occupies vector registers or LDS;
-//  - each 16-byte code load (32 weights) is converted two codes per
-//    instruction to fp32 and multiplied into fp32 with x by FMA (products
-//    exact); the E4M3 scale multiplies each 16-weight block partial, once;
-//  - four wavefronts of a workgroup split the row tile's k range and meet in
-//    LDS; several workgroups per row tile meet through the workspace, summed
-//    in a fixed order by whichever arrives last (no float atomics).
-// Rounding: every fp32 result passes through at most 16 (block) + 1 (scale)
-// + 16 (tile) + (k tiles per wave) + 3 (wave merge) + (workgroups per row
-// tile) + 1 (s_t) roundings; the plans below keep that under 100, i.e. an
-// error below 100 * 2^-24 * sum|w x| = 6e-6 * sum|w x|.
+//  - one wavefront per (64-row tile, 256-k tile), issuing all ten of its
+//    16-byte loads per lane at once; the grid holds every tile of the matrix,
+//    so the whole weight stream is requested from the start;
+//  - in the tile layout lane l carries rows l%32 and 32 + l%32 at k half
+//    l/32 of every 16-k step, so it needs only 16 of each chunk's 32
+//    activations; a workgroup is four wavefronts on four consecutive k tiles
+//    of one row tile and stages those 1024 activations in LDS once;
+//  - codes become bf16 two per instruction (exact: E2M1 values fit bf16) and
+//    meet the bf16 activations in v_dot2_f32_bf16 (products exact in fp32);
+//    the E4M3 scale multiplies each 8-weight half-block partial once;
+//  - the two k halves meet with one lane-half exchange, the four wavefronts
+//    in LDS, and the workgroups of one row tile through the workspace, summed
+//    in a fixed order by whichever arrives last (no floating-point atomics).
+// Rounding: a result passes at most 8 roundings in a half-block partial (4
+// dot2, each measured below 2.5 roundings' worth), 1 for the scale, 16 over
+// the tile's blocks, 1 for the k-half merge, 3 in the wavefront merge, one
+// per workgroup of the row tile (K/1024) and 1 for s_t: for K <= 32768 below
+// 70 * 2^-24 * sum|w x| = 4.2e-6 * sum|w x|.
 #include "device_common.h"
 #include "launchers.h"
 
@@ -24,104 +29,80 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kGemvWaves = 4;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// 8 weights (code word `q`, 8 nibbles, k ascending) against 4 x pairs.
-__device__ __forceinline__ float dot8(uint32_t q, uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3, float p) {
-  f32x2 w;
-  w = e2m1x2<0>(q); p = fmaf(w.x, bf16_lo(x0), p); p = fmaf(w.y, bf16_hi(x0), p);
-  w = e2m1x2<1>(q); p = fmaf(w.x, bf16_lo(x1), p); p = fmaf(w.y, bf16_hi(x1), p);
-  w = e2m1x2<2>(q); p = fmaf(w.x, bf16_lo(x2), p); p = fmaf(w.y, bf16_hi(x2), p);
-  w = e2m1x2<3>(q); p = fmaf(w.x, bf16_lo(x3), p); p = fmaf(w.y, bf16_hi(x3), p);
-  return p;
+template <int SEL>
+__device__ __forceinline__ bf16x2 e2m1x2_bf16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL);
 }
 
-// One 32-k chunk (two scale blocks) of one row: returns acc + s0*p0 + s1*p1.
-// `xc` points at the chunk's 16 x pairs in LDS (the same address in every lane).
+__device__ __forceinline__ float dot2(bf16x2 w, uint32_t x, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(w, __builtin_bit_cast(bf16x2, x), acc, false);
+}
+
+// 8 weights (code word `q`, 8 nibbles, k ascending) against 4 bf16 x pairs.
+__device__ __forceinline__ float dot8(uint32_t q, u32x4 x) {
+  float p = dot2(e2m1x2_bf16<0>(q), x[0], 0.0f);
+  p = dot2(e2m1x2_bf16<1>(q), x[1], p);
+  p = dot2(e2m1x2_bf16<2>(q), x[2], p);
+  return dot2(e2m1x2_bf16<3>(q), x[3], p);
+}
+
+// Chunk C (k steps 2C, 2C+1) of this lane's two rows.  xa / xb: the lane's
+// 8 activations of the two steps; sa / sb: the rows' 16 scale bytes.
 template <int C>
-__device__ __forceinline__ float chunk(u32x4 q, const uint32_t* xc, u32x4 sc, float acc) {
-  const u32x4 xa = *reinterpret_cast<const u32x4*>(xc);
-  const u32x4 xb = *reinterpret_cast<const u32x4*>(xc + 4);
-  const u32x4 xc2 = *reinterpret_cast<const u32x4*>(xc + 8);
-  const u32x4 xd = *reinterpret_cast<const u32x4*>(xc + 12);
-  float p0 = dot8(q[0], xa[0], xa[1], xa[2], xa[3], 0.0f);
-  p0 = dot8(q[1], xb[0], xb[1], xb[2], xb[3], p0);
-  float p1 = dot8(q[2], xc2[0], xc2[1], xc2[2], xc2[3], 0.0f);
-  p1 = dot8(q[3], xd[0], xd[1], xd[2], xd[3], p1);
-  const float s0 = e4m3<(2 * C) % 4>(sc[C / 2]);
-  const float s1 = e4m3<(2 * C + 1) % 4>(sc[C / 2]);
-  acc = fmaf(p0, s0, acc);
-  return fmaf(p1, s1, acc);
-}
-
-struct TileRegs {
-  u32x4 sc;
-  u32x4 q[8];
-};
-
-__device__ __forceinline__ void load_tile(const uint8_t* t, TileRegs& r) {
-  r.sc = load16(t + kTileCodeBytes);
-#pragma unroll
-  for (int c = 0; c < 8; ++c) r.q[c] = load16(t + c * 1024);
-}
-
-// k tiles [kt(p), kt(p+1)) of part p when nkt tiles are cut into `parts` parts.
-__host__ __device__ __forceinline__ int part_begin(int p, int nkt, int parts) {
-  return (int)(((int64_t)p * nkt) / parts);
+__device__ __forceinline__ void chunk(u32x4 q, u32x4 xa, u32x4 xb, u32x4 sa, u32x4 sb, float& acc_a,
+                                      float& acc_b) {
+  acc_a = fmaf(dot8(q[0], xa), e4m3<(2 * C) % 4>(sa[C / 2]), acc_a);
+  acc_b = fmaf(dot8(q[1], xa), e4m3<(2 * C) % 4>(sb[C / 2]), acc_b);
+  acc_a = fmaf(dot8(q[2], xb), e4m3<(2 * C + 1) % 4>(sa[C / 2]), acc_a);
+  acc_b = fmaf(dot8(q[3], xb), e4m3<(2 * C + 1) % 4>(sb[C / 2]), acc_b);
 }
 
 __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t* __restrict__ packed, int64_t n, int64_t k,
                                                    int nkt, int groups, float st,
-                                                   const uint32_t* __restrict__ x2, float* __restrict__ y,
+                                                   const u32x4* __restrict__ x16, float* __restrict__ y,
                                                    unsigned* __restrict__ counters, float* __restrict__ partial,
                                                    int64_t np) {
-  extern __shared__ u32x4 xs4[];  // this workgroup's k range of x, as bf16 pairs, zero past K
-  const uint32_t* xs = reinterpret_cast<const uint32_t*>(xs4);
+  __shared__ u32x4 xs[kGemvWaves * kTileK / 8];  // 4 k tiles of x as bf16 pairs, zero past K
+  __shared__ float red[kGemvWaves][64];
   const int rt = blockIdx.x / groups;
   const int grp = blockIdx.x % groups;
-  // The wave index is uniform across the wavefront; saying so keeps the loop
-  // bounds in scalar registers.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int parts = groups * kGemvWaves;
-  const int wg_kt0 = part_begin(grp * kGemvWaves, nkt, parts);
-  const int wg_kt1 = part_begin(grp * kGemvWaves + kGemvWaves, nkt, parts);
-  const int kt0 = part_begin(grp * kGemvWaves + wave, nkt, parts);
-  const int kt1 = part_begin(grp * kGemvWaves + wave + 1, nkt, parts);
+  const int kt = grp * kGemvWaves + wave;
+  const bool has_tile = kt < nkt;
 
-  // Stage x for the workgroup's k range in LDS (16 bytes = 8 k per thread per step).
-  {
-    const int64_t k_base = (int64_t)wg_kt0 * kTileK;
-    const int n16 = (wg_kt1 - wg_kt0) * (kTileK / 8);
-    const u32x4* xg = reinterpret_cast<const u32x4*>(x2);
-    for (int i = threadIdx.x; i < n16; i += 256) {
-      const int64_t kk = k_base + 8 * (int64_t)i;
-      xs4[i] = kk < k ? xg[kk >> 3] : u32x4{0u, 0u, 0u, 0u};
-    }
+  // This wavefront's tile: all ten loads issued before anything waits.
+  u32x4 q[8], sa = {0u, 0u, 0u, 0u}, sb = {0u, 0u, 0u, 0u};
+  if (has_tile) {
+    const uint8_t* t = packed + ((size_t)rt * nkt + kt) * kTileBytes;
+    sa = load16(t + kScaleOffset + 32 * (lane & 31));
+    sb = load16(t + kScaleOffset + 32 * (lane & 31) + 16);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) q[c] = load16(t + c * 1024 + lane * 16);
   }
-
-  const uint8_t* base = packed + (size_t)rt * nkt * kTileBytes + lane * 16;
-  float acc = 0.0f;
-  TileRegs cur, nxt;
-  if (kt0 < kt1) load_tile(base + (size_t)kt0 * kTileBytes, cur);
+  // Stage the workgroup's 1024 activations (128 x 16 bytes).
+  if (threadIdx.x < kGemvWaves * kTileK / 8) {
+    const int64_t kk = (int64_t)grp * kGemvWaves * kTileK + 8 * (int64_t)threadIdx.x;
+    xs[threadIdx.x] = kk < k ? x16[kk >> 3] : u32x4{0u, 0u, 0u, 0u};
+  }
   __syncthreads();
-  for (int kt = kt0; kt < kt1; ++kt) {
-    if (kt + 1 < kt1) load_tile(base + (size_t)(kt + 1) * kTileBytes, nxt);
-    const uint32_t* xt = xs + (kt - wg_kt0) * (kTileK / 2);
-    float a = 0.0f;
-    a = chunk<0>(cur.q[0], xt + 0, cur.sc, a);
-    a = chunk<1>(cur.q[1], xt + 16, cur.sc, a);
-    a = chunk<2>(cur.q[2], xt + 32, cur.sc, a);
-    a = chunk<3>(cur.q[3], xt + 48, cur.sc, a);
-    a = chunk<4>(cur.q[4], xt + 64, cur.sc, a);
-    a = chunk<5>(cur.q[5], xt + 80, cur.sc, a);
-    a = chunk<6>(cur.q[6], xt + 96, cur.sc, a);
-    a = chunk<7>(cur.q[7], xt + 112, cur.sc, a);
-    acc += a;
-    cur = nxt;
-  }
 
-  __shared__ float red[kGemvWaves][64];
-  red[wave][lane] = acc;
+  float acc_a = 0.0f, acc_b = 0.0f;
+  if (has_tile) {
+    // Activations of chunk c for this lane: k = 32c + 8h (step 2c) and 32c + 16 + 8h (step 2c+1).
+    const u32x4* xt = xs + wave * (kTileK / 8) + (lane >> 5);
+#define NVFP4_GEMV_CHUNK(C) chunk<C>(q[C], xt[4 * C], xt[4 * C + 2], sa, sb, acc_a, acc_b);
+    NVFP4_GEMV_CHUNK(0) NVFP4_GEMV_CHUNK(1) NVFP4_GEMV_CHUNK(2) NVFP4_GEMV_CHUNK(3)
+    NVFP4_GEMV_CHUNK(4) NVFP4_GEMV_CHUNK(5) NVFP4_GEMV_CHUNK(6) NVFP4_GEMV_CHUNK(7)
+#undef NVFP4_GEMV_CHUNK
+  }
+  // Merge the k halves: afterwards lane l < 32 holds row l's two halves in
+  // (acc_a, acc_b) and lane l >= 32 holds row l's (row 32 + l%32).
+  uint32_t ua = __float_as_uint(acc_a), ub = __float_as_uint(acc_b);
+  swap_halves(ua, ub);
+  red[wave][lane] = __uint_as_float(ua) + __uint_as_float(ub);
   __syncthreads();
   const int64_t row = (int64_t)rt * kTileRows + lane;
   if (groups == 1) {
@@ -131,11 +112,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t* __restrict__ p
   if (wave == 0)
     store_coherent(partial + (size_t)grp * np + row, ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane]);
   if (arrive_last(counters + rt, (unsigned)groups)) {
-    if (wave == 0 && row < n) {
-      float s = 0.0f;
-      for (int g2 = 0; g2 < groups; ++g2) s += load_coherent(partial + (size_t)g2 * np + row);
-      y[row] = s * st;
-    }
+    if (wave == 0 && row < n) y[row] = sum_coherent(partial + row, (size_t)np, groups) * st;
   }
 }
 
@@ -146,29 +123,11 @@ __global__ void zero_f32_kernel(float* __restrict__ y, int64_t n) {
 
 }  // namespace
 
+// One wavefront per 256-k tile, four per workgroup: ceil(K / 1024) workgroups per row tile.
 SplitPlan gemv_plan(const Geometry& g) {
-  // Enough workgroups that all 256 CUs stream, each wave keeping >= 1 k tile.
-  const int64_t target = 512;
-  int64_t groups = (target + g.nrt - 1) / g.nrt;
-  int64_t max_groups = g.nkt / kGemvWaves;
-  if (max_groups < 1) max_groups = 1;
-  if (groups > max_groups) groups = max_groups;
-  if (groups > 16) groups = 16;
-  // At most 64 k tiles (32 KB of x) per workgroup in LDS.
-  const int64_t min_groups = (g.nkt + 63) / 64;
-  if (groups < min_groups) groups = min_groups;
+  int64_t groups = (g.nkt + kGemvWaves - 1) / kGemvWaves;
   if (groups < 1) groups = 1;
   return SplitPlan{(int)groups, (int)groups * kGemvWaves};
-}
-
-// Largest k range (in tiles) any workgroup stages.
-static int max_wg_tiles(const Geometry& g, const SplitPlan& p) {
-  int m = 0;
-  for (int grp = 0; grp < p.groups; ++grp) {
-    int t = part_begin(grp * kGemvWaves + kGemvWaves, (int)g.nkt, p.parts) - part_begin(grp * kGemvWaves, (int)g.nkt, p.parts);
-    if (t > m) m = t;
-  }
-  return m;
 }
 
 size_t gemv_workspace_bytes(const Geometry& g) {
@@ -187,10 +146,9 @@ hipError_t launch_gemv(const void* packed, const Geometry& g, float st, const ui
   SplitPlan p = gemv_plan(g);
   unsigned* counters = static_cast<unsigned*>(ws);
   float* partial = ws ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kCounterBytes) : nullptr;
-  const size_t smem = (size_t)max_wg_tiles(g, p) * (kTileK / 2) * 4;
-  hipLaunchKernelGGL(gemv_kernel, dim3((unsigned)(g.nrt * p.groups)), dim3(256), smem, s,
+  hipLaunchKernelGGL(gemv_kernel, dim3((unsigned)(g.nrt * p.groups)), dim3(256), 0, s,
                      static_cast<const uint8_t*>(packed), g.n, g.k, (int)g.nkt, p.groups, st,
-                     reinterpret_cast<const uint32_t*>(x), y, counters, partial, g.nrt * 64);
+                     reinterpret_cast<const u32x4*>(x), y, counters, partial, g.nrt * 64);
   return hipGetLastError();
 }
 

@@ -1,50 +1,57 @@
 // a1: repack canonical NVFP4 codes/scales into the tile layout (and back).
-// A pure byte permutation: every 16-byte lane slot of a tile is one 16-byte run
-// of a canonical row (32 codes, or 16 scale bytes), zero past the matrix edge.
+// A pure byte permutation into the tile layout described in device_common.h,
+// zero past the matrix edge.
 #include "device_common.h"
 #include "launchers.h"
 
 namespace nvfp4 {
 namespace {
 
-// Where tile slot `slot` (16 bytes) of the packed buffer comes from.
-struct SlotSource {
-  int64_t row;       // matrix row
-  int64_t first;     // first canonical byte within the row (codes) or first block (scales)
+// A 16-byte slot of the packed buffer is either four 4-byte pieces of code
+// rows (code region) or one 16-byte run of a scale row (scale region).
+struct Piece {
+  int64_t row;    // matrix row
+  int64_t first;  // first canonical byte within the row
+  int bytes;      // 4 (codes) or 16 (scales)
   bool is_scale;
 };
 
-__device__ __forceinline__ SlotSource slot_source(int64_t slot, int64_t nkt) {
-  int64_t tile = slot / (kTileBytes / 16);
-  int within = (int)(slot % (kTileBytes / 16));  // 0..575
-  int64_t rt = tile / nkt, kt = tile % nkt;
-  SlotSource s;
+__device__ __forceinline__ Piece slot_piece(int64_t slot, int64_t nkt, int d) {
+  const int64_t tile = slot / (kTileBytes / 16);
+  const int within = (int)(slot % (kTileBytes / 16));  // 0..575
+  const int64_t rt = tile / nkt, kt = tile % nkt;
+  Piece p;
   if (within < kTileCodeBytes / 16) {
-    int c = within / 64, l = within % 64;
-    s.row = rt * kTileRows + l;
-    s.first = (kt * kTileK + c * kChunkK) / 2;
-    s.is_scale = false;
+    const int c = within / 64, l = within % 64, r = l & 31, h = l >> 5;
+    p.row = rt * kTileRows + r + 32 * (d & 1);
+    p.first = (kt * kTileK + c * kChunkK + 8 * h + 16 * (d >> 1)) / 2;
+    p.bytes = 4;
+    p.is_scale = false;
   } else {
-    int l = within - kTileCodeBytes / 16;
-    s.row = rt * kTileRows + l;
-    s.first = kt * (kTileK / 16);
-    s.is_scale = true;
+    const int sl = within - kTileCodeBytes / 16;  // 0..63
+    p.row = rt * kTileRows + (sl >> 1) + 32 * (sl & 1);
+    p.first = kt * (kTileK / 16);
+    p.bytes = 16;
+    p.is_scale = true;
   }
-  return s;
+  return p;
 }
 
 __global__ void pack_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                             int64_t n, int64_t k, int64_t nkt, int64_t slots, uint8_t* __restrict__ packed) {
-  int64_t slot = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t slot = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (slot >= slots) return;
-  SlotSource s = slot_source(slot, nkt);
-  const int64_t row_bytes = s.is_scale ? k / 16 : k / 2;
-  const uint8_t* src = (s.is_scale ? scales : codes) + s.row * row_bytes;
   uint8_t out[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    int64_t col = s.first + i;
-    out[i] = (s.row < n && col < row_bytes) ? src[col] : (uint8_t)0;
+  const Piece p0 = slot_piece(slot, nkt, 0);
+  const int npieces = p0.is_scale ? 1 : 4;
+  for (int d = 0; d < npieces; ++d) {
+    const Piece p = d == 0 ? p0 : slot_piece(slot, nkt, d);
+    const int64_t row_bytes = p.is_scale ? k / 16 : k / 2;
+    const uint8_t* src = (p.is_scale ? scales : codes) + p.row * row_bytes;
+    for (int i = 0; i < p.bytes; ++i) {
+      const int64_t col = p.first + i;
+      out[4 * d + i] = (p.row < n && col < row_bytes) ? src[col] : (uint8_t)0;
+    }
   }
   uint4 v;
   v.x = out[0] | (out[1] << 8) | (out[2] << 16) | ((uint32_t)out[3] << 24);
@@ -56,18 +63,22 @@ __global__ void pack_kernel(const uint8_t* __restrict__ codes, const uint8_t* __
 
 __global__ void unpack_kernel(const uint8_t* __restrict__ packed, int64_t n, int64_t k, int64_t nkt,
                               int64_t slots, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
-  int64_t slot = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t slot = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (slot >= slots) return;
-  SlotSource s = slot_source(slot, nkt);
-  if (s.row >= n) return;
-  const int64_t row_bytes = s.is_scale ? k / 16 : k / 2;
-  uint8_t* dst = (s.is_scale ? scales : codes) + s.row * row_bytes;
-  uint4 v = *reinterpret_cast<const uint4*>(packed + slot * 16);
-  uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    int64_t col = s.first + i;
-    if (col < row_bytes) dst[col] = (uint8_t)(w[i / 4] >> (8 * (i % 4)));
+  const uint4 v = *reinterpret_cast<const uint4*>(packed + slot * 16);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  const Piece p0 = slot_piece(slot, nkt, 0);
+  const int npieces = p0.is_scale ? 1 : 4;
+  for (int d = 0; d < npieces; ++d) {
+    const Piece p = d == 0 ? p0 : slot_piece(slot, nkt, d);
+    if (p.row >= n) continue;
+    const int64_t row_bytes = p.is_scale ? k / 16 : k / 2;
+    uint8_t* dst = (p.is_scale ? scales : codes) + p.row * row_bytes;
+    for (int i = 0; i < p.bytes; ++i) {
+      const int64_t col = p.first + i;
+      const int byte = 4 * d + i;
+      if (col < row_bytes) dst[col] = (uint8_t)(w[byte / 4] >> (8 * (byte % 4)));
+    }
   }
 }
 

@@ -41,12 +41,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(const uint8_t* __restrict_
   const int rt0 = blockIdx.y * 2;  // first of the two 64-row tiles
   const int64_t n0 = (int64_t)rt0 * kTileRows;
 
-  // Weight loader: thread -> (row tile rtl, chunk parity cp, lane) : 32 codes.
+  // Weight loader: thread -> (row tile rtl, chunk parity cp, lane): one 16-byte
+  // slot of the tile layout = rows r and 32 + r (r = lane % 32) x two 8-k groups.
   const int w_rtl = tid >> 7;
   const int w_cp = (tid >> 6) & 1;
   const bool w_tile_ok = (int64_t)(rt0 + w_rtl) * kTileRows < n;
-  const uint8_t* w_base = packed + (size_t)(rt0 + w_rtl) * nkt * kTileBytes + lane * 16;
-  const int w_lds_row = w_rtl * 64 + lane;
+  const uint8_t* w_base = packed + (size_t)(rt0 + w_rtl) * nkt * kTileBytes;
+  const int w_r = lane & 31, w_h = lane >> 5;
   // Activation loader: thread -> (row tid/2, k half tid%2): 32 bf16.
   const int x_row = tid >> 1;
   const int x_half = tid & 1;
@@ -54,12 +55,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(const uint8_t* __restrict_
   const uint16_t* x_base = x + (x_ok ? (m0 + x_row) : 0) * ldx + 32 * x_half;
 
   const int nslabs = nkt * (kTileK / kBK);
-  u32x4 sc = {0u, 0u, 0u, 0u};
+  u32x4 sa = {0u, 0u, 0u, 0u}, sb = {0u, 0u, 0u, 0u};
 
   auto load = [&](int slab, Stage& st_) {
     const int kt = slab >> 2, sub = slab & 3;
     const int64_t kk = (int64_t)slab * kBK + 32 * x_half;
-    if (w_tile_ok) st_.w = load16(w_base + (size_t)kt * kTileBytes + (2 * sub + w_cp) * 1024);
+    if (w_tile_ok) st_.w = load16(w_base + (size_t)kt * kTileBytes + (2 * sub + w_cp) * 1024 + lane * 16);
     else st_.w = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -80,27 +81,28 @@ __global__ __launch_bounds__(256) void prefill_kernel(const uint8_t* __restrict_
   if (nslabs > 0) load(0, cur);
   for (int slab = 0; slab < nslabs; ++slab) {
     const int kt = slab >> 2, sub = slab & 3;
-    if (sub == 0) sc = w_tile_ok ? load16(w_base + (size_t)kt * kTileBytes + kTileCodeBytes) : u32x4{0u, 0u, 0u, 0u};
+    if (sub == 0 && w_tile_ok) {
+      sa = load16(w_base + (size_t)kt * kTileBytes + kScaleOffset + 32 * w_r);
+      sb = load16(w_base + (size_t)kt * kTileBytes + kScaleOffset + 32 * w_r + 16);
+    }
     __syncthreads();  // previous slab fully consumed
     {
-      // Dequantise 32 weights: blocks 2c, 2c+1 of this k tile, c = 2*sub + cp.
+      // Dequantise the slot: dword d holds row r + 32*(d&1), k steps 2c + (d>>1)
+      // of this k tile (c = 2*sub + cp), 8 codes at k offset 8h.
       const int c = 2 * sub + w_cp;
-      const uint32_t sw = sc[c >> 1];
-      const float s0 = __builtin_amdgcn_cvt_f32_fp8(sw >> (8 * ((2 * c) & 3)), 0);
-      const float s1 = __builtin_amdgcn_cvt_f32_fp8(sw >> (8 * ((2 * c + 1) & 3)), 0);
-      uint32_t out[16];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const float s = d < 2 ? s0 : s1;
+        const uint32_t sw = (d & 1) ? sb[c >> 1] : sa[c >> 1];
+        const float s = __builtin_amdgcn_cvt_f32_fp8(sw >> (8 * ((2 * c + (d >> 1)) & 3)), 0);
         f32x2 v;
-        v = e2m1x2<0>(cur.w[d]); out[4 * d + 0] = pack_bf16x2(v.x * s, v.y * s);
-        v = e2m1x2<1>(cur.w[d]); out[4 * d + 1] = pack_bf16x2(v.x * s, v.y * s);
-        v = e2m1x2<2>(cur.w[d]); out[4 * d + 2] = pack_bf16x2(v.x * s, v.y * s);
-        v = e2m1x2<3>(cur.w[d]); out[4 * d + 3] = pack_bf16x2(v.x * s, v.y * s);
+        u32x4 o;
+        v = e2m1x2<0>(cur.w[d]); o[0] = pack_exact_bf16x2(v.x * s, v.y * s);
+        v = e2m1x2<1>(cur.w[d]); o[1] = pack_exact_bf16x2(v.x * s, v.y * s);
+        v = e2m1x2<2>(cur.w[d]); o[2] = pack_exact_bf16x2(v.x * s, v.y * s);
+        v = e2m1x2<3>(cur.w[d]); o[3] = pack_exact_bf16x2(v.x * s, v.y * s);
+        const int lrow = w_rtl * 64 + w_r + 32 * (d & 1);
+        *reinterpret_cast<u32x4*>(lds_w + lrow * kLdsStride + 32 * w_cp + 8 * w_h + 16 * (d >> 1)) = o;
       }
-      u32x4* dst = reinterpret_cast<u32x4*>(lds_w + w_lds_row * kLdsStride + 32 * w_cp);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = u32x4{out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]};
       u32x4* xdst = reinterpret_cast<u32x4*>(lds_x + x_row * kLdsStride + 32 * x_half);
 #pragma unroll
       for (int i = 0; i < 4; ++i) xdst[i] = cur.x[i];

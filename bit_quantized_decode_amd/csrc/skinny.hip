@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(const uint8_t* __restrict__
                                                      const uint16_t* __restrict__ x, int64_t m, int64_t ldx,
                                                      void* __restrict__ y, int64_t ldy, int y_bf16,
                                                      unsigned* __restrict__ counters, float* __restrict__ partial,
-                                                     int64_t np) {
+                                                     int64_t np_tiles) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_x[2 * kXTileElems];
   const int rg = blockIdx.x / groups;
   const int grp = blockIdx.x % groups;
@@ -86,35 +86,54 @@ __global__ __launch_bounds__(256) void skinny_kernel(const uint8_t* __restrict__
     }
     return;
   }
-  // Split k: partial[grp][tok][row] for this wave's 64 rows.
+  // Split k: partial[grp][rt][i][lane] = accumulator element i of this lane
+  // (i < 16: acc_a, else acc_b) -- each element is one contiguous 256-byte run,
+  // so the write-through stores go out as full lines.
+  float* mine = partial + (((size_t)grp * np_tiles + rt) * 32) * 64 + lane;
   if (rt < nrt) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const f32x16& a = h ? acc_b : acc_a;
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int64_t row = (int64_t)rt * kTileRows + acc_row(h, 4 * e4, lane);
-        float* pp = partial + ((size_t)grp * 32 + tok) * np + row;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) store_coherent(pp + i, a[4 * e4 + i]);
-      }
+    for (int i = 0; i < 16; ++i) {
+      store_coherent(mine + (size_t)i * 64, acc_a[i]);
+      store_coherent(mine + (size_t)(16 + i) * 64, acc_b[i]);
     }
   }
   if (!arrive_last(counters + rg, (unsigned)groups)) return;
-  // Last to arrive: thread t sums activation row t/8, rows (t%8)*32 .. +32 of the group.
-  const int t_tok = threadIdx.x >> 3;
-  if (t_tok >= m) return;
-  const int64_t row0 = (int64_t)rg * kWaves * kTileRows + (threadIdx.x & 7) * 32;
-  if (row0 >= n) return;
+  // Last to arrive: each wavefront adds up its own tile's partials over the
+  // groups in index order, two groups per round trip, and stores as above.
+  if (rt >= nrt || tok >= m) return;
+  f32x16 sa = {}, sb = {};
+  const size_t gstride = (size_t)np_tiles * 32 * 64;
+  const float* base = partial + ((size_t)rt * 32) * 64 + lane;
+  for (int g0 = 0; g0 < groups; g0 += 2) {
+    const int g1 = g0 + 1 < groups ? g0 + 1 : g0;
+    float v0[32], v1[32];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int g2 = 0; g2 < groups; ++g2) {
-      const float* pp = partial + ((size_t)g2 * 32 + t_tok) * np + row0 + 4 * q;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s4[i] += load_coherent(pp + i);
+    for (int i = 0; i < 32; ++i) {
+      v0[i] = load_coherent(base + g0 * gstride + (size_t)i * 64);
+      v1[i] = load_coherent(base + g1 * gstride + (size_t)i * 64);
     }
-    store4(y, y_bf16, ldy, t_tok, row0 + 4 * q, n, vec, s4[0] * st, s4[1] * st, s4[2] * st, s4[3] * st);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sa[i] += v0[i];
+      sb[i] += v0[16 + i];
+    }
+    if (g0 + 1 < groups) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sa[i] += v1[i];
+        sb[i] += v1[16 + i];
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const f32x16& a = h ? sb : sa;
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const int64_t row = (int64_t)rt * kTileRows + acc_row(h, 4 * e4, lane);
+      store4(y, y_bf16, ldy, tok, row, n, vec, a[4 * e4] * st, a[4 * e4 + 1] * st, a[4 * e4 + 2] * st,
+             a[4 * e4 + 3] * st);
+    }
   }
 }
 
@@ -137,7 +156,7 @@ SplitPlan skinny_plan(const Geometry& g) {
   int64_t max_groups = g.nkt / 2;
   if (max_groups < 1) max_groups = 1;
   if (groups > max_groups) groups = max_groups;
-  if (groups > 32) groups = 32;
+  if (groups > 8) groups = 8;
   if (groups < 1) groups = 1;
   return SplitPlan{(int)groups, (int)groups};
 }
@@ -146,7 +165,7 @@ size_t skinny_workspace_bytes(const Geometry& g) {
   SplitPlan p = skinny_plan(g);
   if (p.groups <= 1) return 0;
   const size_t nrg = (size_t)(g.nrt + kWaves - 1) / kWaves;
-  return kCounterBytes + (size_t)p.groups * 32 * nrg * kWaves * 64 * 4;
+  return kCounterBytes + (size_t)p.groups * nrg * kWaves * 32 * 64 * 4;
 }
 
 hipError_t launch_zero_rows(void* y, int64_t m, int64_t n, int64_t ldy, bool y_bf16, hipStream_t s) {
@@ -167,7 +186,7 @@ hipError_t launch_skinny(const void* packed, const Geometry& g, float st, const 
   float* partial = ws ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kCounterBytes) : nullptr;
   hipLaunchKernelGGL(skinny_kernel, dim3((unsigned)(nrg * p.groups)), dim3(256), 0, s,
                      static_cast<const uint8_t*>(packed), g.n, g.k, (int)g.nkt, (int)g.nrt, p.groups, st, x, m, ldx,
-                     y, ldy, y_bf16 ? 1 : 0, counters, partial, nrg * kWaves * 64);
+                     y, ldy, y_bf16 ? 1 : 0, counters, partial, nrg * kWaves);
   return hipGetLastError();
 }
 
