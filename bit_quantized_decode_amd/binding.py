@@ -26,7 +26,8 @@ NVFP4_BF16 = 1
 EXPORTED = (
     "nvfp4_abi_version", "nvfp4_status_str", "nvfp4_last_error", "nvfp4_packed_bytes", "nvfp4_pack",
     "nvfp4_unpack", "nvfp4_gemv_workspace_bytes", "nvfp4_gemv", "nvfp4_gemm_workspace_bytes", "nvfp4_gemm",
-    "nvfp4_moe_workspace_bytes", "nvfp4_moe_grouped",
+    "nvfp4_gemv_batched_workspace_bytes", "nvfp4_gemv_batched", "nvfp4_gemm_batched_workspace_bytes",
+    "nvfp4_gemm_batched", "nvfp4_moe_workspace_bytes", "nvfp4_moe_grouped",
 )
 
 
@@ -34,6 +35,15 @@ class Nvfp4Error(RuntimeError):
     def __init__(self, status, message):
         super().__init__(message)
         self.status = status
+
+
+class Problem(ctypes.Structure):
+    """Mirror of struct nvfp4_problem."""
+    _fields_ = [
+        ("packed", ctypes.c_void_p), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+        ("tensor_scale", ctypes.c_float), ("x", ctypes.c_void_p), ("ldx", ctypes.c_int64),
+        ("y", ctypes.c_void_p), ("ldy", ctypes.c_int64),
+    ]
 
 
 class MoeArgs(ctypes.Structure):
@@ -77,6 +87,10 @@ def lib():
         "nvfp4_gemv": (I, [P, i64, i64, ctypes.c_float, P, P, P, sz, P]),
         "nvfp4_gemm_workspace_bytes": (I, [i64, i64, i64, ctypes.POINTER(sz)]),
         "nvfp4_gemm": (I, [P, i64, i64, ctypes.c_float, P, i64, i64, P, i64, I, P, sz, P]),
+        "nvfp4_gemv_batched_workspace_bytes": (I, [ctypes.POINTER(Problem), I, ctypes.POINTER(sz)]),
+        "nvfp4_gemv_batched": (I, [ctypes.POINTER(Problem), I, P, sz, P]),
+        "nvfp4_gemm_batched_workspace_bytes": (I, [ctypes.POINTER(Problem), I, i64, ctypes.POINTER(sz)]),
+        "nvfp4_gemm_batched": (I, [ctypes.POINTER(Problem), I, i64, I, P, sz, P]),
         "nvfp4_moe_workspace_bytes": (I, [ctypes.POINTER(MoeArgs), ctypes.POINTER(sz)]),
         "nvfp4_moe_grouped": (I, [ctypes.POINTER(MoeArgs), P]),
     }
@@ -184,6 +198,43 @@ def gemm(packed, n, k, tensor_scale, x, y=None, y_dtype=torch.bfloat16, ws=None,
     check(lib().nvfp4_gemm(_ptr(packed), n, k, float(tensor_scale), _ptr(x), m, x.stride(0), _ptr(y), y.stride(0),
                            dt, _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
     return y
+
+
+def problems(items):
+    """ctypes array of Problem from (packed, n, k, tensor_scale, x, y) tuples of tensors."""
+    arr = (Problem * len(items))()
+    for i, (packed, n, k, st, x, y) in enumerate(items):
+        arr[i].packed = packed.data_ptr()
+        arr[i].n, arr[i].k, arr[i].tensor_scale = n, k, float(st)
+        arr[i].x = x.data_ptr()
+        arr[i].ldx = x.stride(0) if x.dim() == 2 else k
+        arr[i].y = y.data_ptr()
+        arr[i].ldy = y.stride(0) if y.dim() == 2 else n
+    return arr
+
+
+def gemv_batched(items, ws=None, stream=None):
+    """Several GEMVs in one launch: items = [(packed, n, k, tensor_scale, x [k], y fp32 [n]), ...]."""
+    arr = problems(items)
+    L = lib()
+    need = ctypes.c_size_t()
+    check(L.nvfp4_gemv_batched_workspace_bytes(arr, len(items), ctypes.byref(need)))
+    if ws is None and items:
+        ws = workspace(need.value, items[0][4].device)
+    check(L.nvfp4_gemv_batched(arr, len(items), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def gemm_batched(items, ws=None, stream=None):
+    """Several GEMMs sharing m and the output dtype: items = [(packed, n, k, tensor_scale, x [m][ldx], y [m][ldy])]."""
+    arr = problems(items)
+    L = lib()
+    m = items[0][4].shape[0] if items else 0
+    dt = NVFP4_BF16 if items and items[0][5].dtype == torch.bfloat16 else NVFP4_F32
+    need = ctypes.c_size_t()
+    check(L.nvfp4_gemm_batched_workspace_bytes(arr, len(items), m, ctypes.byref(need)))
+    if ws is None and items:
+        ws = workspace(need.value, items[0][4].device)
+    check(L.nvfp4_gemm_batched(arr, len(items), m, dt, _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def moe_args(**kw):

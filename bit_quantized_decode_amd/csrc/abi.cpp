@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <vector>
 
 #include "../../include/nvfp4.h"
 #include "launchers.h"
@@ -187,6 +188,40 @@ int nvfp4_gemm(const void* packed, int64_t n, int64_t k, float tensor_scale, con
   NVFP4_GUARD_END
 }
 
+// Validate a batch and convert it; `gemm_m` < 0 for GEMV batches.
+static int check_batch(const nvfp4_problem* pr, int count, int64_t gemm_m, int y_dtype, bool need_buffers,
+                       nvfp4::Problem* out) {
+  if (count < 0) return fail(NVFP4_ERR_ARG, "count=%d is negative", count);
+  if (count > 0 && !pr) return fail(NVFP4_ERR_NULL, "problems is NULL");
+  if (gemm_m >= 0 && y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16)
+    return fail(NVFP4_ERR_DTYPE, "unknown y_dtype %d", y_dtype);
+  if (gemm_m > kMaxDim) return fail(NVFP4_ERR_SHAPE, "m=%lld out of range", (long long)gemm_m);
+  int64_t tiles = 0;
+  for (int i = 0; i < count; ++i) {
+    const nvfp4_problem& q = pr[i];
+    NVFP4_TRY(check_shape(q.n, q.k));
+    NVFP4_TRY(check_rows(q.n));
+    if (i % nvfp4::kMaxBatch == 0) tiles = 0;
+    tiles += (q.n + 63) / 64;
+    if (tiles > nvfp4::kCounterSlots)
+      return fail(NVFP4_ERR_SHAPE, "a launch of %d problems exceeds %lld row tiles", nvfp4::kMaxBatch,
+                  (long long)nvfp4::kCounterSlots);
+    out[i] = nvfp4::Problem{q.packed, q.n, q.k, q.tensor_scale, q.x, q.ldx, q.y, q.ldy};
+    if (!need_buffers || q.n == 0 || gemm_m == 0) continue;
+    if (gemm_m > 0) {
+      if (q.ldx < q.k || q.ldx % 8 != 0)
+        return fail(NVFP4_ERR_SHAPE, "problem %d: ldx=%lld must be >= k and a multiple of 8", i, (long long)q.ldx);
+      if (q.ldy < q.n) return fail(NVFP4_ERR_SHAPE, "problem %d: ldy=%lld must be >= n", i, (long long)q.ldy);
+    }
+    if (!q.y || (q.k > 0 && (!q.packed || !q.x))) return fail(NVFP4_ERR_NULL, "problem %d: NULL pointer", i);
+    if (!aligned16(q.y) || (q.k > 0 && (!aligned16(q.packed) || !aligned16(q.x))))
+      return fail(NVFP4_ERR_ALIGN, "problem %d: packed, x and y must be 16-byte aligned", i);
+    for (int j = 0; j < i; ++j)
+      if (pr[j].y == q.y && pr[j].n > 0) return fail(NVFP4_ERR_ARG, "problems %d and %d share an output", j, i);
+  }
+  return NVFP4_OK;
+}
+
 static int check_moe(const nvfp4_moe_args* a, bool need_buffers) {
   if (!a) return fail(NVFP4_ERR_NULL, "args is NULL");
   if (a->tokens < 0 || a->hidden <= 0 || a->inter <= 0 || a->experts <= 0)
@@ -224,6 +259,80 @@ static int check_moe(const nvfp4_moe_args* a, bool need_buffers) {
   const size_t need = nvfp4::moe_workspace_bytes(a->tokens, a->experts, a->top_k, a->hidden, a->inter);
   if (a->workspace_bytes < need) return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, a->workspace_bytes);
   return NVFP4_OK;
+}
+
+int nvfp4_gemv_batched_workspace_bytes(const nvfp4_problem* problems, int count, size_t* bytes) {
+  NVFP4_GUARD_BEGIN
+  if (!bytes) return fail(NVFP4_ERR_NULL, "bytes is NULL");
+  std::vector<nvfp4::Problem> pr((size_t)(count > 0 ? count : 0));
+  NVFP4_TRY(check_batch(problems, count, -1, NVFP4_F32, false, pr.data()));
+  *bytes = nvfp4::gemv_batch_workspace_bytes(pr.data(), count);
+  return ok();
+  NVFP4_GUARD_END
+}
+
+int nvfp4_gemv_batched(const nvfp4_problem* problems, int count, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  NVFP4_GUARD_BEGIN
+  std::vector<nvfp4::Problem> pr((size_t)(count > 0 ? count : 0));
+  NVFP4_TRY(check_batch(problems, count, -1, NVFP4_F32, true, pr.data()));
+  if (count == 0) return ok();
+  const size_t need = nvfp4::gemv_batch_workspace_bytes(pr.data(), count);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace ? workspace_bytes : 0);
+  if (need > 0 && !aligned16(workspace)) return fail(NVFP4_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return hip_status(nvfp4::launch_gemv_batch(pr.data(), count, workspace, (hipStream_t)stream), "gemv batch launch");
+  NVFP4_GUARD_END
+}
+
+int nvfp4_gemm_batched_workspace_bytes(const nvfp4_problem* problems, int count, int64_t m, size_t* bytes) {
+  NVFP4_GUARD_BEGIN
+  if (!bytes) return fail(NVFP4_ERR_NULL, "bytes is NULL");
+  if (m < 0) return fail(NVFP4_ERR_SHAPE, "m=%lld is negative", (long long)m);
+  std::vector<nvfp4::Problem> pr((size_t)(count > 0 ? count : 0));
+  NVFP4_TRY(check_batch(problems, count, m, NVFP4_F32, false, pr.data()));
+  size_t need = 0;
+  if (m <= 32) {
+    need = nvfp4::skinny_batch_workspace_bytes(pr.data(), count);
+  } else {
+    for (int i = 0; i < count; ++i) {
+      const size_t b = nvfp4::prefill_workspace_bytes(m, nvfp4::geometry(pr[i].n, pr[i].k));
+      if (b > need) need = b;
+    }
+  }
+  *bytes = need;
+  return ok();
+  NVFP4_GUARD_END
+}
+
+int nvfp4_gemm_batched(const nvfp4_problem* problems, int count, int64_t m, int y_dtype, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  NVFP4_GUARD_BEGIN
+  if (m < 0) return fail(NVFP4_ERR_SHAPE, "m=%lld is negative", (long long)m);
+  std::vector<nvfp4::Problem> pr((size_t)(count > 0 ? count : 0));
+  NVFP4_TRY(check_batch(problems, count, m, y_dtype, true, pr.data()));
+  if (count == 0 || m == 0) return ok();
+  const bool bf16 = y_dtype == NVFP4_BF16;
+  if (m <= 32) {
+    const size_t need = nvfp4::skinny_batch_workspace_bytes(pr.data(), count);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+      return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace ? workspace_bytes : 0);
+    if (need > 0 && !aligned16(workspace)) return fail(NVFP4_ERR_ALIGN, "workspace must be 16-byte aligned");
+    return hip_status(nvfp4::launch_skinny_batch(pr.data(), count, m, bf16, workspace, (hipStream_t)stream),
+                      "skinny gemm batch launch");
+  }
+  for (int i = 0; i < count; ++i) {
+    const nvfp4::Geometry g = nvfp4::geometry(pr[i].n, pr[i].k);
+    const size_t need = nvfp4::prefill_workspace_bytes(m, g);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+      return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace ? workspace_bytes : 0);
+    if (g.n == 0) continue;
+    hipError_t e = nvfp4::launch_prefill(pr[i].packed, g, pr[i].st, pr[i].x, m, pr[i].ldx, pr[i].y, pr[i].ldy, bf16,
+                                         workspace, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "prefill gemm launch");
+  }
+  return ok();
+  NVFP4_GUARD_END
 }
 
 int nvfp4_moe_workspace_bytes(const nvfp4_moe_args* args, size_t* bytes) {

@@ -59,15 +59,36 @@ __device__ __forceinline__ void chunk(u32x4 q, u32x4 xa, u32x4 xb, u32x4 sa, u32
   acc_b = fmaf(dot8(q[3], xb), e4m3<(2 * C + 1) % 4>(sb[C / 2]), acc_b);
 }
 
-__global__ __launch_bounds__(256) void gemv_kernel(const uint8_t* __restrict__ packed, int64_t n, int64_t k,
-                                                   int nkt, int groups, float st,
-                                                   const u32x4* __restrict__ x16, float* __restrict__ y,
-                                                   unsigned* __restrict__ counters, float* __restrict__ partial,
-                                                   int64_t np) {
+// A batch of up to kMaxBatch GEMVs in one launch; workgroups [wg_begin[p],
+// wg_begin[p+1]) belong to problem p.
+struct GemvBatch {
+  int count;
+  int wg_begin[kMaxBatch + 1];
+  const uint8_t* packed[kMaxBatch];
+  const u32x4* x[kMaxBatch];
+  float* y[kMaxBatch];
+  int64_t n[kMaxBatch];
+  int64_t k[kMaxBatch];
+  int nkt[kMaxBatch];
+  int groups[kMaxBatch];
+  float st[kMaxBatch];
+  int counter_base[kMaxBatch];
+  int64_t partial_base[kMaxBatch];
+};
+
+__global__ __launch_bounds__(256) void gemv_kernel(const GemvBatch b, unsigned* __restrict__ counters,
+                                                   float* __restrict__ partial_all) {
   __shared__ u32x4 xs[kGemvWaves * kTileK / 8];  // 4 k tiles of x as bf16 pairs, zero past K
   __shared__ float red[kGemvWaves][64];
-  const int rt = blockIdx.x / groups;
-  const int grp = blockIdx.x % groups;
+  int p = 0;
+  while (p + 1 < b.count && (int)blockIdx.x >= b.wg_begin[p + 1]) ++p;
+  const uint8_t* __restrict__ packed = b.packed[p];
+  const u32x4* __restrict__ x16 = b.x[p];
+  const int64_t n = b.n[p], k = b.k[p];
+  const int nkt = b.nkt[p], groups = b.groups[p];
+  const int local = (int)blockIdx.x - b.wg_begin[p];
+  const int rt = local / groups;
+  const int grp = local % groups;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int kt = grp * kGemvWaves + wave;
@@ -105,13 +126,17 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t* __restrict__ p
   red[wave][lane] = __uint_as_float(ua) + __uint_as_float(ub);
   __syncthreads();
   const int64_t row = (int64_t)rt * kTileRows + lane;
+  const float st = b.st[p];
+  float* __restrict__ y = b.y[p];
   if (groups == 1) {
     if (wave == 0 && row < n) y[row] = (((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane]) * st;
     return;
   }
+  const int64_t np = (int64_t)((n + 63) / 64) * 64;
+  float* partial = partial_all + b.partial_base[p];
   if (wave == 0)
     store_coherent(partial + (size_t)grp * np + row, ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane]);
-  if (arrive_last(counters + rt, (unsigned)groups)) {
+  if (arrive_last(counters + b.counter_base[p] + rt, (unsigned)groups)) {
     if (wave == 0 && row < n) y[row] = sum_coherent(partial + row, (size_t)np, groups) * st;
   }
 }
@@ -136,20 +161,66 @@ size_t gemv_workspace_bytes(const Geometry& g) {
   return kCounterBytes + (size_t)p.groups * (size_t)g.nrt * 64 * 4;
 }
 
+size_t gemv_batch_workspace_bytes(const Problem* p, int count) {
+  // Each launch of up to kMaxBatch problems lays out its partials from offset 0.
+  size_t worst = 0;
+  for (int b0 = 0; b0 < count; b0 += kMaxBatch) {
+    size_t part = 0;
+    for (int i = b0; i < count && i < b0 + kMaxBatch; ++i) {
+      const Geometry g = geometry(p[i].n, p[i].k);
+      const SplitPlan pl = gemv_plan(g);
+      if (pl.groups > 1 && g.n > 0 && g.k > 0) part += (size_t)pl.groups * (size_t)g.nrt * 64 * 4;
+    }
+    if (part > worst) worst = part;
+  }
+  return worst ? kCounterBytes + worst : 0;
+}
+
+hipError_t launch_gemv_batch(const Problem* p, int count, void* ws, hipStream_t s) {
+  for (int b0 = 0; b0 < count; b0 += kMaxBatch) {
+    GemvBatch b = {};
+    int wgs = 0, counters = 0;
+    int64_t pbase = 0;
+    for (int i = b0; i < count && i < b0 + kMaxBatch; ++i) {
+      const Geometry g = geometry(p[i].n, p[i].k);
+      if (g.n == 0) continue;
+      if (g.k == 0) {
+        hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)((g.n + 255) / 256)), dim3(256), 0, s,
+                           static_cast<float*>(p[i].y), g.n);
+        continue;
+      }
+      const SplitPlan pl = gemv_plan(g);
+      const int j = b.count++;
+      b.wg_begin[j] = wgs;
+      b.packed[j] = static_cast<const uint8_t*>(p[i].packed);
+      b.x[j] = reinterpret_cast<const u32x4*>(p[i].x);
+      b.y[j] = static_cast<float*>(p[i].y);
+      b.n[j] = g.n;
+      b.k[j] = g.k;
+      b.nkt[j] = (int)g.nkt;
+      b.groups[j] = pl.groups;
+      b.st[j] = p[i].st;
+      b.counter_base[j] = counters;
+      b.partial_base[j] = pbase;
+      wgs += (int)(g.nrt * pl.groups);
+      if (pl.groups > 1) {
+        counters += (int)g.nrt;
+        pbase += (int64_t)pl.groups * g.nrt * 64;
+      }
+    }
+    if (b.count == 0) continue;
+    b.wg_begin[b.count] = wgs;
+    unsigned* cnt = static_cast<unsigned*>(ws);
+    float* partial = ws ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kCounterBytes) : nullptr;
+    hipLaunchKernelGGL(gemv_kernel, dim3((unsigned)wgs), dim3(256), 0, s, b, cnt, partial);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_gemv(const void* packed, const Geometry& g, float st, const uint16_t* x, float* y, void* ws,
                        hipStream_t s) {
-  if (g.n == 0) return hipSuccess;
-  if (g.k == 0) {
-    hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)((g.n + 255) / 256)), dim3(256), 0, s, y, g.n);
-    return hipGetLastError();
-  }
-  SplitPlan p = gemv_plan(g);
-  unsigned* counters = static_cast<unsigned*>(ws);
-  float* partial = ws ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kCounterBytes) : nullptr;
-  hipLaunchKernelGGL(gemv_kernel, dim3((unsigned)(g.nrt * p.groups)), dim3(256), 0, s,
-                     static_cast<const uint8_t*>(packed), g.n, g.k, (int)g.nkt, p.groups, st,
-                     reinterpret_cast<const u32x4*>(x), y, counters, partial, g.nrt * 64);
-  return hipGetLastError();
+  Problem pr{packed, g.n, g.k, st, x, 0, y, 0};
+  return launch_gemv_batch(&pr, 1, ws, s);
 }
 
 }  // namespace nvfp4

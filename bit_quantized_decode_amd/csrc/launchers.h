@@ -45,6 +45,23 @@ size_t gemv_workspace_bytes(const Geometry& g);
 size_t skinny_workspace_bytes(const Geometry& g);
 size_t prefill_workspace_bytes(int64_t m, const Geometry& g);
 
+// One product of a batched launch (host view).
+struct Problem {
+  const void* packed;
+  int64_t n, k;
+  float st;
+  const uint16_t* x;
+  int64_t ldx;
+  void* y;
+  int64_t ldy;
+};
+constexpr int kMaxBatch = 8;  // problems per kernel launch (more are split into launches)
+
+size_t gemv_batch_workspace_bytes(const Problem* p, int count);
+hipError_t launch_gemv_batch(const Problem* p, int count, void* ws, hipStream_t s);
+size_t skinny_batch_workspace_bytes(const Problem* p, int count);
+hipError_t launch_skinny_batch(const Problem* p, int count, int64_t m, bool y_bf16, void* ws, hipStream_t s);
+
 hipError_t launch_pack(const uint8_t* codes, const uint8_t* scales, const Geometry& g, void* packed,
                        hipStream_t s);
 hipError_t launch_unpack(const void* packed, const Geometry& g, uint8_t* codes, uint8_t* scales,

@@ -49,26 +49,51 @@ __device__ __forceinline__ void store4(void* y, int y_bf16, int64_t ldy, int64_t
   }
 }
 
-// Workgroup (row group rg, k part grp): four 64-row tiles 4*rg .. 4*rg+3, one
-// per wavefront, over k tiles [part_begin(grp), part_begin(grp + 1)).
-__global__ __launch_bounds__(256) void skinny_kernel(const uint8_t* __restrict__ packed, int64_t n, int64_t k,
-                                                     int nkt, int nrt, int groups, float st,
-                                                     const uint16_t* __restrict__ x, int64_t m, int64_t ldx,
-                                                     void* __restrict__ y, int64_t ldy, int y_bf16,
-                                                     unsigned* __restrict__ counters, float* __restrict__ partial,
-                                                     int64_t np_tiles) {
+// A batch of up to kMaxBatch skinny products sharing m and the output type;
+// workgroups [wg_begin[p], wg_begin[p+1]) belong to problem p.  Within a
+// problem, workgroup (row group rg, k part grp) owns the four 64-row tiles
+// 4*rg .. 4*rg+3, one per wavefront, over k tiles [part_begin(grp),
+// part_begin(grp + 1)).
+struct SkinnyBatch {
+  int count;
+  int wg_begin[kMaxBatch + 1];
+  const uint8_t* packed[kMaxBatch];
+  const uint16_t* x[kMaxBatch];
+  void* y[kMaxBatch];
+  int64_t ldx[kMaxBatch];
+  int64_t ldy[kMaxBatch];
+  int64_t n[kMaxBatch];
+  int64_t k[kMaxBatch];
+  int nkt[kMaxBatch];
+  int nrt[kMaxBatch];
+  int groups[kMaxBatch];
+  float st[kMaxBatch];
+  int counter_base[kMaxBatch];
+  int64_t partial_base[kMaxBatch];  // floats
+};
+
+__global__ __launch_bounds__(256) void skinny_kernel(const SkinnyBatch b, int64_t m, int y_bf16,
+                                                     unsigned* __restrict__ counters,
+                                                     float* __restrict__ partial_all) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_x[2 * kXTileElems];
-  const int rg = blockIdx.x / groups;
-  const int grp = blockIdx.x % groups;
+  int p = 0;
+  while (p + 1 < b.count && (int)blockIdx.x >= b.wg_begin[p + 1]) ++p;
+  const int groups = b.groups[p], nkt = b.nkt[p], nrt = b.nrt[p];
+  const int64_t n = b.n[p], k = b.k[p], ldx = b.ldx[p], ldy = b.ldy[p];
+  const float st = b.st[p];
+  void* __restrict__ y = b.y[p];
+  const int local = (int)blockIdx.x - b.wg_begin[p];
+  const int rg = local / groups;
+  const int grp = local % groups;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int rt = rg * kWaves + wave;
   const int kt0 = part_begin(grp, nkt, groups), kt1 = part_begin(grp + 1, nkt, groups);
   const int stage_row = threadIdx.x >> 3;
-  const uint16_t* xrow = stage_row < m ? x + stage_row * ldx : nullptr;
+  const uint16_t* xrow = stage_row < m ? b.x[p] + stage_row * ldx : nullptr;
   f32x16 acc_a = {}, acc_b = {};
-  wg_skinny(rt < nrt ? packed + (size_t)rt * nkt * kTileBytes : nullptr, kt0, kt1, k, xrow, lds_x, lane, acc_a,
-            acc_b);
+  wg_skinny(rt < nrt ? b.packed[p] + (size_t)rt * nkt * kTileBytes : nullptr, kt0, kt1, k, xrow, lds_x, lane,
+            acc_a, acc_b);
 
   const int tok = lane & 31;
   const bool vec = (ldy & 3) == 0;
@@ -89,6 +114,8 @@ __global__ __launch_bounds__(256) void skinny_kernel(const uint8_t* __restrict__
   // Split k: partial[grp][rt][i][lane] = accumulator element i of this lane
   // (i < 16: acc_a, else acc_b) -- each element is one contiguous 256-byte run,
   // so the write-through stores go out as full lines.
+  const int np_tiles = ((nrt + kWaves - 1) / kWaves) * kWaves;
+  float* partial = partial_all + b.partial_base[p];
   float* mine = partial + (((size_t)grp * np_tiles + rt) * 32) * 64 + lane;
   if (rt < nrt) {
 #pragma unroll
@@ -97,7 +124,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(const uint8_t* __restrict__
       store_coherent(mine + (size_t)(16 + i) * 64, acc_b[i]);
     }
   }
-  if (!arrive_last(counters + rg, (unsigned)groups)) return;
+  if (!arrive_last(counters + b.counter_base[p] + rg, (unsigned)groups)) return;
   // Last to arrive: each wavefront adds up its own tile's partials over the
   // groups in index order, two groups per round trip, and stores as above.
   if (rt >= nrt || tok >= m) return;
@@ -145,27 +172,60 @@ __global__ void zero_rows_kernel(void* __restrict__ y, int64_t m, int64_t n, int
   else static_cast<float*>(y)[r * ldy + c] = 0.0f;
 }
 
+// K parts per problem for a batch: aim at about 2048 wavefronts over the whole
+// batch (two per SIMD), i.e. `tpw` k tiles per wavefront, with at most 12 parts
+// per row group (bounding the last workgroup's reduction) and none empty.
+int skinny_groups(const Geometry& g, int64_t batch_units) {
+  int64_t tpw = (batch_units + 2047) / 2048;
+  if (tpw < 2) tpw = 2;
+  int64_t groups = (g.nkt + tpw - 1) / tpw;
+  if (groups > 12) groups = 12;
+  if (groups > g.nkt) groups = g.nkt;
+  if (groups < 1) groups = 1;
+  return (int)groups;
+}
+
+int64_t batch_units(const Problem* p, int count) {
+  int64_t u = 0;
+  for (int i = 0; i < count; ++i) {
+    const Geometry g = geometry(p[i].n, p[i].k);
+    u += ((g.nrt + kWaves - 1) / kWaves) * kWaves * g.nkt;
+  }
+  return u;
+}
+
+size_t partial_floats(const Geometry& g, int groups) {
+  if (groups <= 1) return 0;
+  const int64_t nrg = (g.nrt + kWaves - 1) / kWaves;
+  return (size_t)groups * nrg * kWaves * 32 * 64;
+}
+
 }  // namespace
 
-// Row groups of 256 rows; k is split across `groups` workgroups so that about
-// `target` workgroups stream at once, each keeping at least two k tiles.
 SplitPlan skinny_plan(const Geometry& g) {
-  const int64_t target = 384;
-  const int64_t nrg = (g.nrt + kWaves - 1) / kWaves;
-  int64_t groups = (target + nrg - 1) / nrg;
-  int64_t max_groups = g.nkt / 2;
-  if (max_groups < 1) max_groups = 1;
-  if (groups > max_groups) groups = max_groups;
-  if (groups > 8) groups = 8;
-  if (groups < 1) groups = 1;
-  return SplitPlan{(int)groups, (int)groups};
+  Problem pr{nullptr, g.n, g.k, 1.0f, nullptr, 0, nullptr, 0};
+  const int groups = skinny_groups(g, batch_units(&pr, 1));
+  return SplitPlan{groups, groups};
 }
 
 size_t skinny_workspace_bytes(const Geometry& g) {
-  SplitPlan p = skinny_plan(g);
-  if (p.groups <= 1) return 0;
-  const size_t nrg = (size_t)(g.nrt + kWaves - 1) / kWaves;
-  return kCounterBytes + (size_t)p.groups * nrg * kWaves * 32 * 64 * 4;
+  const size_t f = partial_floats(g, skinny_plan(g).groups);
+  return f ? kCounterBytes + f * 4 : 0;
+}
+
+size_t skinny_batch_workspace_bytes(const Problem* p, int count) {
+  size_t worst = 0;
+  for (int b0 = 0; b0 < count; b0 += kMaxBatch) {
+    const int cnt = count - b0 < kMaxBatch ? count - b0 : kMaxBatch;
+    const int64_t units = batch_units(p + b0, cnt);
+    size_t f = 0;
+    for (int i = b0; i < b0 + cnt; ++i) {
+      const Geometry g = geometry(p[i].n, p[i].k);
+      if (g.n > 0 && g.k > 0) f += partial_floats(g, skinny_groups(g, units));
+    }
+    if (f > worst) worst = f;
+  }
+  return worst ? kCounterBytes + worst * 4 : 0;
 }
 
 hipError_t launch_zero_rows(void* y, int64_t m, int64_t n, int64_t ldy, bool y_bf16, hipStream_t s) {
@@ -176,18 +236,58 @@ hipError_t launch_zero_rows(void* y, int64_t m, int64_t n, int64_t ldy, bool y_b
   return hipGetLastError();
 }
 
+hipError_t launch_skinny_batch(const Problem* p, int count, int64_t m, bool y_bf16, void* ws, hipStream_t s) {
+  if (m == 0) return hipSuccess;
+  for (int b0 = 0; b0 < count; b0 += kMaxBatch) {
+    const int cnt = count - b0 < kMaxBatch ? count - b0 : kMaxBatch;
+    const int64_t units = batch_units(p + b0, cnt);
+    SkinnyBatch b = {};
+    int wgs = 0, counters = 0;
+    int64_t pbase = 0;
+    for (int i = b0; i < b0 + cnt; ++i) {
+      const Geometry g = geometry(p[i].n, p[i].k);
+      if (g.n == 0) continue;
+      if (g.k == 0) {
+        hipError_t e = launch_zero_rows(p[i].y, m, g.n, p[i].ldy, y_bf16, s);
+        if (e != hipSuccess) return e;
+        continue;
+      }
+      const int groups = skinny_groups(g, units);
+      const int64_t nrg = (g.nrt + kWaves - 1) / kWaves;
+      const int j = b.count++;
+      b.wg_begin[j] = wgs;
+      b.packed[j] = static_cast<const uint8_t*>(p[i].packed);
+      b.x[j] = p[i].x;
+      b.y[j] = p[i].y;
+      b.ldx[j] = p[i].ldx;
+      b.ldy[j] = p[i].ldy;
+      b.n[j] = g.n;
+      b.k[j] = g.k;
+      b.nkt[j] = (int)g.nkt;
+      b.nrt[j] = (int)g.nrt;
+      b.groups[j] = groups;
+      b.st[j] = p[i].st;
+      b.counter_base[j] = counters;
+      b.partial_base[j] = pbase;
+      wgs += (int)(nrg * groups);
+      if (groups > 1) {
+        counters += (int)nrg;
+        pbase += (int64_t)partial_floats(g, groups);
+      }
+    }
+    if (b.count == 0) continue;
+    b.wg_begin[b.count] = wgs;
+    unsigned* cnt_ptr = static_cast<unsigned*>(ws);
+    float* partial = ws ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kCounterBytes) : nullptr;
+    hipLaunchKernelGGL(skinny_kernel, dim3((unsigned)wgs), dim3(256), 0, s, b, m, y_bf16 ? 1 : 0, cnt_ptr, partial);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_skinny(const void* packed, const Geometry& g, float st, const uint16_t* x, int64_t m, int64_t ldx,
                          void* y, int64_t ldy, bool y_bf16, void* ws, hipStream_t s) {
-  if (m == 0 || g.n == 0) return hipSuccess;
-  if (g.k == 0) return launch_zero_rows(y, m, g.n, ldy, y_bf16, s);
-  SplitPlan p = skinny_plan(g);
-  const int64_t nrg = (g.nrt + kWaves - 1) / kWaves;
-  unsigned* counters = static_cast<unsigned*>(ws);
-  float* partial = ws ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kCounterBytes) : nullptr;
-  hipLaunchKernelGGL(skinny_kernel, dim3((unsigned)(nrg * p.groups)), dim3(256), 0, s,
-                     static_cast<const uint8_t*>(packed), g.n, g.k, (int)g.nkt, (int)g.nrt, p.groups, st, x, m, ldx,
-                     y, ldy, y_bf16 ? 1 : 0, counters, partial, nrg * kWaves);
-  return hipGetLastError();
+  Problem pr{packed, g.n, g.k, st, x, ldx, y, ldy};
+  return launch_skinny_batch(&pr, 1, m, y_bf16, ws, s);
 }
 
 }  // namespace nvfp4

@@ -137,6 +137,38 @@ int nvfp4_gemm(const void* packed, int64_t n, int64_t k, float tensor_scale,
                void* y, int64_t ldy, int y_dtype,
                void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Batched products: several independent matrices in one launch ----------
+ * A decode step multiplies several weight matrices of a layer by their own
+ * activations (gate, up, down, QKV, O); the Ignis README's decode round runs
+ * them as one replayed sequence.  These calls take a host array of problems
+ * and compute each as nvfp4_gemv / nvfp4_gemm would, but as one launch per
+ * eight problems, so that the launch ramp and the cross-workgroup reduction
+ * tail are paid once per batch and the split of K is balanced over the whole
+ * batch.  GEMV results are bit-identical to single calls; a GEMM of a batch may
+ * split K differently from a single call, so its results meet the same error
+ * bound but may differ in the last bits.  Problems must not share outputs.
+ * The workspace rules are those of nvfp4_gemv / nvfp4_gemm.
+ */
+typedef struct nvfp4_problem {
+  const void* packed;       /* packed weights of an [n][k] matrix */
+  int64_t n, k;
+  float tensor_scale;
+  const uint16_t* x;        /* bf16 activations: [k] (gemv) or [m][ldx] (gemm) */
+  int64_t ldx;              /* gemm only: row stride of x in elements (>= k, multiple of 8) */
+  void* y;                  /* fp32 [n] (gemv) or y_dtype [m][ldy] (gemm) */
+  int64_t ldy;              /* gemm only: row stride of y in elements (>= n) */
+} nvfp4_problem;
+
+int nvfp4_gemv_batched_workspace_bytes(const nvfp4_problem* problems /* host */, int count,
+                                       size_t* bytes /* host */);
+int nvfp4_gemv_batched(const nvfp4_problem* problems /* host */, int count, void* workspace,
+                       size_t workspace_bytes, void* stream);
+/* All problems of a batch share m and y_dtype. */
+int nvfp4_gemm_batched_workspace_bytes(const nvfp4_problem* problems /* host */, int count, int64_t m,
+                                       size_t* bytes /* host */);
+int nvfp4_gemm_batched(const nvfp4_problem* problems /* host */, int count, int64_t m, int y_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- a4-a8: top-k routed mixture-of-experts layer ----------------------------
  * Per token t (CHImp-Alpha-v1.0 model card, "How it fits on one GPU": each
  * token is routed to 10 of 512 experts and only those experts' weights are read):

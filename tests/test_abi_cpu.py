@@ -28,7 +28,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 16, names
     assert set(names) == set(B.EXPORTED)
     for name in names:
         assert hasattr(L, name), name
@@ -138,3 +138,35 @@ def test_moe_workspace_size_covers_intermediates():
     need = B.moe_workspace_bytes(32, 512, 10, 2048, 512)
     # h (bf16 320 x 512) + d (fp32 320 x 2048) + indices
     assert need >= 320 * 512 * 2 + 320 * 2048 * 4
+
+
+def test_batched_validation(L):
+    A, M = 0x10000, 0x10008
+    arr = (B.Problem * 3)()
+    for i in range(3):
+        arr[i].packed, arr[i].n, arr[i].k, arr[i].tensor_scale = A, 64, 256, 1.0
+        arr[i].x, arr[i].ldx, arr[i].y, arr[i].ldy = A, 256, A + 0x1000 * (i + 1), 64
+    sz = ctypes.c_size_t()
+    assert L.nvfp4_gemv_batched_workspace_bytes(arr, 3, ctypes.byref(sz)) == B.NVFP4_OK
+    assert L.nvfp4_gemv_batched(None, 2, None, 0, None) == B.NVFP4_ERR_NULL
+    assert L.nvfp4_gemv_batched(arr, -1, None, 0, None) == B.NVFP4_ERR_ARG
+    assert L.nvfp4_gemv_batched(arr, 0, None, 0, None) == B.NVFP4_OK
+    arr[1].k = 40
+    assert L.nvfp4_gemv_batched(arr, 3, None, 0, None) == B.NVFP4_ERR_SHAPE
+    arr[1].k = 256
+    arr[2].x = M
+    assert L.nvfp4_gemv_batched(arr, 3, None, 0, None) == B.NVFP4_ERR_ALIGN
+    arr[2].x = A
+    arr[2].y = arr[0].y
+    assert L.nvfp4_gemv_batched(arr, 3, None, 0, None) == B.NVFP4_ERR_ARG      # shared output
+    arr[2].y = A + 0x9000
+    assert L.nvfp4_gemm_batched(arr, 3, 32, 9, None, 0, None) == B.NVFP4_ERR_DTYPE
+    arr[0].ldx = 100
+    assert L.nvfp4_gemm_batched(arr, 3, 32, 1, None, 0, None) == B.NVFP4_ERR_SHAPE
+    arr[0].ldx = 256
+    assert L.nvfp4_gemm_batched(arr, 3, 0, 1, None, 0, None) == B.NVFP4_OK     # m = 0
+    big = (B.Problem * 1)()
+    big[0].packed, big[0].n, big[0].k, big[0].x, big[0].y = A, 5120, 17408, A, A
+    big[0].ldx, big[0].ldy = 17408, 5120
+    assert L.nvfp4_gemm_batched_workspace_bytes(big, 1, 32, ctypes.byref(sz)) == B.NVFP4_OK and sz.value > 0
+    assert L.nvfp4_gemm_batched(big, 1, 32, 1, None, 0, None) == B.NVFP4_ERR_WORKSPACE

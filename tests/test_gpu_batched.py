@@ -1,0 +1,86 @@
+"""GPU parity of the batched entry points (several matrices in one launch)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_quantized_decode_amd import binding as B
+from bit_quantized_decode_amd import inputs as I
+from helpers import (assert_within, bf16_to_f64, device, oracle_threads, pack_to_device, random_matrix,
+                     sample_rows, to_dev_bf16, ulp_bf16)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def layer():
+    dev = device()
+    mats = []
+    for m in I.DENSE_LAYER:
+        c, s = I.nvfp4_matrix(I.DECODE_B1, m.matrix_id, m.n, m.k)
+        mats.append((m, c, s, pack_to_device(c, s, dev)))
+    return mats
+
+
+def test_gemv_batched_equals_single_calls(layer):
+    dev = device()
+    xs = [to_dev_bf16(I.activations(I.DECODE_B1, m.matrix_id, 1, m.k)[0], dev) for m, _, _, _ in layer]
+    ys = [torch.empty(m.n, dtype=torch.float32, device=dev) for m, _, _, _ in layer]
+    B.gemv_batched([(p, m.n, m.k, I.TENSOR_SCALE, x, y) for (m, _, _, p), x, y in zip(layer, xs, ys)])
+    for (m, c, s, p), x, y in zip(layer, xs, ys):
+        single = B.gemv(p, m.n, m.k, I.TENSOR_SCALE, x)
+        torch.cuda.synchronize()
+        assert torch.equal(single.view(torch.int32), y.view(torch.int32)), m.name
+
+
+def test_gemm_batched_layer_parity(layer):
+    dev = device()
+    xb = [I.activations(I.DECODE_B32, m.matrix_id, 32, m.k) for m, _, _, _ in layer]
+    ys = [torch.empty((32, m.n), dtype=torch.float32, device=dev) for m, _, _, _ in layer]
+    B.gemm_batched([(p, m.n, m.k, I.TENSOR_SCALE, to_dev_bf16(x, dev), y)
+                    for (m, _, _, p), x, y in zip(layer, xb, ys)])
+    torch.cuda.synchronize()
+    for (m, c, s, p), x, y in zip(layer, xb, ys):
+        rows = sample_rows(m.n, 256, 300 + m.matrix_id)
+        y_ref, sabs = oracle.gemm(c, s, I.TENSOR_SCALE, x, rows=rows, nthreads=oracle_threads())
+        assert_within(y.cpu().numpy()[:, rows], y_ref, sabs, what=f"batched {m.name}")
+
+
+@pytest.mark.parametrize("m", [5, 32, 70])
+def test_gemm_batched_ragged_mixed_shapes(m):
+    """Ten problems (two launches of up to eight), ragged shapes, bf16 output."""
+    dev = device()
+    rng = np.random.default_rng(77 + m)
+    shapes = [(1, 16), (100, 48), (65, 272), (200, 1040), (130, 2320), (64, 256), (7, 4112), (300, 512),
+              (33, 96), (129, 1024)]
+    items, refs = [], []
+    for n, k in shapes:
+        c, s = random_matrix(rng, n, k)
+        x = I.bf16_round(rng.standard_normal((m, k)).astype(np.float32))
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        items.append((pack_to_device(c, s, dev), n, k, I.TENSOR_SCALE, to_dev_bf16(x, dev), y))
+        refs.append((c, s, x))
+    B.gemm_batched(items)
+    torch.cuda.synchronize()
+    for (p, n, k, st, x, y), (c, s, xb) in zip(items, refs):
+        y_ref, sabs = oracle.gemm(c, s, st, xb)
+        assert_within(bf16_to_f64(y), y_ref, sabs, extra=ulp_bf16(y_ref), what=f"batched m={m} {n}x{k}")
+
+
+def test_gemv_batched_ragged_mixed_shapes():
+    dev = device()
+    rng = np.random.default_rng(78)
+    shapes = [(1, 16), (100, 48), (65, 272), (200, 1040), (130, 2320), (64, 256), (7, 4112), (300, 512),
+              (33, 96), (129, 17408)]
+    items, refs = [], []
+    for n, k in shapes:
+        c, s = random_matrix(rng, n, k)
+        x = I.bf16_round(rng.standard_normal(k).astype(np.float32))
+        y = torch.empty(n, dtype=torch.float32, device=dev)
+        items.append((pack_to_device(c, s, dev), n, k, I.TENSOR_SCALE, to_dev_bf16(x, dev), y))
+        refs.append((c, s, x))
+    B.gemv_batched(items)
+    torch.cuda.synchronize()
+    for (p, n, k, st, x, y), (c, s, xb) in zip(items, refs):
+        y_ref, sabs = oracle.gemm(c, s, st, xb[None, :])
+        assert_within(y.cpu().numpy(), y_ref[0], sabs[0], what=f"gemv batched {n}x{k}")
