@@ -148,9 +148,18 @@ def main():
         B.gemm_batched([(packed[cp][j], m.n, m.k, I.TENSOR_SCALE, x32[j], y32[j]) for j, m in enumerate(layer)],
                        ws=ws_split)
 
+    def pre_items(cp):
+        return [(pre_packed[cp][j], mat.n, mat.k, I.TENSOR_SCALE, pre_x[j], pre_y[j]) for j, mat in enumerate(pre)]
+
+    if "prefill" in rows:
+        # The three prefill products share one stream-K launch; its workspace
+        # (counters + cut-tile partial sums) is larger than the decode rows'.
+        need = B.gemm_batched_workspace_bytes(pre_items(0), 512)
+        if need > ws_split.numel():
+            ws_split = B.workspace(need, dev)
+
     def row_pre(cp):
-        for j, mat in enumerate(pre):
-            B.gemm(pre_packed[cp][j], mat.n, mat.k, I.TENSOR_SCALE, pre_x[j], y=pre_y[j], ws=ws_split)
+        B.gemm_batched(pre_items(cp), ws=ws_split)
 
     plan = []   # (row name, callable(copy), copies, copy for step i, outputs to check)
     if "decode_b1" in rows:

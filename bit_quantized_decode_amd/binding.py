@@ -224,6 +224,14 @@ def gemv_batched(items, ws=None, stream=None):
     check(L.nvfp4_gemv_batched(arr, len(items), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
 
 
+def gemm_batched_workspace_bytes(items, m):
+    """Workspace bytes nvfp4_gemm_batched needs for these problems at m activation rows."""
+    arr = problems(items)
+    need = ctypes.c_size_t()
+    check(lib().nvfp4_gemm_batched_workspace_bytes(arr, len(items), m, ctypes.byref(need)))
+    return need.value
+
+
 def gemm_batched(items, ws=None, stream=None):
     """Several GEMMs sharing m and the output dtype: items = [(packed, n, k, tensor_scale, x [m][ldx], y [m][ldy])]."""
     arr = problems(items)

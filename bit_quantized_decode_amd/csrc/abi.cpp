@@ -295,10 +295,7 @@ int nvfp4_gemm_batched_workspace_bytes(const nvfp4_problem* problems, int count,
   if (m <= 32) {
     need = nvfp4::skinny_batch_workspace_bytes(pr.data(), count);
   } else {
-    for (int i = 0; i < count; ++i) {
-      const size_t b = nvfp4::prefill_workspace_bytes(m, nvfp4::geometry(pr[i].n, pr[i].k));
-      if (b > need) need = b;
-    }
+    need = nvfp4::prefill_batch_workspace_bytes(pr.data(), count, m);
   }
   *bytes = need;
   return ok();
@@ -321,17 +318,12 @@ int nvfp4_gemm_batched(const nvfp4_problem* problems, int count, int64_t m, int 
     return hip_status(nvfp4::launch_skinny_batch(pr.data(), count, m, bf16, workspace, (hipStream_t)stream),
                       "skinny gemm batch launch");
   }
-  for (int i = 0; i < count; ++i) {
-    const nvfp4::Geometry g = nvfp4::geometry(pr[i].n, pr[i].k);
-    const size_t need = nvfp4::prefill_workspace_bytes(m, g);
-    if (need > 0 && (!workspace || workspace_bytes < need))
-      return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace ? workspace_bytes : 0);
-    if (g.n == 0) continue;
-    hipError_t e = nvfp4::launch_prefill(pr[i].packed, g, pr[i].st, pr[i].x, m, pr[i].ldx, pr[i].y, pr[i].ldy, bf16,
-                                         workspace, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_status(e, "prefill gemm launch");
-  }
-  return ok();
+  const size_t need = nvfp4::prefill_batch_workspace_bytes(pr.data(), count, m);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace ? workspace_bytes : 0);
+  if (need > 0 && !aligned16(workspace)) return fail(NVFP4_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return hip_status(nvfp4::launch_prefill_batch(pr.data(), count, m, bf16, workspace, (hipStream_t)stream),
+                    "prefill gemm batch launch");
   NVFP4_GUARD_END
 }
 

@@ -61,6 +61,8 @@ size_t gemv_batch_workspace_bytes(const Problem* p, int count);
 hipError_t launch_gemv_batch(const Problem* p, int count, void* ws, hipStream_t s);
 size_t skinny_batch_workspace_bytes(const Problem* p, int count);
 hipError_t launch_skinny_batch(const Problem* p, int count, int64_t m, bool y_bf16, void* ws, hipStream_t s);
+size_t prefill_batch_workspace_bytes(const Problem* p, int count, int64_t m);
+hipError_t launch_prefill_batch(const Problem* p, int count, int64_t m, bool y_bf16, void* ws, hipStream_t s);
 
 hipError_t launch_pack(const uint8_t* codes, const uint8_t* scales, const Geometry& g, void* packed,
                        hipStream_t s);

@@ -2,192 +2,467 @@
 //
 // y[i][j] = s_t * sum_k W[j][k] * x[i][k]
 //
-// Compute-bound: each weight is dequantised exactly to bf16 (E2M1 x E4M3 in
-// fp32 is exact and fits bf16) into an LDS tile once per workgroup, and bf16
-// MFMA does the product with fp32 accumulation; s_t is applied after
-// accumulation.  A workgroup computes a 128 (activation rows) x 128 (weight
-// rows) output tile over 64-k slabs; four wavefronts each own 64 x 64 of it
-// (2 x 2 v_mfma_f32_32x32x16_bf16 tiles).  The next slab's global loads are
-// in flight while the current slab is multiplied.  Accumulation is two-level
-// (a fresh accumulator per 1024 k, then added to the running sum) to bound
-// the roundings any output sees.
-#include "device_common.h"
+// Compute-bound.  Every weight is dequantised exactly to bf16 (E2M1 x E4M3
+// in fp32 has at most 6 significant bits, so the fp32 product is exact and
+// its upper half is its bf16) and bf16 MFMA (v_mfma_f32_32x32x16_bf16) forms
+// the products with fp32 accumulation; s_t is applied after accumulation.
+//
+// Workgroup tile: BM = 32*JT activation rows x 256 weight rows.  Each of the
+// four wavefronts owns one 64-row packed weight tile and dequantises it
+// straight into MFMA A operands: the packed layout already puts a lane's
+// eight codes of a k step where the A operand wants them, so weights never
+// pass through LDS and no weight is dequantised twice in a workgroup.  The
+// activation tile (BM rows x 64 k per iteration) is staged through LDS,
+// double buffered, its 16-byte chunks XOR-swizzled by row so that the B
+// operand reads are bank-conflict free; every wavefront reads all of it.
+// Weights stream from memory four iterations ahead of use, activations two.
+//
+// Work decomposition (stream-K): the (output tile, 64-k iteration) pairs of
+// all problems of a launch are laid end to end and cut into one equal share
+// per persistent workgroup, so no compute unit idles at the end of a launch
+// whatever the tile count -- the pages' split-K prefill, balanced exactly.
+// A tile cut between workgroups is finished by whichever contributor arrives
+// last: it adds all contributions in k order (deterministic, independent of
+// arrival order) and writes the output.  No workgroup ever waits for
+// another.  Consecutive shares run on the same XCD, so an XCD's workgroups
+// walk neighbouring tiles and share their activation rows in its L2.
+#include "skinny_core.h"
 #include "launchers.h"
 
 namespace nvfp4 {
 namespace {
 
-constexpr int kBM = 128;            // activation rows per workgroup
-constexpr int kBN = 128;            // weight rows per workgroup (two 64-row tiles)
-constexpr int kBK = 64;             // k per slab
-constexpr int kLdsStride = kBK + 8; // bf16 elements per LDS row (16-byte pad against bank conflicts)
-constexpr int kFlushSlabs = 16;     // slabs per first-level accumulation (1024 k)
+constexpr int kBN = 256;        // weight rows per workgroup tile: four packed row tiles
+constexpr int kBK = 64;         // k per iteration
+constexpr int kPreWgs = 256;    // persistent workgroups (the compute units of an MI355X)
+constexpr int kMinShare = 8;    // iterations per workgroup below which fewer workgroups are used
+constexpr int kMaxPre = 8;      // problems per launch
 
-struct Stage {
-  u32x4 w;        // 32 codes of one weight row
-  u32x4 x[4];     // 32 bf16 of one activation row
+struct PrefillBatch {
+  int count;
+  int mtiles;                       // activation-row tiles
+  int wgs;                          // workgroups (shares)
+  int y_bf16;
+  int64_t m;                        // activation rows
+  int64_t total;                    // iterations over all problems
+  int64_t iter_begin[kMaxPre + 1];  // first global iteration of each problem
+  int tile_base[kMaxPre];           // first global tile (counter slot) of each problem
+  int iters[kMaxPre];               // iterations per tile
+  int nkt[kMaxPre];
+  int nrt[kMaxPre];
+  const uint8_t* packed[kMaxPre];
+  const uint16_t* x[kMaxPre];
+  void* y[kMaxPre];
+  int64_t n[kMaxPre], k[kMaxPre], ldx[kMaxPre], ldy[kMaxPre];
+  float st[kMaxPre];
 };
 
-__global__ __launch_bounds__(256) void prefill_kernel(const uint8_t* __restrict__ packed, int64_t n, int64_t k,
-                                                      int nkt, float st, const uint16_t* __restrict__ x, int64_t m,
-                                                      int64_t ldx, void* __restrict__ y, int64_t ldy, int y_bf16) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds_w[kBN * kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_x[kBM * kLdsStride];
+// Share w covers global iterations [share_begin(w), share_begin(w + 1)).
+__device__ __forceinline__ int64_t share_begin(int w, int64_t total, int wgs) { return ((int64_t)w * total) / wgs; }
+// The share holding global iteration g.
+__device__ __forceinline__ int owner_of(int64_t g, int64_t total, int wgs) { return (int)(((g + 1) * wgs - 1) / total); }
 
+// LDS byte offset of 16-byte chunk c (0..7) of activation row r (128 bytes a row).
+__device__ __forceinline__ int swz(int r, int c) { return r * (kBK * 2) + ((c ^ (r & 7)) << 4); }
+
+// Weights of one iteration for one lane: two 1 KB chunks of the packed tile
+// (k steps 0-1 and 2-3 of the iteration) and the scale dword of rows r and
+// 32 + r that covers the iteration's four 16-k blocks.
+struct WStage {
+  u32x4 q0, q1;
+  uint32_t sa, sb;
+};
+
+// Partial sums of a cut tile: per workgroup two slots (its first and its last
+// segment), each the workgroup tile in accumulator order, laid out so that
+// one wavefront store writes 1 KB contiguously: float4 index u of lane l of
+// wavefront v is at ((v * 8 * JT + u) * 64 + l) * 4 floats.
+template <int JT>
+constexpr size_t part_floats() { return (size_t)4 * 8 * JT * 64 * 4; }
+
+// Four 16-byte stores 1 KB apart, through to memory (not held in this XCD's
+// L2); the trailing nops cover the store-data read of the last store.
+__device__ __forceinline__ void store4x4_coherent(float* p, f32x4 a, f32x4 b, f32x4 c, f32x4 d) {
+  asm volatile(
+      "global_store_dwordx4 %0, %1, off sc1\n"
+      "global_store_dwordx4 %0, %2, off offset:1024 sc1\n"
+      "global_store_dwordx4 %0, %3, off offset:2048 sc1\n"
+      "global_store_dwordx4 %0, %4, off offset:3072 sc1\n"
+      "s_nop 1"
+      :
+      : "v"(p), "v"(a), "v"(b), "v"(c), "v"(d)
+      : "memory");
+}
+
+// Sixteen 16-byte loads 1 KB apart that bypass the non-coherent caches; the
+// wait sits in the same statement, so none is in flight when it ends.
+__device__ __forceinline__ void load16x4_strided_coherent(const float* p, f32x4 (&v)[16]) {
+  const char* c0 = reinterpret_cast<const char*>(p);
+  const char* c1 = c0 + 4096;
+  const char* c2 = c0 + 8192;
+  const char* c3 = c0 + 12288;
+  asm volatile(
+      "global_load_dwordx4 %0, %16, off sc1\n"
+      "global_load_dwordx4 %1, %16, off offset:1024 sc1\n"
+      "global_load_dwordx4 %2, %16, off offset:2048 sc1\n"
+      "global_load_dwordx4 %3, %16, off offset:3072 sc1\n"
+      "global_load_dwordx4 %4, %17, off sc1\n"
+      "global_load_dwordx4 %5, %17, off offset:1024 sc1\n"
+      "global_load_dwordx4 %6, %17, off offset:2048 sc1\n"
+      "global_load_dwordx4 %7, %17, off offset:3072 sc1\n"
+      "global_load_dwordx4 %8, %18, off sc1\n"
+      "global_load_dwordx4 %9, %18, off offset:1024 sc1\n"
+      "global_load_dwordx4 %10, %18, off offset:2048 sc1\n"
+      "global_load_dwordx4 %11, %18, off offset:3072 sc1\n"
+      "global_load_dwordx4 %12, %19, off sc1\n"
+      "global_load_dwordx4 %13, %19, off offset:1024 sc1\n"
+      "global_load_dwordx4 %14, %19, off offset:2048 sc1\n"
+      "global_load_dwordx4 %15, %19, off offset:3072 sc1\n"
+      "s_waitcnt vmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
+        "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]),
+        "=&v"(v[15])
+      : "v"(c0), "v"(c1), "v"(c2), "v"(c3)
+      : "memory");
+}
+
+// One 16-k step KS (0..3) of an iteration: A operands for weight rows r and
+// 32 + r from the resident codes, B operands for the JT activation tiles
+// from LDS, 2 * JT MFMAs.
+template <int KS, int JT>
+__device__ __forceinline__ void kstep(const uint8_t* xl, int lane, const WStage& w, f32x16 (&acc)[2][JT]) {
+  constexpr int J = KS & 1;
+  const u32x4 q = KS < 2 ? w.q0 : w.q1;
+  const bf16x8 a0 = dequant8(q[2 * J], e4m3<KS>(w.sa));
+  const bf16x8 a1 = dequant8(q[2 * J + 1], e4m3<KS>(w.sb));
+  const int chunk = 2 * KS + (lane >> 5);
+#pragma unroll
+  for (int jt = 0; jt < JT; ++jt) {
+    const bf16x8 bx = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xl + swz(32 * jt + (lane & 31), chunk)));
+    acc[0][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bx, acc[0][jt], 0, 0, 0);
+    acc[1][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bx, acc[1][jt], 0, 0, 0);
+  }
+}
+
+template <int JT>
+__device__ __forceinline__ f32x4 acc4(const f32x16 (&acc)[2][JT], int u) {
+  // float4 u of a lane: accumulator tile t = u / 4 (i = t / JT, jt = t % JT), elements 4 * (u % 4) ..
+  const f32x16& a = acc[(u >> 2) / JT][(u >> 2) % JT];
+  const int e = 4 * (u & 3);
+  return f32x4{a[e], a[e + 1], a[e + 2], a[e + 3]};
+}
+
+template <int JT>
+__global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillBatch b, unsigned* __restrict__ counters,
+                                                         float* __restrict__ partials) {
+  constexpr int kBM = 32 * JT;
+  constexpr int kXBuf = kBM * kBK * 2;  // bytes of one activation buffer
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kXBuf];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int64_t m0 = (int64_t)blockIdx.x * kBM;
-  const int rt0 = blockIdx.y * 2;  // first of the two 64-row tiles
-  const int64_t n0 = (int64_t)rt0 * kTileRows;
 
-  // Weight loader: thread -> (row tile rtl, chunk parity cp, lane): one 16-byte
-  // slot of the tile layout = rows r and 32 + r (r = lane % 32) x two 8-k groups.
-  const int w_rtl = tid >> 7;
-  const int w_cp = (tid >> 6) & 1;
-  const bool w_tile_ok = (int64_t)(rt0 + w_rtl) * kTileRows < n;
-  const uint8_t* w_base = packed + (size_t)(rt0 + w_rtl) * nkt * kTileBytes;
-  const int w_r = lane & 31, w_h = lane >> 5;
-  // Activation loader: thread -> (row tid/2, k half tid%2): 32 bf16.
-  const int x_row = tid >> 1;
-  const int x_half = tid & 1;
-  const bool x_ok = m0 + x_row < m;
-  const uint16_t* x_base = x + (x_ok ? (m0 + x_row) : 0) * ldx + 32 * x_half;
+  // Share of this workgroup.  Dispatch places workgroup b on XCD b % 8; give
+  // each XCD a contiguous run of shares.
+  int w = (int)blockIdx.x;
+  if ((b.wgs & 7) == 0) w = (int)(blockIdx.x & 7) * (b.wgs >> 3) + (int)(blockIdx.x >> 3);
+  const int64_t g_begin = share_begin(w, b.total, b.wgs);
+  const int64_t g_end = share_begin(w + 1, b.total, b.wgs);
 
-  const int nslabs = nkt * (kTileK / kBK);
-  u32x4 sa = {0u, 0u, 0u, 0u}, sb = {0u, 0u, 0u, 0u};
+  const int xr0 = tid >> 3, xc = tid & 7;  // activation loader: rows xr0 + 32j, 16-byte chunk xc
 
-  auto load = [&](int slab, Stage& st_) {
-    const int kt = slab >> 2, sub = slab & 3;
-    const int64_t kk = (int64_t)slab * kBK + 32 * x_half;
-    if (w_tile_ok) st_.w = load16(w_base + (size_t)kt * kTileBytes + (2 * sub + w_cp) * 1024 + lane * 16);
-    else st_.w = u32x4{0u, 0u, 0u, 0u};
+  for (int64_t g = g_begin; g < g_end;) {
+    // ---- locate the segment: problem p, tile (mt, nt), iterations [ib, ie)
+    int p = 0;
+    while (p + 1 < b.count && g >= b.iter_begin[p + 1]) ++p;
+    const int iters = b.iters[p];
+    const int64_t gl = g - b.iter_begin[p];
+    const int tile = (int)(gl / iters);
+    const int ib = (int)(gl - (int64_t)tile * iters);
+    const int64_t tile_g0 = b.iter_begin[p] + (int64_t)tile * iters;
+    const int ie = (int)(g_end - tile_g0 < iters ? g_end - tile_g0 : iters);
+    const int mt = tile % b.mtiles, nt = tile / b.mtiles;
+    const int64_t m0 = (int64_t)mt * kBM;
+    const int64_t kdim = b.k[p];
+    const int nkt = b.nkt[p];
+
+    // Activation sources (rows past m re-read row m-1; their outputs are not written).
+    const uint16_t* xsrc[JT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (x_ok && kk + 8 * i < k) st_.x[i] = load16(x_base + (int64_t)slab * kBK + 8 * i);
-      else st_.x[i] = u32x4{0u, 0u, 0u, 0u};
+    for (int j = 0; j < JT; ++j) {
+      int64_t row = m0 + xr0 + 32 * j;
+      row = row < b.m ? row : b.m - 1;
+      xsrc[j] = b.x[p] + row * b.ldx[p] + 8 * xc;
     }
-  };
+    // Weight source: this wavefront's packed row tile (clamped; rows past n are not written).
+    int rt = nt * 4 + wave;
+    rt = rt < b.nrt[p] ? rt : b.nrt[p] - 1;
+    const uint8_t* wt = b.packed[p] + (size_t)rt * nkt * kTileBytes;
+    const uint8_t* wcode = wt + lane * 16;
+    const uint8_t* wscale = wt + kScaleOffset + 32 * (lane & 31);
 
-  // Wave tile: rows (weights) wn*64.., activation rows wm*64..
-  const int wm = wave >> 1, wn = wave & 1;
-  f32x16 acc[2][2], tot[2][2];
+    auto load_w = [&](int it, WStage& s) {
+      const size_t t = (size_t)(it >> 2) * kTileBytes;
+      const int sub = it & 3;
+      s.q0 = load16(wcode + t + (2 * sub) * 1024);
+      s.q1 = load16(wcode + t + (2 * sub + 1) * 1024);
+      s.sa = *reinterpret_cast<const uint32_t*>(wscale + t + 4 * sub);
+      s.sb = *reinterpret_cast<const uint32_t*>(wscale + t + 16 + 4 * sub);
+    };
+    auto load_x = [&](int it, u32x4 (&v)[JT]) {
+      const bool in = (int64_t)it * kBK + 8 * xc < kdim;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < JT; ++j) v[j] = in ? load16(xsrc[j] + (int64_t)it * kBK) : u32x4{0u, 0u, 0u, 0u};
+    };
+    auto store_x = [&](int buf, const u32x4 (&v)[JT]) {
+      uint8_t* xl = lds + buf * kXBuf;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) { acc[i][j] = f32x16{}; tot[i][j] = f32x16{}; }
+      for (int j = 0; j < JT; ++j) *reinterpret_cast<u32x4*>(xl + swz(xr0 + 32 * j, xc)) = v[j];
+    };
 
-  Stage cur;
-  if (nslabs > 0) load(0, cur);
-  for (int slab = 0; slab < nslabs; ++slab) {
-    const int kt = slab >> 2, sub = slab & 3;
-    if (sub == 0 && w_tile_ok) {
-      sa = load16(w_base + (size_t)kt * kTileBytes + kScaleOffset + 32 * w_r);
-      sb = load16(w_base + (size_t)kt * kTileBytes + kScaleOffset + 32 * w_r + 16);
-    }
-    __syncthreads();  // previous slab fully consumed
-    {
-      // Dequantise the slot: dword d holds row r + 32*(d&1), k steps 2c + (d>>1)
-      // of this k tile (c = 2*sub + cp), 8 codes at k offset 8h.
-      const int c = 2 * sub + w_cp;
+    f32x16 acc[2][JT];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t sw = (d & 1) ? sb[c >> 1] : sa[c >> 1];
-        const float s = __builtin_amdgcn_cvt_f32_fp8(sw >> (8 * ((2 * c + (d >> 1)) & 3)), 0);
-        f32x2 v;
-        u32x4 o;
-        v = e2m1x2<0>(cur.w[d]); o[0] = pack_exact_bf16x2(v.x * s, v.y * s);
-        v = e2m1x2<1>(cur.w[d]); o[1] = pack_exact_bf16x2(v.x * s, v.y * s);
-        v = e2m1x2<2>(cur.w[d]); o[2] = pack_exact_bf16x2(v.x * s, v.y * s);
-        v = e2m1x2<3>(cur.w[d]); o[3] = pack_exact_bf16x2(v.x * s, v.y * s);
-        const int lrow = w_rtl * 64 + w_r + 32 * (d & 1);
-        *reinterpret_cast<u32x4*>(lds_w + lrow * kLdsStride + 32 * w_cp + 8 * w_h + 16 * (d >> 1)) = o;
-      }
-      u32x4* xdst = reinterpret_cast<u32x4*>(lds_x + x_row * kLdsStride + 32 * x_half);
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xdst[i] = cur.x[i];
-    }
+      for (int j = 0; j < JT; ++j) acc[i][j] = f32x16{};
+
+    // ---- pipeline.  Loads past the segment re-read its last iteration, so
+    // each executed step issues the same loads in the same order.
+    const int last = ie - 1;
+    auto clampi = [&](int it) { return it < last ? it : last; };
+    WStage w0, w1, w2, w3;
+    u32x4 xa[JT], xb[JT];
+    load_w(ib, w0);
+    load_w(clampi(ib + 1), w1);
+    load_w(clampi(ib + 2), w2);
+    load_w(clampi(ib + 3), w3);
+    load_x(ib, xa);
+    load_x(clampi(ib + 1), xb);
+    store_x(0, xa);
     __syncthreads();
-    if (slab + 1 < nslabs) load(slab + 1, cur);
-
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int kof = ks * 16 + 8 * (lane >> 5);
-      bf16x8 a[2], b[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                              lds_w + (wn * 64 + i * 32 + (lane & 31)) * kLdsStride + kof));
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                              lds_x + (wm * 64 + j * 32 + (lane & 31)) * kLdsStride + kof));
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    if ((slab + 1) % kFlushSlabs == 0 || slab + 1 == nslabs) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) { tot[i][j] += acc[i][j]; acc[i][j] = f32x16{}; }
-    }
+    // Step S of a group of four (iteration it = i + S, LDS buffer S & 1):
+    // issue the activation loads of it + 2, multiply it, stage it + 1's
+    // activations into the other buffer, issue the weight loads of it + 4.
+#define NVFP4_PREFILL_STEP(S, XCUR, XNEXT, WCUR)                        \
+  if (i + (S) < ie) {                                                   \
+    const int it = i + (S);                                             \
+    load_x(clampi(it + 2), XCUR);                                       \
+    {                                                                   \
+      const uint8_t* xl = lds + ((S) & 1) * kXBuf;                      \
+      kstep<0, JT>(xl, lane, WCUR, acc);                                \
+      kstep<1, JT>(xl, lane, WCUR, acc);                                \
+      kstep<2, JT>(xl, lane, WCUR, acc);                                \
+      kstep<3, JT>(xl, lane, WCUR, acc);                                \
+    }                                                                   \
+    if (it + 1 < ie) store_x(((S) + 1) & 1, XNEXT);                     \
+    load_w(clampi(it + 4), WCUR);                                       \
+    __syncthreads();                                                    \
   }
+    for (int i = ib; i < ie; i += 4) {
+      NVFP4_PREFILL_STEP(0, xa, xb, w0)
+      NVFP4_PREFILL_STEP(1, xb, xa, w1)
+      NVFP4_PREFILL_STEP(2, xa, xb, w2)
+      NVFP4_PREFILL_STEP(3, xb, xa, w3)
+    }
+#undef NVFP4_PREFILL_STEP
 
-  // Epilogue: element e of tile (i, j) is weight row n0 + wn*64 + i*32 + 8*(e/4) + 4*(lane/32) + e%4,
-  // activation row m0 + wm*64 + j*32 + lane%32.
-  const bool vec = (ldy & 3) == 0;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t row = m0 + wm * 64 + j * 32 + (lane & 31);
-      if (row >= m) continue;
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int64_t col = n0 + wn * 64 + i * 32 + 8 * e4 + 4 * (lane >> 5);
-        const float v0 = tot[i][j][4 * e4 + 0] * st, v1 = tot[i][j][4 * e4 + 1] * st;
-        const float v2 = tot[i][j][4 * e4 + 2] * st, v3 = tot[i][j][4 * e4 + 3] * st;
-        if (y_bf16) {
-          uint16_t* yr = static_cast<uint16_t*>(y) + row * ldy + col;
-          if (vec && col + 4 <= n) {
-            *reinterpret_cast<uint2*>(yr) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
-          } else {
-            if (col + 0 < n) yr[0] = to_bf16(v0);
-            if (col + 1 < n) yr[1] = to_bf16(v1);
-            if (col + 2 < n) yr[2] = to_bf16(v2);
-            if (col + 3 < n) yr[3] = to_bf16(v3);
-          }
+    // ---- output ------------------------------------------------------------
+    // Accumulator element e of tile (i, jt) of this lane: weight row
+    // 64 * wave + 32 * i + 8 * (e / 4) + 4 * (lane / 32) + e % 4 of the tile,
+    // activation row 32 * jt + lane % 32.
+    const float st = b.st[p];
+    void* const y = b.y[p];
+    const int64_t ldy = b.ldy[p], n = b.n[p];
+    const bool vec = (ldy & 3) == 0;
+    const int64_t col0 = (int64_t)nt * kBN + 64 * wave + 4 * (lane >> 5);
+    auto write_y = [&](int u, f32x4 v) {
+      const int t = u >> 2, i = t / JT, jt = t % JT;
+      const int64_t row = m0 + 32 * jt + (lane & 31);
+      if (row >= b.m) return;
+      const int64_t col = col0 + 32 * i + 8 * (u & 3);
+      if (col >= n) return;
+      const float v0 = v[0] * st, v1 = v[1] * st, v2 = v[2] * st, v3 = v[3] * st;
+      if (b.y_bf16) {
+        uint16_t* yr = static_cast<uint16_t*>(y) + row * ldy + col;
+        if (vec && col + 4 <= n) {
+          *reinterpret_cast<uint2*>(yr) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
         } else {
-          float* yr = static_cast<float*>(y) + row * ldy + col;
-          if (vec && col + 4 <= n) {
-            *reinterpret_cast<f32x4*>(yr) = f32x4{v0, v1, v2, v3};
-          } else {
-            if (col + 0 < n) yr[0] = v0;
-            if (col + 1 < n) yr[1] = v1;
-            if (col + 2 < n) yr[2] = v2;
-            if (col + 3 < n) yr[3] = v3;
+          yr[0] = to_bf16(v0);
+          if (col + 1 < n) yr[1] = to_bf16(v1);
+          if (col + 2 < n) yr[2] = to_bf16(v2);
+          if (col + 3 < n) yr[3] = to_bf16(v3);
+        }
+      } else {
+        float* yr = static_cast<float*>(y) + row * ldy + col;
+        if (vec && col + 4 <= n) {
+          *reinterpret_cast<f32x4*>(yr) = f32x4{v0, v1, v2, v3};
+        } else {
+          yr[0] = v0;
+          if (col + 1 < n) yr[1] = v1;
+          if (col + 2 < n) yr[2] = v2;
+          if (col + 3 < n) yr[3] = v3;
+        }
+      }
+    };
+
+    if (ib == 0 && ie == iters) {
+#pragma unroll
+      for (int u = 0; u < 8 * JT; ++u) write_y(u, acc4<JT>(acc, u));
+    } else {
+      // Cut tile: publish this segment's sums, then the last contributor to
+      // arrive adds all contributions in k order.
+      const int slot = g_begin >= tile_g0 ? 0 : 1;  // this workgroup's first or last segment
+      const size_t lane_off = ((size_t)wave * 8 * JT * 64 + lane) * 4;
+      float* mine = partials + ((size_t)w * 2 + slot) * part_floats<JT>() + lane_off;
+#pragma unroll
+      for (int u = 0; u < 8 * JT; u += 4)
+        store4x4_coherent(mine + (size_t)u * 256, acc4<JT>(acc, u), acc4<JT>(acc, u + 1), acc4<JT>(acc, u + 2),
+                          acc4<JT>(acc, u + 3));
+      const int c_first = owner_of(tile_g0, b.total, b.wgs);
+      const int c_last = owner_of(tile_g0 + iters - 1, b.total, b.wgs);
+      if (arrive_last(counters + b.tile_base[p] + tile, (unsigned)(c_last - c_first + 1))) {
+#pragma unroll
+        for (int q = 0; q < JT / 2; ++q) {
+          // float4s 16q .. 16q + 15 of this lane, summed over the contributors in order
+          f32x4 s[16];
+          for (int c = c_first; c <= c_last; ++c) {
+            // Every contribution, this workgroup's own included, is read back
+            // from its slot: the accumulators need not stay live here.
+            f32x4 v[16];
+            const int cslot = share_begin(c, b.total, b.wgs) >= tile_g0 ? 0 : 1;
+            load16x4_strided_coherent(
+                partials + ((size_t)c * 2 + cslot) * part_floats<JT>() + lane_off + (size_t)(16 * q) * 256, v);
+            if (c == c_first) {
+#pragma unroll
+              for (int u = 0; u < 16; ++u) s[u] = v[u];
+            } else {
+#pragma unroll
+              for (int u = 0; u < 16; ++u) s[u] += v[u];
+            }
           }
+#pragma unroll
+          for (int u = 0; u < 16; ++u) write_y(16 * q + u, s[u]);
         }
       }
     }
+    g = tile_g0 + ie;
+  }
+}
+
+struct Plan {
+  int jt;         // activation-row tiles of 32 per workgroup tile
+  int64_t mrows;  // activation rows per launch (all of them unless the counter slots run out)
+};
+
+Plan prefill_plan(const Problem* p, int count, int64_t m) {
+  Plan pl;
+  pl.jt = m > 128 ? 8 : (m > 64 ? 4 : 2);
+  const int64_t bm = 32 * pl.jt;
+  int64_t ntiles = 0;
+  for (int i = 0; i < count; ++i) ntiles += (((p[i].n + 63) / 64) + 3) / 4;
+  // One counter per output tile of a launch: cut m so that a launch's tiles fit.
+  const int64_t max_mt = ntiles > 0 ? kCounterSlots / ntiles : 1;
+  const int64_t mt = (m + bm - 1) / bm;
+  pl.mrows = (mt <= max_mt ? mt : max_mt) * bm;
+  return pl;
+}
+
+size_t part_bytes(int jt) {
+  return (jt == 8 ? part_floats<8>() : jt == 4 ? part_floats<4>() : part_floats<2>()) * sizeof(float);
 }
 
 }  // namespace
 
-size_t prefill_workspace_bytes(int64_t, const Geometry&) { return 0; }
+size_t prefill_batch_workspace_bytes(const Problem* p, int count, int64_t m) {
+  if (m <= 0 || count <= 0) return 0;
+  size_t need = 0;
+  for (int c0 = 0; c0 < count; c0 += kMaxPre) {
+    const int cn = count - c0 < kMaxPre ? count - c0 : kMaxPre;
+    const Plan pl = prefill_plan(p + c0, cn, m);
+    const size_t b = kCounterBytes + (size_t)2 * kPreWgs * part_bytes(pl.jt);
+    if (b > need) need = b;
+  }
+  return need;
+}
+
+size_t prefill_workspace_bytes(int64_t m, const Geometry& g) {
+  Problem pr{nullptr, g.n, g.k, 1.0f, nullptr, g.k, nullptr, g.n};
+  return prefill_batch_workspace_bytes(&pr, 1, m);
+}
 
 hipError_t launch_zero_rows(void* y, int64_t m, int64_t n, int64_t ldy, bool y_bf16, hipStream_t s);
 
+hipError_t launch_prefill_batch(const Problem* p, int count, int64_t m, bool y_bf16, void* ws, hipStream_t s) {
+  if (m <= 0) return hipSuccess;
+  const size_t esize = y_bf16 ? 2 : 4;
+  // k == 0: the product is empty, the outputs are zero.
+  for (int i = 0; i < count; ++i)
+    if (p[i].n > 0 && p[i].k == 0) {
+      hipError_t e = launch_zero_rows(p[i].y, m, p[i].n, p[i].ldy, y_bf16, s);
+      if (e != hipSuccess) return e;
+    }
+  unsigned* counters = static_cast<unsigned*>(ws);
+  float* partials = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kCounterBytes);
+  for (int c0 = 0; c0 < count; c0 += kMaxPre) {
+    const int cn = count - c0 < kMaxPre ? count - c0 : kMaxPre;
+    // The problems of this launch that have work.
+    Problem q[kMaxPre];
+    int nq = 0;
+    for (int i = c0; i < c0 + cn; ++i)
+      if (p[i].n > 0 && p[i].k > 0) q[nq++] = p[i];
+    if (nq == 0) continue;
+    const Plan pl = prefill_plan(q, nq, m);
+    const int64_t bm = 32 * pl.jt;
+    for (int64_t r0 = 0; r0 < m; r0 += pl.mrows) {
+      const int64_t mr = m - r0 < pl.mrows ? m - r0 : pl.mrows;
+      PrefillBatch b{};
+      b.count = nq;
+      b.mtiles = (int)((mr + bm - 1) / bm);
+      b.y_bf16 = y_bf16 ? 1 : 0;
+      b.m = mr;
+      int64_t it = 0;
+      int tiles = 0;
+      for (int j = 0; j < nq; ++j) {
+        const Geometry g = geometry(q[j].n, q[j].k);
+        const int ntn = (int)((g.nrt + 3) / 4);
+        b.iter_begin[j] = it;
+        b.tile_base[j] = tiles;
+        b.iters[j] = (int)((q[j].k + kBK - 1) / kBK);
+        b.nkt[j] = (int)g.nkt;
+        b.nrt[j] = (int)g.nrt;
+        b.packed[j] = static_cast<const uint8_t*>(q[j].packed);
+        b.x[j] = q[j].x + r0 * q[j].ldx;
+        b.y[j] = static_cast<uint8_t*>(q[j].y) + (size_t)r0 * q[j].ldy * esize;
+        b.n[j] = q[j].n;
+        b.k[j] = q[j].k;
+        b.ldx[j] = q[j].ldx;
+        b.ldy[j] = q[j].ldy;
+        b.st[j] = q[j].st;
+        tiles += ntn * b.mtiles;
+        it += (int64_t)ntn * b.mtiles * b.iters[j];
+      }
+      b.iter_begin[nq] = it;
+      b.total = it;
+      int64_t wgs = it / kMinShare;
+      wgs = wgs < 1 ? 1 : (wgs > kPreWgs ? kPreWgs : wgs);
+      b.wgs = (int)wgs;
+      switch (pl.jt) {
+        case 8: hipLaunchKernelGGL(prefill_kernel<8>, dim3((unsigned)wgs), dim3(256), 0, s, b, counters, partials); break;
+        case 4: hipLaunchKernelGGL(prefill_kernel<4>, dim3((unsigned)wgs), dim3(256), 0, s, b, counters, partials); break;
+        default: hipLaunchKernelGGL(prefill_kernel<2>, dim3((unsigned)wgs), dim3(256), 0, s, b, counters, partials); break;
+      }
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_prefill(const void* packed, const Geometry& g, float st, const uint16_t* x, int64_t m, int64_t ldx,
-                          void* y, int64_t ldy, bool y_bf16, void*, hipStream_t s) {
+                          void* y, int64_t ldy, bool y_bf16, void* ws, hipStream_t s) {
   if (m == 0 || g.n == 0) return hipSuccess;
-  if (g.k == 0) return launch_zero_rows(y, m, g.n, ldy, y_bf16, s);
-  dim3 grid((unsigned)((m + kBM - 1) / kBM), (unsigned)((g.nrt + 1) / 2));
-  hipLaunchKernelGGL(prefill_kernel, grid, dim3(256), 0, s, static_cast<const uint8_t*>(packed), g.n, g.k,
-                     (int)g.nkt, st, x, m, ldx, y, ldy, y_bf16 ? 1 : 0);
-  return hipGetLastError();
+  Problem pr{packed, g.n, g.k, st, x, ldx, y, ldy};
+  return launch_prefill_batch(&pr, 1, m, y_bf16, ws, s);
 }
 
 }  // namespace nvfp4

@@ -84,3 +84,22 @@ def test_gemv_batched_ragged_mixed_shapes():
     for (p, n, k, st, x, y), (c, s, xb) in zip(items, refs):
         y_ref, sabs = oracle.gemm(c, s, st, xb[None, :])
         assert_within(y.cpu().numpy(), y_ref[0], sabs[0], what=f"gemv batched {n}x{k}")
+
+
+def test_prefill_batched_full_size():
+    """The 512-token prefill's three products (gate, up, down) in one launch,
+    sampled weight rows x all 512 tokens, fp32 output (strict bound)."""
+    dev = device()
+    items, refs = [], []
+    for mat in I.PREFILL_MATRICES:
+        c, s = I.nvfp4_matrix(I.PREFILL_512, mat.matrix_id, mat.n, mat.k)
+        x = I.activations(I.PREFILL_512, mat.matrix_id, 512, mat.k)
+        y = torch.empty((512, mat.n), dtype=torch.float32, device=dev)
+        items.append((pack_to_device(c, s, dev), mat.n, mat.k, I.TENSOR_SCALE, to_dev_bf16(x, dev), y))
+        refs.append((mat, c, s, x))
+    B.gemm_batched(items)
+    torch.cuda.synchronize()
+    for (p, n, k, st, xd, y), (mat, c, s, x) in zip(items, refs):
+        rows = sample_rows(n, 32, 400 + mat.matrix_id)
+        y_ref, sabs = oracle.gemm(c, s, st, x, rows=rows, nthreads=oracle_threads())
+        assert_within(y.cpu().numpy()[:, rows], y_ref, sabs, what=f"prefill batched {mat.name}")

@@ -123,3 +123,30 @@ def test_prefill_full_size(mat):
     x = I.activations(I.PREFILL_512, mat.matrix_id, 512, mat.k)
     rows = sample_rows(mat.n, 48, 200 + mat.matrix_id)
     check_both_dtypes(codes, scales, I.TENSOR_SCALE, x, rows=rows, what=f"prefill {mat.name}")
+
+
+@pytest.mark.parametrize("m,n,k", [(64, 256, 16384), (100, 300, 8192), (520, 700, 4096)])
+def test_prefill_tiles_cut_between_many_workgroups(m, n, k):
+    """Few output tiles over a long k: each tile's k range is shared by many
+    workgroups (up to 32 here), whose partial sums the last one adds in order."""
+    rng = np.random.default_rng(m * 13 + n + k)
+    codes, scales = random_matrix(rng, n, k)
+    x = I.bf16_round(rng.standard_normal((m, k)).astype(np.float32))
+    check_both_dtypes(codes, scales, I.TENSOR_SCALE, x, what=f"prefill cut m={m} {n}x{k}")
+
+
+def test_prefill_repeat_is_bit_identical_and_counters_return_to_zero():
+    """The fix-up order of cut tiles is fixed, so results do not depend on
+    which workgroup finishes a tile; every call leaves the counters zero."""
+    dev = device()
+    mat = I.PREFILL_MATRICES[2]
+    codes, scales = I.nvfp4_matrix(I.PREFILL_512, mat.matrix_id, mat.n, mat.k)
+    packed = pack_to_device(codes, scales, dev)
+    x = to_dev_bf16(I.activations(I.PREFILL_512, mat.matrix_id, 512, mat.k), dev)
+    need = B.gemm_workspace_bytes(512, mat.n, mat.k)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    y1 = B.gemm(packed, mat.n, mat.k, I.TENSOR_SCALE, x, ws=ws).clone()
+    y2 = B.gemm(packed, mat.n, mat.k, I.TENSOR_SCALE, x, ws=ws).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert int(torch.count_nonzero(ws[: 1 << 18])) == 0
