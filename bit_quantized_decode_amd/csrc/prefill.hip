@@ -50,6 +50,7 @@ struct PrefillBatch {
   int iters[kMaxPre];               // iterations per tile
   int nkt[kMaxPre];
   int nrt[kMaxPre];
+  int ntn[kMaxPre];                 // weight-row tiles (of 256 rows)
   const uint8_t* packed[kMaxPre];
   const uint16_t* x[kMaxPre];
   void* y[kMaxPre];
@@ -57,13 +58,29 @@ struct PrefillBatch {
   float st[kMaxPre];
 };
 
+// One problem's fields, as the kernel uses them.
+struct ProbView {
+  int64_t iter_begin;
+  const uint8_t* packed;
+  const uint16_t* x;
+  void* y;
+  int64_t n, k, ldx, ldy;
+  float st;
+  int tile_base, iters, nkt, nrt, ntn;
+};
+
 // Share w covers global iterations [share_begin(w), share_begin(w + 1)).
 __device__ __forceinline__ int64_t share_begin(int w, int64_t total, int wgs) { return ((int64_t)w * total) / wgs; }
 // The share holding global iteration g.
 __device__ __forceinline__ int owner_of(int64_t g, int64_t total, int wgs) { return (int)(((g + 1) * wgs - 1) / total); }
 
-// LDS byte offset of 16-byte chunk c (0..7) of activation row r (128 bytes a row).
-__device__ __forceinline__ int swz(int r, int c) { return r * (kBK * 2) + ((c ^ (r & 7)) << 4); }
+// LDS byte offset of 16-byte chunk c (0..7) of activation row r (128 bytes a
+// row).  The chunk is XOR-permuted by a row function that differs between
+// any 8 consecutive rows and between the 8 rows of either parity among any 16
+// consecutive rows, so that a wavefront's 16-byte reads of one chunk column
+// are bank-conflict free whether the LDS serves 128 or 256 bytes a clock.
+__device__ __forceinline__ int swz_key(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
+__device__ __forceinline__ int swz(int r, int c) { return r * (kBK * 2) + ((c ^ swz_key(r)) << 4); }
 
 // Weights of one iteration for one lane: two 1 KB chunks of the packed tile
 // (k steps 0-1 and 2-3 of the iteration) and the scale dword of rows r and
@@ -80,144 +97,234 @@ struct WStage {
 template <int JT>
 constexpr size_t part_floats() { return (size_t)4 * 8 * JT * 64 * 4; }
 
-// Four 16-byte stores 1 KB apart, through to memory (not held in this XCD's
-// L2); the trailing nops cover the store-data read of the last store.
-__device__ __forceinline__ void store4x4_coherent(float* p, f32x4 a, f32x4 b, f32x4 c, f32x4 d) {
-  asm volatile(
-      "global_store_dwordx4 %0, %1, off sc1\n"
-      "global_store_dwordx4 %0, %2, off offset:1024 sc1\n"
-      "global_store_dwordx4 %0, %3, off offset:2048 sc1\n"
-      "global_store_dwordx4 %0, %4, off offset:3072 sc1\n"
-      "s_nop 1"
-      :
-      : "v"(p), "v"(a), "v"(b), "v"(c), "v"(d)
-      : "memory");
+// Partial-sum slot access.  Stores write through to memory (cache policy
+// sc1), so that a finisher on any XCD can read them.  A finisher on the
+// writers' own XCD reads through its L2 (sc0: past the L1 only); any other
+// reads from memory (sc1).
+struct PartBuf {
+  __amdgpu_buffer_rsrc_t r;
+};
+__device__ __forceinline__ PartBuf part_buf(float* partials, size_t slot, size_t floats) {
+  PartBuf b;
+  b.r = __builtin_amdgcn_make_buffer_rsrc(partials + slot * floats, 0, (int)(floats * sizeof(float)), 0x00020000);
+  return b;
 }
-
-// Sixteen 16-byte loads 1 KB apart that bypass the non-coherent caches; the
-// wait sits in the same statement, so none is in flight when it ends.
-__device__ __forceinline__ void load16x4_strided_coherent(const float* p, f32x4 (&v)[16]) {
-  const char* c0 = reinterpret_cast<const char*>(p);
-  const char* c1 = c0 + 4096;
-  const char* c2 = c0 + 8192;
-  const char* c3 = c0 + 12288;
-  asm volatile(
-      "global_load_dwordx4 %0, %16, off sc1\n"
-      "global_load_dwordx4 %1, %16, off offset:1024 sc1\n"
-      "global_load_dwordx4 %2, %16, off offset:2048 sc1\n"
-      "global_load_dwordx4 %3, %16, off offset:3072 sc1\n"
-      "global_load_dwordx4 %4, %17, off sc1\n"
-      "global_load_dwordx4 %5, %17, off offset:1024 sc1\n"
-      "global_load_dwordx4 %6, %17, off offset:2048 sc1\n"
-      "global_load_dwordx4 %7, %17, off offset:3072 sc1\n"
-      "global_load_dwordx4 %8, %18, off sc1\n"
-      "global_load_dwordx4 %9, %18, off offset:1024 sc1\n"
-      "global_load_dwordx4 %10, %18, off offset:2048 sc1\n"
-      "global_load_dwordx4 %11, %18, off offset:3072 sc1\n"
-      "global_load_dwordx4 %12, %19, off sc1\n"
-      "global_load_dwordx4 %13, %19, off offset:1024 sc1\n"
-      "global_load_dwordx4 %14, %19, off offset:2048 sc1\n"
-      "global_load_dwordx4 %15, %19, off offset:3072 sc1\n"
-      "s_waitcnt vmcnt(0)"
-      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
-        "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]),
-        "=&v"(v[15])
-      : "v"(c0), "v"(c1), "v"(c2), "v"(c3)
-      : "memory");
+// Byte offset = voff (per lane) + soff (uniform).
+__device__ __forceinline__ void store_part(const PartBuf& b, int voff, int soff, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), b.r, voff, soff, 16);
 }
+template <int POLICY>  // 1: through this XCD's L2 (sc0); 16: from memory (sc1)
+__device__ __forceinline__ f32x4 load_part(const PartBuf& b, int voff, int soff) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(b.r, voff, soff, POLICY));
+}
+template <int V>
+struct Policy {
+  static constexpr int value = V;
+};
 
-// One 16-k step KS (0..3) of an iteration: A operands for weight rows r and
-// 32 + r from the resident codes, B operands for the JT activation tiles
-// from LDS, 2 * JT MFMAs.
-template <int KS, int JT>
-__device__ __forceinline__ void kstep(const uint8_t* xl, int lane, const WStage& w, f32x16 (&acc)[2][JT]) {
-  constexpr int J = KS & 1;
+// The XCD this wavefront runs on (hardware register XCC_ID, bits 3:0).
+__device__ __forceinline__ unsigned xcc_id() { return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 15u; }
+
+// Per-tile XCD masks live in the upper half of the counter area.
+constexpr int kMaskBase = (int)(kCounterSlots / 2);
+
+// A operands of k step KS (0..3) of an iteration: weight rows r (a0) and
+// 32 + r (a1).  Chunk KS / 2 of the iteration holds k steps 2 (KS / 2) and
+// 2 (KS / 2) + 1 (dwords 0-1 and 2-3); the 16-k block of k step KS is byte KS
+// of the iteration's scale dword.
+struct AOps {
+  bf16x8 a0, a1;
+};
+
+template <int KS>
+__device__ __forceinline__ void dequant_ks(const WStage& w, AOps& o) {
   const u32x4 q = KS < 2 ? w.q0 : w.q1;
-  const bf16x8 a0 = dequant8(q[2 * J], e4m3<KS>(w.sa));
-  const bf16x8 a1 = dequant8(q[2 * J + 1], e4m3<KS>(w.sb));
-  const int chunk = 2 * KS + (lane >> 5);
+  o.a0 = dequant8(q[2 * (KS & 1)], e4m3<KS>(w.sa));
+  o.a1 = dequant8(q[2 * (KS & 1) + 1], e4m3<KS>(w.sb));
+}
+
+// B operands of k step KS: the JT activation tiles' 16-k slices from LDS.
+template <int KS, int JT>
+__device__ __forceinline__ void load_b(const uint8_t* xl, int lane, bf16x8 (&b)[JT]) {
+  const uint8_t* row = xl + (lane & 31) * (kBK * 2);
+  const int c = ((2 * KS + (lane >> 5)) ^ swz_key(lane & 31)) << 4;  // swz_key(32 jt + r) == swz_key(r)
+#pragma unroll
+  for (int jt = 0; jt < JT; ++jt)
+    b[jt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + jt * 32 * (kBK * 2) + c));
+}
+
+template <int JT>
+__device__ __forceinline__ void mfma_ks(const AOps& a, const bf16x8 (&b)[JT], f32x16 (&acc)[2][JT]) {
 #pragma unroll
   for (int jt = 0; jt < JT; ++jt) {
-    const bf16x8 bx = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xl + swz(32 * jt + (lane & 31), chunk)));
-    acc[0][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bx, acc[0][jt], 0, 0, 0);
-    acc[1][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bx, acc[1][jt], 0, 0, 0);
+    acc[0][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.a0, b[jt], acc[0][jt], 0, 0, 0);
+    acc[1][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.a1, b[jt], acc[1][jt], 0, 0, 0);
   }
 }
 
+// Instruction interleave of one k step: each MFMA is followed by a share of
+// the next k step's operand work (an LDS read, dequantisation VALU), so that
+// this work issues while the matrix core runs; memory loads go wherever their
+// addresses are ready.
 template <int JT>
-__device__ __forceinline__ f32x4 acc4(const f32x16 (&acc)[2][JT], int u) {
-  // float4 u of a lane: accumulator tile t = u / 4 (i = t / JT, jt = t % JT), elements 4 * (u % 4) ..
-  const f32x16& a = acc[(u >> 2) / JT][(u >> 2) % JT];
-  const int e = 4 * (u & 3);
-  return f32x4{a[e], a[e + 1], a[e + 2], a[e + 3]};
+__device__ __forceinline__ void interleave_ks() {
+#pragma unroll
+  for (int j = 0; j < 2 * JT; ++j) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA
+    if (j < JT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // DS read
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);                 // VALU
+  }
 }
 
-template <int JT>
+
+// One 16-byte-per-lane load from memory straight into LDS: lane l's 16
+// bytes land at dst + 16 l (dst is the same for the whole wavefront).  Kept
+// out of lambdas: a lambda body is also compiled for the host, where this
+// builtin does not exist.
+__device__ __forceinline__ void load_lds16(const void* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(const_cast<void*>(src), (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
+// Wavefront's half H (accumulator tiles acc[H][*]) into its LDS buffer:
+// activation row 32 jt + lane % 32 at byte 128 row, the 4 columns
+// 8 e4 + 4 (lane / 32) of the half as 16-byte chunk 2 e4 + lane / 32.
+template <int H, int JT>
+__device__ __forceinline__ void stage_half(const f32x16 (&acc)[2][JT], uint8_t* buf, int lane) {
+#pragma unroll
+  for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const f32x16& a = acc[H][jt];
+      *reinterpret_cast<f32x4*>(buf + swz(32 * jt + (lane & 31), 2 * e4 + (lane >> 5))) =
+          f32x4{a[4 * e4], a[4 * e4 + 1], a[4 * e4 + 2], a[4 * e4 + 3]};
+    }
+}
+
+// vmcnt-only wait (gfx9 s_waitcnt encoding; expcnt and lgkmcnt left free).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// vmcnt <= N and lgkmcnt == 0.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+// Workgroup barrier that adds no waits of its own: the loads into LDS that
+// the next iteration reads are waited for explicitly (wait_vmcnt) before it.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int JT, bool KFULL>
 __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillBatch b, unsigned* __restrict__ counters,
                                                          float* __restrict__ partials) {
   constexpr int kBM = 32 * JT;
   constexpr int kXBuf = kBM * kBK * 2;  // bytes of one activation buffer
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kXBuf];
+  // Four activation buffers, each its own LDS object: accesses to distinct
+  // objects carry distinct alias scopes, which lets the compiler see that a
+  // load into one buffer does not feed reads of another (else it would wait
+  // for every load in flight before each LDS read).
+  __shared__ __attribute__((aligned(16))) uint8_t xb0[kXBuf];
+  __shared__ __attribute__((aligned(16))) uint8_t xb1[kXBuf];
+  __shared__ __attribute__((aligned(16))) uint8_t xb2[kXBuf];
+  __shared__ __attribute__((aligned(16))) uint8_t xb3[kXBuf];
+#define NVFP4_XBUF(I) ((I) == 0 ? xb0 : (I) == 1 ? xb1 : (I) == 2 ? xb2 : xb3)
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
 
   // Share of this workgroup.  Dispatch places workgroup b on XCD b % 8; give
   // each XCD a contiguous run of shares.
+  // Scalars used inside the lambdas below are copied out of the argument
+  // struct: a lambda capturing the struct itself would take its address and
+  // force a copy of it into scratch memory.
+  const int b_wgs = b.wgs, b_count = b.count;
+  const int64_t b_total = b.total, b_m = b.m;
+  const bool b_ybf16 = b.y_bf16 != 0;
   int w = (int)blockIdx.x;
-  if ((b.wgs & 7) == 0) w = (int)(blockIdx.x & 7) * (b.wgs >> 3) + (int)(blockIdx.x >> 3);
-  const int64_t g_begin = share_begin(w, b.total, b.wgs);
-  const int64_t g_end = share_begin(w + 1, b.total, b.wgs);
-
-  const int xr0 = tid >> 3, xc = tid & 7;  // activation loader: rows xr0 + 32j, 16-byte chunk xc
+  if ((b_wgs & 7) == 0) w = (int)(blockIdx.x & 7) * (b_wgs >> 3) + (int)(blockIdx.x >> 3);
+  const int64_t g_begin = share_begin(w, b_total, b_wgs);
+  const int64_t g_end = share_begin(w + 1, b_total, b_wgs);
 
   for (int64_t g = g_begin; g < g_end;) {
     // ---- locate the segment: problem p, tile (mt, nt), iterations [ib, ie)
+    // Per-problem fields are picked with static indices: indexing the
+    // argument arrays at run time would copy them to scratch memory (and lose
+    // the address space of the pointers in them).
     int p = 0;
-    while (p + 1 < b.count && g >= b.iter_begin[p + 1]) ++p;
-    const int iters = b.iters[p];
-    const int64_t gl = g - b.iter_begin[p];
+#pragma unroll
+    for (int i = 1; i < kMaxPre; ++i)
+      if (i < b_count && g >= b.iter_begin[i]) p = i;
+    ProbView pv;
+#pragma unroll
+    for (int i = 0; i < kMaxPre; ++i)
+      if (i == p) pv = ProbView{b.iter_begin[i], b.packed[i], b.x[i], b.y[i], b.n[i], b.k[i], b.ldx[i], b.ldy[i],
+                                b.st[i], b.tile_base[i], b.iters[i], b.nkt[i], b.nrt[i], b.ntn[i]};
+    const int iters = pv.iters;
+    const int64_t gl = g - pv.iter_begin;
     const int tile = (int)(gl / iters);
     const int ib = (int)(gl - (int64_t)tile * iters);
-    const int64_t tile_g0 = b.iter_begin[p] + (int64_t)tile * iters;
+    const int64_t tile_g0 = pv.iter_begin + (int64_t)tile * iters;
     const int ie = (int)(g_end - tile_g0 < iters ? g_end - tile_g0 : iters);
-    const int mt = tile % b.mtiles, nt = tile / b.mtiles;
+    // Tiles run activation-slab-major, so the shares of one XCD mostly read one slab of activation rows.
+    const int mt = tile / pv.ntn, nt = tile % pv.ntn;
     const int64_t m0 = (int64_t)mt * kBM;
-    const int64_t kdim = b.k[p];
-    const int nkt = b.nkt[p];
+    const int64_t kdim = pv.k;
+    const int nkt = pv.nkt;
 
-    // Activation sources (rows past m re-read row m-1; their outputs are not written).
-    const uint16_t* xsrc[JT];
+    // Activations go from memory straight into LDS: load j of this wavefront
+    // fills the 1 KB block q = wave * JT + j of a buffer, lane l landing at
+    // byte 16 l -- row 8 q + l / 8, physical chunk l % 8 -- so lane l fetches
+    // the logical chunk that the swizzle puts there.  Rows past m re-read row
+    // m - 1 (their outputs are not written).
+    const uint16_t* xrow[JT];
+    int c8[JT];  // k offset (elements) of this lane's chunk within an iteration
 #pragma unroll
     for (int j = 0; j < JT; ++j) {
-      int64_t row = m0 + xr0 + 32 * j;
-      row = row < b.m ? row : b.m - 1;
-      xsrc[j] = b.x[p] + row * b.ldx[p] + 8 * xc;
+      const int row = 8 * (wave * JT + j) + (lane >> 3);
+      c8[j] = 8 * ((lane & 7) ^ swz_key(row));
+      int64_t r = m0 + row;
+      r = r < b_m ? r : b_m - 1;
+      xrow[j] = pv.x + r * pv.ldx;
     }
+    auto dma_x = [&](int it, uint8_t* xbuf) __attribute__((always_inline)) {
+      uint8_t* dst = xbuf + wave * JT * 1024;
+#pragma unroll
+      for (int j = 0; j < JT; ++j) {
+        int64_t kk = (int64_t)it * kBK + c8[j];
+        if (!KFULL) kk = kk < kdim ? kk : kdim - 8;  // in bounds; zeroed once landed
+        load_lds16(xrow[j] + kk, dst + j * 1024);
+      }
+    };
+    // Iteration it's chunks at k >= K must read as zeros (K % 64 != 0 only):
+    // each lane clears the chunks it loaded, after they have landed.
+    auto zero_tail = [&](int it, uint8_t* xbuf) __attribute__((always_inline)) {
+      if (KFULL || it != iters - 1) return;
+#pragma unroll
+      for (int j = 0; j < JT; ++j)
+        if ((int64_t)it * kBK + c8[j] >= kdim)
+          *reinterpret_cast<u32x4*>(xbuf + (wave * JT + j) * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+    };
+
     // Weight source: this wavefront's packed row tile (clamped; rows past n are not written).
     int rt = nt * 4 + wave;
-    rt = rt < b.nrt[p] ? rt : b.nrt[p] - 1;
-    const uint8_t* wt = b.packed[p] + (size_t)rt * nkt * kTileBytes;
-    const uint8_t* wcode = wt + lane * 16;
-    const uint8_t* wscale = wt + kScaleOffset + 32 * (lane & 31);
-
-    auto load_w = [&](int it, WStage& s) {
-      const size_t t = (size_t)(it >> 2) * kTileBytes;
-      const int sub = it & 3;
-      s.q0 = load16(wcode + t + (2 * sub) * 1024);
-      s.q1 = load16(wcode + t + (2 * sub + 1) * 1024);
-      s.sa = *reinterpret_cast<const uint32_t*>(wscale + t + 4 * sub);
-      s.sb = *reinterpret_cast<const uint32_t*>(wscale + t + 16 + 4 * sub);
-    };
-    auto load_x = [&](int it, u32x4 (&v)[JT]) {
-      const bool in = (int64_t)it * kBK + 8 * xc < kdim;
-#pragma unroll
-      for (int j = 0; j < JT; ++j) v[j] = in ? load16(xsrc[j] + (int64_t)it * kBK) : u32x4{0u, 0u, 0u, 0u};
-    };
-    auto store_x = [&](int buf, const u32x4 (&v)[JT]) {
-      uint8_t* xl = lds + buf * kXBuf;
-#pragma unroll
-      for (int j = 0; j < JT; ++j) *reinterpret_cast<u32x4*>(xl + swz(xr0 + 32 * j, xc)) = v[j];
+    rt = rt < pv.nrt ? rt : pv.nrt - 1;
+    // Addresses: a wavefront-uniform base (scalar registers) plus a fixed
+    // 32-bit per-lane offset, so no per-step vector address arithmetic.
+    const uint8_t* wt = pv.packed + (size_t)rt * nkt * kTileBytes;
+    const uint32_t lane_code = lane * 16;
+    const uint32_t lane_scale = kScaleOffset + 32 * (lane & 31);
+    auto load_w = [&](int it, WStage& s) __attribute__((always_inline)) {
+      const uint8_t* tb = wt + (size_t)(it >> 2) * kTileBytes;
+      const uint8_t* cb = tb + (it & 3) * 2048;
+      const uint8_t* sb = tb + 4 * (it & 3);
+      s.q0 = load16(cb + lane_code);
+      s.q1 = load16(cb + 1024 + lane_code);
+      s.sa = *reinterpret_cast<const uint32_t*>(sb + lane_scale);
+      s.sb = *reinterpret_cast<const uint32_t*>(sb + 16 + lane_scale);
     };
 
     f32x16 acc[2][JT];
@@ -226,63 +333,109 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillBatch b, u
 #pragma unroll
       for (int j = 0; j < JT; ++j) acc[i][j] = f32x16{};
 
-    // ---- pipeline.  Loads past the segment re-read its last iteration, so
-    // each executed step issues the same loads in the same order.
+    // ---- pipeline.  Four LDS activation buffers: iteration it lives in
+    // buffer (it - ib) % 4, loaded three iterations ahead; weights are loaded
+    // four iterations ahead; each k step's operands are read from LDS and
+    // dequantised during the previous k step's MFMAs.  Loads past the segment
+    // re-read its last iteration, so every step issues the same memory
+    // instructions in the same order -- per step JT activation loads (k step
+    // 0) and four weight loads (k step 2) -- and the main loop has no branches.
+    // Before k step 3 of step it the activations of it + 1 (loaded at k step
+    // 0 of step it - 2) must have landed; after them 4 + JT + 4 + JT + 4
+    // memory instructions have been issued.
+    constexpr int kVmAfterX = 12 + 2 * JT;
     const int last = ie - 1;
-    auto clampi = [&](int it) { return it < last ? it : last; };
+    auto clampi = [&](int it) __attribute__((always_inline)) { return it < last ? it : last; };
     WStage w0, w1, w2, w3;
-    u32x4 xa[JT], xb[JT];
     load_w(ib, w0);
     load_w(clampi(ib + 1), w1);
     load_w(clampi(ib + 2), w2);
     load_w(clampi(ib + 3), w3);
-    load_x(ib, xa);
-    load_x(clampi(ib + 1), xb);
-    store_x(0, xa);
-    __syncthreads();
-    // Step S of a group of four (iteration it = i + S, LDS buffer S & 1):
-    // issue the activation loads of it + 2, multiply it, stage it + 1's
-    // activations into the other buffer, issue the weight loads of it + 4.
-#define NVFP4_PREFILL_STEP(S, XCUR, XNEXT, WCUR)                        \
-  if (i + (S) < ie) {                                                   \
+    dma_x(ib, NVFP4_XBUF(0));
+    dma_x(clampi(ib + 1), NVFP4_XBUF(1));
+    dma_x(clampi(ib + 2), NVFP4_XBUF(2));
+    wait_vmcnt<0>();
+    zero_tail(ib, NVFP4_XBUF(0));
+    zero_tail(clampi(ib + 1), NVFP4_XBUF(1));
+    zero_tail(clampi(ib + 2), NVFP4_XBUF(2));
+    barrier_only();
+    AOps ac, an;
+    bf16x8 bc[JT], bn[JT];
+    load_b<0, JT>(NVFP4_XBUF(0), lane, bc);
+    dequant_ks<0>(w0, ac);
+    // Step S of a group of four: iteration it = i + S in buffer S.  On entry
+    // ac / bc hold k step 0's operands; on exit, iteration it + 1's.  Before
+    // k step 3 every wavefront waits for its loads of it + 1's activations
+    // (which also covers the weights of it + 1) and for its own LDS reads,
+    // then the workgroup barrier publishes buffer it + 1, so that k step 3
+    // can read it + 1's first B operands while its MFMAs run.
+#define NVFP4_PREFILL_STEP(S, WC, WN)                                   \
+  {                                                                     \
     const int it = i + (S);                                             \
-    load_x(clampi(it + 2), XCUR);                                       \
-    {                                                                   \
-      const uint8_t* xl = lds + ((S) & 1) * kXBuf;                      \
-      kstep<0, JT>(xl, lane, WCUR, acc);                                \
-      kstep<1, JT>(xl, lane, WCUR, acc);                                \
-      kstep<2, JT>(xl, lane, WCUR, acc);                                \
-      kstep<3, JT>(xl, lane, WCUR, acc);                                \
-    }                                                                   \
-    if (it + 1 < ie) store_x(((S) + 1) & 1, XNEXT);                     \
-    load_w(clampi(it + 4), WCUR);                                       \
-    __syncthreads();                                                    \
+    const uint8_t* xcur = NVFP4_XBUF(S);                                \
+    load_b<1, JT>(xcur, lane, bn);                                      \
+    dma_x(clampi(it + 3), NVFP4_XBUF(((S) + 3) & 3));                   \
+    dequant_ks<1>(WC, an);                                              \
+    mfma_ks<JT>(ac, bc, acc);                                           \
+    interleave_ks<JT>();                                                \
+    __builtin_amdgcn_sched_barrier(0);                                  \
+    load_b<2, JT>(xcur, lane, bc);                                      \
+    dequant_ks<2>(WC, ac);                                              \
+    mfma_ks<JT>(an, bn, acc);                                           \
+    interleave_ks<JT>();                                                \
+    __builtin_amdgcn_sched_barrier(0);                                  \
+    load_b<3, JT>(xcur, lane, bn);                                      \
+    dequant_ks<3>(WC, an);                                              \
+    load_w(clampi(it + 4), WC);                                         \
+    mfma_ks<JT>(ac, bc, acc);                                           \
+    interleave_ks<JT>();                                                \
+    __builtin_amdgcn_sched_barrier(0);                                  \
+    wait_vmcnt_lgkm0<kVmAfterX>();                                      \
+    zero_tail(it + 1, NVFP4_XBUF(((S) + 1) & 3));                       \
+    barrier_only();                                                     \
+    __builtin_amdgcn_sched_barrier(0);                                  \
+    load_b<0, JT>(NVFP4_XBUF(((S) + 1) & 3), lane, bc);                 \
+    dequant_ks<0>(WN, ac);                                              \
+    mfma_ks<JT>(an, bn, acc);                                           \
+    interleave_ks<JT>();                                                \
+    __builtin_amdgcn_sched_barrier(0);                                  \
   }
-    for (int i = ib; i < ie; i += 4) {
-      NVFP4_PREFILL_STEP(0, xa, xb, w0)
-      NVFP4_PREFILL_STEP(1, xb, xa, w1)
-      NVFP4_PREFILL_STEP(2, xa, xb, w2)
-      NVFP4_PREFILL_STEP(3, xb, xa, w3)
+    int i = ib;
+    for (; i + 4 <= ie; i += 4) {
+      NVFP4_PREFILL_STEP(0, w0, w1)
+      NVFP4_PREFILL_STEP(1, w1, w2)
+      NVFP4_PREFILL_STEP(2, w2, w3)
+      NVFP4_PREFILL_STEP(3, w3, w0)
     }
+    if (i < ie) NVFP4_PREFILL_STEP(0, w0, w1)
+    if (i + 1 < ie) NVFP4_PREFILL_STEP(1, w1, w2)
+    if (i + 2 < ie) NVFP4_PREFILL_STEP(2, w2, w3)
 #undef NVFP4_PREFILL_STEP
 
     // ---- output ------------------------------------------------------------
     // Accumulator element e of tile (i, jt) of this lane: weight row
     // 64 * wave + 32 * i + 8 * (e / 4) + 4 * (lane / 32) + e % 4 of the tile,
-    // activation row 32 * jt + lane % 32.
-    const float st = b.st[p];
-    void* const y = b.y[p];
-    const int64_t ldy = b.ldy[p], n = b.n[p];
+    // activation row 32 * jt + lane % 32.  The tile leaves the registers
+    // through LDS one half (i) at a time: wavefront v writes its columns
+    // [64 v + 32 i, +32) of all BM activation rows into activation buffer v
+    // (row r at byte 128 r, 16-byte column chunk c at the swizzled slot), and
+    // then all threads move whole 16-byte chunks -- coalesced output rows, or
+    // partial sums in chunk order (half i, buffer v, row r, chunk c at
+    // ((i * 4 + v) * BM + r) * 8 + c).
+    wait_vmcnt<0>();  // activation loads past the segment still target the buffers
+    __syncthreads();
+    const float st = pv.st;
+    void* const y = pv.y;
+    const int64_t ldy = pv.ldy, n = pv.n;
     const bool vec = (ldy & 3) == 0;
-    const int64_t col0 = (int64_t)nt * kBN + 64 * wave + 4 * (lane >> 5);
-    auto write_y = [&](int u, f32x4 v) {
-      const int t = u >> 2, i = t / JT, jt = t % JT;
-      const int64_t row = m0 + 32 * jt + (lane & 31);
-      if (row >= b.m) return;
-      const int64_t col = col0 + 32 * i + 8 * (u & 3);
-      if (col >= n) return;
-      const float v0 = v[0] * st, v1 = v[1] * st, v2 = v[2] * st, v3 = v[3] * st;
-      if (b.y_bf16) {
+    uint8_t* const mybuf = wave == 0 ? NVFP4_XBUF(0) : wave == 1 ? NVFP4_XBUF(1) : wave == 2 ? NVFP4_XBUF(2) : NVFP4_XBUF(3);
+    // 4 output columns (chunk c of buffer v, half h) of activation row r, scaled by s_t.
+    auto store_y = [&](int h, int v, int r, int c, f32x4 val) __attribute__((always_inline)) {
+      const int64_t row = m0 + r;
+      const int64_t col = (int64_t)nt * kBN + 64 * v + 32 * h + 4 * c;
+      if (row >= b_m || col >= n) return;
+      const float v0 = val[0] * st, v1 = val[1] * st, v2 = val[2] * st, v3 = val[3] * st;
+      if (b_ybf16) {
         uint16_t* yr = static_cast<uint16_t*>(y) + row * ldy + col;
         if (vec && col + 4 <= n) {
           *reinterpret_cast<uint2*>(yr) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
@@ -304,49 +457,142 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillBatch b, u
         }
       }
     };
+    // Thread tid moves chunks q = v * JT + j of a half: buffer v, local chunk
+    // e = tid + 256 j, i.e. activation row tid / 8 + 32 j, column chunk tid % 8.
+    // When the whole tile lies inside y (and rows are 16-byte aligned) the
+    // stores need no checks: one per-thread base pointer, a scalar row stride.
+    const bool y_full = vec && m0 + kBM <= b_m && (int64_t)nt * kBN + kBN <= n;
+    const int64_t esize = b_ybf16 ? 2 : 4;
+    uint8_t* const ythr =
+        static_cast<uint8_t*>(y) + ((m0 + (tid >> 3)) * ldy + (int64_t)nt * kBN + 4 * (tid & 7)) * esize;
+    const int64_t yrow32 = 32 * ldy * esize;
+    auto store_fast = [&](int h, int v, int j, f32x4 val) __attribute__((always_inline)) {
+      uint8_t* yr = ythr + j * yrow32 + (64 * v + 32 * h) * esize;
+      if (b_ybf16)
+        *reinterpret_cast<uint2*>(yr) = make_uint2(pack_bf16x2(val[0] * st, val[1] * st), pack_bf16x2(val[2] * st, val[3] * st));
+      else
+        *reinterpret_cast<f32x4*>(yr) = f32x4{val[0] * st, val[1] * st, val[2] * st, val[3] * st};
+    };
+    auto buf_of = [&](int v) __attribute__((always_inline)) -> uint8_t* {
+      return v == 0 ? NVFP4_XBUF(0) : v == 1 ? NVFP4_XBUF(1) : v == 2 ? NVFP4_XBUF(2) : NVFP4_XBUF(3);
+    };
+    auto write_half = [&](int h) __attribute__((always_inline)) {
+      if (y_full) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int j = 0; j < JT; ++j) {
+            const int e = tid + 256 * j;
+            store_fast(h, v, j, *reinterpret_cast<const f32x4*>(NVFP4_XBUF(v) + swz(e >> 3, e & 7)));
+          }
+        return;
+      }
+#pragma unroll 1
+      for (int q = 0; q < 4 * JT; ++q) {
+        const int v = q / JT, e = tid + 256 * (q % JT);
+        store_y(h, v, e >> 3, e & 7, *reinterpret_cast<const f32x4*>(buf_of(v) + swz(e >> 3, e & 7)));
+      }
+    };
 
     if (ib == 0 && ie == iters) {
-#pragma unroll
-      for (int u = 0; u < 8 * JT; ++u) write_y(u, acc4<JT>(acc, u));
+      stage_half<0, JT>(acc, mybuf, lane);
+      __syncthreads();
+      write_half(0);
+      __syncthreads();
+      stage_half<1, JT>(acc, mybuf, lane);
+      __syncthreads();
+      write_half(1);
     } else {
-      // Cut tile: publish this segment's sums, then the last contributor to
-      // arrive adds all contributions in k order.
+      // Cut tile: publish this segment's sums (written through to memory),
+      // note this workgroup's XCD in the tile's mask, and let the last
+      // contributor to arrive add all contributions in k order.
       const int slot = g_begin >= tile_g0 ? 0 : 1;  // this workgroup's first or last segment
-      const size_t lane_off = ((size_t)wave * 8 * JT * 64 + lane) * 4;
-      float* mine = partials + ((size_t)w * 2 + slot) * part_floats<JT>() + lane_off;
+      const PartBuf mine = part_buf(partials, (size_t)w * 2 + slot, part_floats<JT>());
+      auto publish_half = [&](int h) __attribute__((always_inline)) {
+#pragma unroll 4
+        for (int q = 0; q < 4 * JT; ++q) {
+          const int v = q / JT, e = tid + 256 * (q % JT);
+          store_part(mine, tid * 16, ((h * 4 + v) * kBM * 8 + 256 * (q % JT)) * 16,
+                     *reinterpret_cast<const f32x4*>(buf_of(v) + swz(e >> 3, e & 7)));
+        }
+      };
+      stage_half<0, JT>(acc, mybuf, lane);
+      __syncthreads();
+      publish_half(0);
+      __syncthreads();
+      stage_half<1, JT>(acc, mybuf, lane);
+      __syncthreads();
+      publish_half(1);
+      const int gtile = pv.tile_base + tile;
+      const unsigned xcc = xcc_id();
+      if (threadIdx.x == 0)
+        __hip_atomic_fetch_or(counters + kMaskBase + gtile, 1u << xcc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int c_first = owner_of(tile_g0, b_total, b_wgs);
+      const int c_last = owner_of(tile_g0 + iters - 1, b_total, b_wgs);
+      if (arrive_last(counters + gtile, (unsigned)(c_last - c_first + 1))) {
+        // Every contributor ran on this XCD: their sums are in this XCD's L2
+        // and are read from there; else from memory.
+        const unsigned mask = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(counters + kMaskBase + gtile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        __syncthreads();
+        if (threadIdx.x == 0)
+          __hip_atomic_store(counters + kMaskBase + gtile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool local = mask == (1u << xcc);
+        // ((p_first + p_next) + ...) in contributor (k) order, into the LDS
+        // chunks; every contribution, this workgroup's own included, is read
+        // from its slot, so the accumulators are dead once published.
+        // ((p_first + p_next) + ...) in contributor (k) order, summed in
+        // registers two buffers' chunks at a time and stored from there;
+        // every contribution, this workgroup's own included, is read from
+        // its slot, so the accumulators are dead once published.
+        auto finish_half = [&](int h, auto policy) __attribute__((always_inline)) {
+          constexpr int POL = decltype(policy)::value;
 #pragma unroll
-      for (int u = 0; u < 8 * JT; u += 4)
-        store4x4_coherent(mine + (size_t)u * 256, acc4<JT>(acc, u), acc4<JT>(acc, u + 1), acc4<JT>(acc, u + 2),
-                          acc4<JT>(acc, u + 3));
-      const int c_first = owner_of(tile_g0, b.total, b.wgs);
-      const int c_last = owner_of(tile_g0 + iters - 1, b.total, b.wgs);
-      if (arrive_last(counters + b.tile_base[p] + tile, (unsigned)(c_last - c_first + 1))) {
+          for (int v0 = 0; v0 < 4; v0 += 2) {
+            f32x4 sum[2 * JT];
+            for (int c = c_first; c <= c_last; ++c) {
+              const PartBuf src =
+                  part_buf(partials, (size_t)c * 2 + (share_begin(c, b_total, b_wgs) >= tile_g0 ? 0 : 1),
+                           part_floats<JT>());
+              f32x4 val[2 * JT];
 #pragma unroll
-        for (int q = 0; q < JT / 2; ++q) {
-          // float4s 16q .. 16q + 15 of this lane, summed over the contributors in order
-          f32x4 s[16];
-          for (int c = c_first; c <= c_last; ++c) {
-            // Every contribution, this workgroup's own included, is read back
-            // from its slot: the accumulators need not stay live here.
-            f32x4 v[16];
-            const int cslot = share_begin(c, b.total, b.wgs) >= tile_g0 ? 0 : 1;
-            load16x4_strided_coherent(
-                partials + ((size_t)c * 2 + cslot) * part_floats<JT>() + lane_off + (size_t)(16 * q) * 256, v);
-            if (c == c_first) {
+              for (int v = 0; v < 2; ++v)
 #pragma unroll
-              for (int u = 0; u < 16; ++u) s[u] = v[u];
-            } else {
+                for (int j = 0; j < JT; ++j)
+                  val[v * JT + j] = load_part<POL>(src, tid * 16, ((h * 4 + v0 + v) * kBM * 8 + 256 * j) * 16);
 #pragma unroll
-              for (int u = 0; u < 16; ++u) s[u] += v[u];
+              for (int q = 0; q < 2 * JT; ++q) sum[q] = c == c_first ? val[q] : sum[q] + val[q];
             }
-          }
+            // Partial tiles at the edge of y go out through LDS and the checked loop.
 #pragma unroll
-          for (int u = 0; u < 16; ++u) write_y(16 * q + u, s[u]);
+            for (int v = 0; v < 2; ++v)
+#pragma unroll
+              for (int j = 0; j < JT; ++j) {
+                const int e = tid + 256 * j;
+                if (y_full) store_fast(h, v0 + v, j, sum[v * JT + j]);
+                else *reinterpret_cast<f32x4*>(NVFP4_XBUF(v0 + v) + swz(e >> 3, e & 7)) = sum[v * JT + j];
+              }
+          }
+          if (!y_full) write_half(h);  // each thread reads back only the chunks it wrote
+        };
+        if (local) {
+          finish_half(0, Policy<1>());
+          finish_half(1, Policy<1>());
+        } else {
+          finish_half(0, Policy<16>());
+          finish_half(1, Policy<16>());
         }
       }
     }
+    __syncthreads();  // the buffers are refilled by the next segment
     g = tile_g0 + ie;
   }
+#undef NVFP4_XBUF
+}
+
+template <int JT, bool KFULL>
+void launch_one(const PrefillBatch& b, unsigned wgs, unsigned* counters, float* partials, hipStream_t s) {
+  prefill_kernel<JT, KFULL><<<dim3(wgs), dim3(256), 0, s>>>(b, counters, partials);
 }
 
 struct Plan {
@@ -360,8 +606,11 @@ Plan prefill_plan(const Problem* p, int count, int64_t m) {
   const int64_t bm = 32 * pl.jt;
   int64_t ntiles = 0;
   for (int i = 0; i < count; ++i) ntiles += (((p[i].n + 63) / 64) + 3) / 4;
-  // One counter per output tile of a launch: cut m so that a launch's tiles fit.
-  const int64_t max_mt = ntiles > 0 ? kCounterSlots / ntiles : 1;
+  // One counter and one XCD mask per output tile of a launch: cut m so that a launch's tiles fit.
+  // (Launches hold at most 8 problems of at most kCounterSlots row tiles of
+  // 64 in all, so ntiles <= kCounterSlots / 4 and max_mt >= 2.)
+  int64_t max_mt = ntiles > 0 ? (kCounterSlots / 2) / ntiles : 1;
+  if (max_mt < 1) max_mt = 1;
   const int64_t mt = (m + bm - 1) / bm;
   pl.mrows = (mt <= max_mt ? mt : max_mt) * bm;
   return pl;
@@ -430,6 +679,7 @@ hipError_t launch_prefill_batch(const Problem* p, int count, int64_t m, bool y_b
         b.iters[j] = (int)((q[j].k + kBK - 1) / kBK);
         b.nkt[j] = (int)g.nkt;
         b.nrt[j] = (int)g.nrt;
+        b.ntn[j] = ntn;
         b.packed[j] = static_cast<const uint8_t*>(q[j].packed);
         b.x[j] = q[j].x + r0 * q[j].ldx;
         b.y[j] = static_cast<uint8_t*>(q[j].y) + (size_t)r0 * q[j].ldy * esize;
@@ -446,10 +696,18 @@ hipError_t launch_prefill_batch(const Problem* p, int count, int64_t m, bool y_b
       int64_t wgs = it / kMinShare;
       wgs = wgs < 1 ? 1 : (wgs > kPreWgs ? kPreWgs : wgs);
       b.wgs = (int)wgs;
-      switch (pl.jt) {
-        case 8: hipLaunchKernelGGL(prefill_kernel<8>, dim3((unsigned)wgs), dim3(256), 0, s, b, counters, partials); break;
-        case 4: hipLaunchKernelGGL(prefill_kernel<4>, dim3((unsigned)wgs), dim3(256), 0, s, b, counters, partials); break;
-        default: hipLaunchKernelGGL(prefill_kernel<2>, dim3((unsigned)wgs), dim3(256), 0, s, b, counters, partials); break;
+      bool kfull = true;  // every problem's k a multiple of the iteration depth
+      for (int j = 0; j < nq; ++j) kfull = kfull && (q[j].k % kBK) == 0;
+      const unsigned nwg = (unsigned)wgs;
+      if (pl.jt == 8) {
+        if (kfull) launch_one<8, true>(b, nwg, counters, partials, s);
+        else launch_one<8, false>(b, nwg, counters, partials, s);
+      } else if (pl.jt == 4) {
+        if (kfull) launch_one<4, true>(b, nwg, counters, partials, s);
+        else launch_one<4, false>(b, nwg, counters, partials, s);
+      } else {
+        if (kfull) launch_one<2, true>(b, nwg, counters, partials, s);
+        else launch_one<2, false>(b, nwg, counters, partials, s);
       }
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
