@@ -575,7 +575,49 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillBatch b, u
           }
           if (!y_full) write_half(h);  // each thread reads back only the chunks it wrote
         };
-        if (local) {
+        // Two contributions (the usual case): both slots' chunks of a batch
+        // are loaded together, halving the round trips.
+        auto finish_pair_half = [&](auto hc, auto policy) __attribute__((always_inline)) {
+          constexpr int H = decltype(hc)::value;
+          constexpr int POL = decltype(policy)::value;
+          const PartBuf s0 =
+              part_buf(partials, (size_t)c_first * 2 + (share_begin(c_first, b_total, b_wgs) >= tile_g0 ? 0 : 1),
+                       part_floats<JT>());
+          const PartBuf s1 =
+              part_buf(partials, (size_t)c_last * 2 + (share_begin(c_last, b_total, b_wgs) >= tile_g0 ? 0 : 1),
+                       part_floats<JT>());
+#pragma unroll
+          for (int v0 = 0; v0 < 4; v0 += 2) {  // two buffers' chunks at a time
+            f32x4 p0[2 * JT], p1[2 * JT];
+#pragma unroll
+            for (int v = 0; v < 2; ++v)
+#pragma unroll
+              for (int j = 0; j < JT; ++j) {
+                const int off = ((H * 4 + v0 + v) * kBM * 8 + 256 * j) * 16;
+                p0[v * JT + j] = load_part<POL>(s0, tid * 16, off);
+                p1[v * JT + j] = load_part<POL>(s1, tid * 16, off);
+              }
+#pragma unroll
+            for (int v = 0; v < 2; ++v)
+#pragma unroll
+              for (int j = 0; j < JT; ++j) {
+                const int e = tid + 256 * j;
+                const f32x4 sum = p0[v * JT + j] + p1[v * JT + j];
+                if (y_full) store_fast(H, v0 + v, j, sum);
+                else *reinterpret_cast<f32x4*>(NVFP4_XBUF(v0 + v) + swz(e >> 3, e & 7)) = sum;
+              }
+          }
+          if (!y_full) write_half(H);  // each thread reads back only the chunks it wrote
+        };
+        if (c_last - c_first == 1) {
+          if (local) {
+            finish_pair_half(Policy<0>(), Policy<1>());
+            finish_pair_half(Policy<1>(), Policy<1>());
+          } else {
+            finish_pair_half(Policy<0>(), Policy<16>());
+            finish_pair_half(Policy<1>(), Policy<16>());
+          }
+        } else if (local) {
           finish_half(0, Policy<1>());
           finish_half(1, Policy<1>());
         } else {
