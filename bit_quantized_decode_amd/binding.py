@@ -224,6 +224,26 @@ def gemv_batched(items, ws=None, stream=None):
     check(L.nvfp4_gemv_batched(arr, len(items), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
 
 
+def gemv_batched_prepared(items, ws=None, stream=None):
+    """nvfp4_gemv_batched with its arguments marshalled once: returns a
+    zero-argument callable that only makes the library call (for tight
+    launch loops)."""
+    arr = problems(items)
+    L = lib()
+    need = ctypes.c_size_t()
+    check(L.nvfp4_gemv_batched_workspace_bytes(arr, len(items), ctypes.byref(need)))
+    if ws is None and items:
+        ws = workspace(need.value, items[0][4].device)
+    fn, n, wsp, wsb, st = L.nvfp4_gemv_batched, len(items), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)
+    keep = (items, ws)  # the tensors must outlive the callable
+
+    def call():
+        check(fn(arr, n, wsp, wsb, st))
+        return keep
+
+    return call
+
+
 def gemm_batched_workspace_bytes(items, m):
     """Workspace bytes nvfp4_gemm_batched needs for these problems at m activation rows."""
     arr = problems(items)
