@@ -150,3 +150,21 @@ def test_prefill_repeat_is_bit_identical_and_counters_return_to_zero():
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
     assert int(torch.count_nonzero(ws[: 1 << 18])) == 0
+
+
+@pytest.mark.parametrize("m", [1, 7, 40, 300])
+def test_empty_k_writes_zero_outputs(m):
+    """k = 0 is an empty sum: every output is 0 (GEMV at m = 1 too)."""
+    dev = device()
+    n = 130
+    packed = torch.zeros(16, dtype=torch.uint8, device=dev)
+    x = torch.zeros((m, 8), dtype=torch.bfloat16, device=dev)
+    y = torch.full((m, n), 7.0, dtype=torch.float32, device=dev)
+    B.gemm(packed, n, 0, I.TENSOR_SCALE, x[:, :0], y=y)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(y)) == 0
+    if m == 1:
+        yv = torch.full((n,), 7.0, dtype=torch.float32, device=dev)
+        B.gemv(packed, n, 0, I.TENSOR_SCALE, x[0, :0], y=yv)
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(yv)) == 0
