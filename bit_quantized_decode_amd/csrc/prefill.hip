@@ -185,6 +185,23 @@ __device__ __forceinline__ void load_lds16(const void* src, uint8_t* dst) {
   __builtin_amdgcn_global_load_lds(const_cast<void*>(src), (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
 }
 
+// Float4 u (0 .. 8 JT - 1) of a lane's accumulators: tile t = u / 4 (half
+// t / JT, activation tile t % JT), elements 4 (u % 4) .. + 3.
+template <int JT>
+__device__ __forceinline__ f32x4 frag4(const f32x16 (&acc)[2][JT], int u) {
+  const f32x16& a = acc[(u >> 2) / JT][(u >> 2) % JT];
+  const int e = 4 * (u & 3);
+  return f32x4{a[e], a[e + 1], a[e + 2], a[e + 3]};
+}
+
+// Float4 u of a half (0 .. 4 JT - 1) into the wavefront's LDS buffer at the
+// place stage_half puts it.
+template <int JT>
+__device__ __forceinline__ void stage_frag(uint8_t* buf, int lane, int u, f32x4 v) {
+  const int jt = (u >> 2) % JT, e4 = u & 3;
+  *reinterpret_cast<f32x4*>(buf + swz(32 * jt + (lane & 31), 2 * e4 + (lane >> 5))) = v;
+}
+
 // Wavefront's half H (accumulator tiles acc[H][*]) into its LDS buffer:
 // activation row 32 jt + lane % 32 at byte 128 row, the 4 columns
 // 8 e4 + 4 (lane / 32) of the half as 16-byte chunk 2 e4 + lane / 32.
@@ -503,26 +520,16 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillBatch b, u
       __syncthreads();
       write_half(1);
     } else {
-      // Cut tile: publish this segment's sums (written through to memory),
+      // Cut tile: publish this segment's sums straight from the
+      // accumulators (written through to memory, in accumulator order: float4
+      // u of lane l of wavefront v at ((v * 8 JT + u) * 64 + l) * 16 bytes),
       // note this workgroup's XCD in the tile's mask, and let the last
       // contributor to arrive add all contributions in k order.
       const int slot = g_begin >= tile_g0 ? 0 : 1;  // this workgroup's first or last segment
       const PartBuf mine = part_buf(partials, (size_t)w * 2 + slot, part_floats<JT>());
-      auto publish_half = [&](int h) __attribute__((always_inline)) {
-#pragma unroll 4
-        for (int q = 0; q < 4 * JT; ++q) {
-          const int v = q / JT, e = tid + 256 * (q % JT);
-          store_part(mine, tid * 16, ((h * 4 + v) * kBM * 8 + 256 * (q % JT)) * 16,
-                     *reinterpret_cast<const f32x4*>(buf_of(v) + swz(e >> 3, e & 7)));
-        }
-      };
-      stage_half<0, JT>(acc, mybuf, lane);
-      __syncthreads();
-      publish_half(0);
-      __syncthreads();
-      stage_half<1, JT>(acc, mybuf, lane);
-      __syncthreads();
-      publish_half(1);
+      const int frag_off = (wave * 8 * JT * 64 + lane) * 16;
+#pragma unroll
+      for (int u = 0; u < 8 * JT; ++u) store_part(mine, frag_off, u * 1024, frag4<JT>(acc, u));
       const int gtile = pv.tile_base + tile;
       const unsigned xcc = xcc_id();
       if (threadIdx.x == 0)
@@ -538,91 +545,59 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillBatch b, u
         if (threadIdx.x == 0)
           __hip_atomic_store(counters + kMaskBase + gtile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const bool local = mask == (1u << xcc);
-        // ((p_first + p_next) + ...) in contributor (k) order, into the LDS
-        // chunks; every contribution, this workgroup's own included, is read
-        // from its slot, so the accumulators are dead once published.
-        // ((p_first + p_next) + ...) in contributor (k) order, summed in
-        // registers two buffers' chunks at a time and stored from there;
-        // every contribution, this workgroup's own included, is read from
-        // its slot, so the accumulators are dead once published.
-        auto finish_half = [&](int h, auto policy) __attribute__((always_inline)) {
-          constexpr int POL = decltype(policy)::value;
-#pragma unroll
-          for (int v0 = 0; v0 < 4; v0 += 2) {
-            f32x4 sum[2 * JT];
-            for (int c = c_first; c <= c_last; ++c) {
-              const PartBuf src =
-                  part_buf(partials, (size_t)c * 2 + (share_begin(c, b_total, b_wgs) >= tile_g0 ? 0 : 1),
-                           part_floats<JT>());
-              f32x4 val[2 * JT];
-#pragma unroll
-              for (int v = 0; v < 2; ++v)
-#pragma unroll
-                for (int j = 0; j < JT; ++j)
-                  val[v * JT + j] = load_part<POL>(src, tid * 16, ((h * 4 + v0 + v) * kBM * 8 + 256 * j) * 16);
-#pragma unroll
-              for (int q = 0; q < 2 * JT; ++q) sum[q] = c == c_first ? val[q] : sum[q] + val[q];
-            }
-            // Partial tiles at the edge of y go out through LDS and the checked loop.
-#pragma unroll
-            for (int v = 0; v < 2; ++v)
-#pragma unroll
-              for (int j = 0; j < JT; ++j) {
-                const int e = tid + 256 * j;
-                if (y_full) store_fast(h, v0 + v, j, sum[v * JT + j]);
-                else *reinterpret_cast<f32x4*>(NVFP4_XBUF(v0 + v) + swz(e >> 3, e & 7)) = sum[v * JT + j];
-              }
-          }
-          if (!y_full) write_half(h);  // each thread reads back only the chunks it wrote
+        auto slot_of = [&](int c) __attribute__((always_inline)) {
+          return part_buf(partials, (size_t)c * 2 + (share_begin(c, b_total, b_wgs) >= tile_g0 ? 0 : 1),
+                          part_floats<JT>());
         };
-        // Two contributions (the usual case): both slots' chunks of a batch
-        // are loaded together, halving the round trips.
-        auto finish_pair_half = [&](auto hc, auto policy) __attribute__((always_inline)) {
+        // Each wavefront sums its own fragments (16 float4 at a time) and
+        // stages them like its accumulators; the workgroup then writes the
+        // half out coalesced.
+        // Sums are ((p_first + p_next) + ...) in contributor (k) order; every
+        // contribution, this workgroup's own included, is read from its slot
+        // (the accumulators are dead once published), and with two
+        // contributions both slots' fragments are loaded together.
+        auto finish_half = [&](auto hc, auto policy) __attribute__((always_inline)) {
           constexpr int H = decltype(hc)::value;
           constexpr int POL = decltype(policy)::value;
-          const PartBuf s0 =
-              part_buf(partials, (size_t)c_first * 2 + (share_begin(c_first, b_total, b_wgs) >= tile_g0 ? 0 : 1),
-                       part_floats<JT>());
-          const PartBuf s1 =
-              part_buf(partials, (size_t)c_last * 2 + (share_begin(c_last, b_total, b_wgs) >= tile_g0 ? 0 : 1),
-                       part_floats<JT>());
+          __syncthreads();  // the buffers are free
+          // A half holds 4 JT float4s per lane, taken G at a time.
+          constexpr int G = 4 * JT < 16 ? 4 * JT : 16;
 #pragma unroll
-          for (int v0 = 0; v0 < 4; v0 += 2) {  // two buffers' chunks at a time
-            f32x4 p0[2 * JT], p1[2 * JT];
+          for (int q = 0; q < 4 * JT / G; ++q) {  // float4s u = 4 JT H + G q + [0, G)
+            constexpr int U0 = 4 * JT * H;
+            f32x4 sum[G];
+            if (c_last - c_first == 1) {
+              const PartBuf s0 = slot_of(c_first), s1 = slot_of(c_last);
+              f32x4 v0[G], v1[G];
 #pragma unroll
-            for (int v = 0; v < 2; ++v)
-#pragma unroll
-              for (int j = 0; j < JT; ++j) {
-                const int off = ((H * 4 + v0 + v) * kBM * 8 + 256 * j) * 16;
-                p0[v * JT + j] = load_part<POL>(s0, tid * 16, off);
-                p1[v * JT + j] = load_part<POL>(s1, tid * 16, off);
+              for (int t = 0; t < G; ++t) {
+                v0[t] = load_part<POL>(s0, frag_off, (U0 + G * q + t) * 1024);
+                v1[t] = load_part<POL>(s1, frag_off, (U0 + G * q + t) * 1024);
               }
 #pragma unroll
-            for (int v = 0; v < 2; ++v)
+              for (int t = 0; t < G; ++t) sum[t] = v0[t] + v1[t];
+            } else {
+              for (int c = c_first; c <= c_last; ++c) {
+                const PartBuf src = slot_of(c);
+                f32x4 v[G];
 #pragma unroll
-              for (int j = 0; j < JT; ++j) {
-                const int e = tid + 256 * j;
-                const f32x4 sum = p0[v * JT + j] + p1[v * JT + j];
-                if (y_full) store_fast(H, v0 + v, j, sum);
-                else *reinterpret_cast<f32x4*>(NVFP4_XBUF(v0 + v) + swz(e >> 3, e & 7)) = sum;
+                for (int t = 0; t < G; ++t) v[t] = load_part<POL>(src, frag_off, (U0 + G * q + t) * 1024);
+#pragma unroll
+                for (int t = 0; t < G; ++t) sum[t] = c == c_first ? v[t] : sum[t] + v[t];
               }
+            }
+#pragma unroll
+            for (int t = 0; t < G; ++t) stage_frag<JT>(mybuf, lane, G * q + t, sum[t]);
           }
-          if (!y_full) write_half(H);  // each thread reads back only the chunks it wrote
+          __syncthreads();
+          write_half(H);
         };
-        if (c_last - c_first == 1) {
-          if (local) {
-            finish_pair_half(Policy<0>(), Policy<1>());
-            finish_pair_half(Policy<1>(), Policy<1>());
-          } else {
-            finish_pair_half(Policy<0>(), Policy<16>());
-            finish_pair_half(Policy<1>(), Policy<16>());
-          }
-        } else if (local) {
-          finish_half(0, Policy<1>());
-          finish_half(1, Policy<1>());
+        if (local) {
+          finish_half(Policy<0>(), Policy<1>());
+          finish_half(Policy<1>(), Policy<1>());
         } else {
-          finish_half(0, Policy<16>());
-          finish_half(1, Policy<16>());
+          finish_half(Policy<0>(), Policy<16>());
+          finish_half(Policy<1>(), Policy<16>());
         }
       }
     }
