@@ -44,7 +44,7 @@ def parse():
     p.add_argument("--rows", default="decode_b1,decode_b32,moe,prefill")
     p.add_argument("--order", default="prefill,moe,decode_b32,decode_b1",
                    help="row order within a step (the batch-1 GEMV last: see the note at the plan)")
-    p.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    p.add_argument("--graphs", action="store_true", help="replay per-row HIP graphs instead of direct launches")
     return p.parse_args()
 
 
@@ -115,11 +115,16 @@ def main():
                                                    shape.inter), dev, kind="moe")
         del w
 
+    moe_calls = []
+    if "moe" in rows:
+        for cp in range(2):
+            pg_, pu_, pd_ = moe_pools[cp]
+            moe_calls.append(B.moe_grouped_prepared(moe_x, moe_logits, shape.top_k, pg_, pu_, pd_, stride_gu,
+                                                    stride_gu, stride_d, sts[0], sts[1], sts[2], shape.inter,
+                                                    y_dtype=torch.float32, ws=moe_ws, outputs=moe_out)[0])
+
     def run_moe(cp):
-        pg_, pu_, pd_ = moe_pools[cp]
-        return B.moe_grouped(moe_x, moe_logits, shape.top_k, pg_, pu_, pd_, stride_gu, stride_gu, stride_d,
-                             sts[0], sts[1], sts[2], shape.inter, y_dtype=torch.float32, ws=moe_ws,
-                             outputs=moe_out)
+        moe_calls[cp]()
 
     # ---- prefill ----------------------------------------------------------
     pre = I.PREFILL_MATRICES
@@ -139,8 +144,11 @@ def main():
     torch.cuda.synchronize()
     log(f"setup {time.time() - t_setup:.1f}s")
 
-    # ---- one step: each row's launches, captured once per weight copy as a
-    # HIP graph and replayed (the launch cost stays off the GPU timeline) ------
+    # ---- one step: each row's launches, made directly with their arguments
+    # marshalled once per weight copy (prepared library calls), so that the
+    # events around a row, on the kernels' own stream, bracket its kernels.
+    # (--graphs replays per-row HIP graphs instead; on ROCm a graph launch
+    # adds more GPU-side time than direct launches: 5-7 us per row.)
     # The layer's five products go out as one batched launch (per row).
     b1_calls = [B.gemv_batched_prepared([(packed[cp][j], m.n, m.k, I.TENSOR_SCALE, x1[j], y1[j])
                                          for j, m in enumerate(layer)], ws=ws_split)
@@ -149,22 +157,27 @@ def main():
     def row_b1(cp):
         b1_calls[cp]()
 
+    b32_calls = [B.gemm_batched_prepared([(packed[cp][j], m.n, m.k, I.TENSOR_SCALE, x32[j], y32[j])
+                                          for j, m in enumerate(layer)], ws=ws_split)
+                 for cp in range(dense_copies)] if "decode_b32" in rows else []
+
     def row_b32(cp):
-        B.gemm_batched([(packed[cp][j], m.n, m.k, I.TENSOR_SCALE, x32[j], y32[j]) for j, m in enumerate(layer)],
-                       ws=ws_split)
+        b32_calls[cp]()
 
     def pre_items(cp):
         return [(pre_packed[cp][j], mat.n, mat.k, I.TENSOR_SCALE, pre_x[j], pre_y[j]) for j, mat in enumerate(pre)]
 
+    pre_calls = []
     if "prefill" in rows:
         # The three prefill products share one stream-K launch; its workspace
         # (counters + cut-tile partial sums) is larger than the decode rows'.
         need = B.gemm_batched_workspace_bytes(pre_items(0), 512)
         if need > ws_split.numel():
             ws_split = B.workspace(need, dev)
+        pre_calls = [B.gemm_batched_prepared(pre_items(cp), ws=ws_split) for cp in range(pre_copies)]
 
     def row_pre(cp):
-        B.gemm_batched(pre_items(cp), ws=ws_split)
+        pre_calls[cp]()
 
     # Row order within a step: the compute-bound prefill first, the decode
     # rows after the memory-bound MoE.  A sustained matrix-core burst lowers
@@ -178,14 +191,14 @@ def main():
         "decode_b1": ("decode_b1", row_b1, dense_copies, lambda i: (2 * i) % dense_copies, y1),
     }
     plan = [plan_all[r] for r in args.order.split(",") if r in rows]   # (row name, callable(copy), copies, copy for step i, outputs)
-    # Eager reference outputs (copy 0), then capture.
+    # Eager reference outputs (copy 0), then (--graphs) capture.
     eager = {}
     for name, fn, ncp, _, outs in plan:
         fn(0)
         torch.cuda.synchronize()
         eager[name] = [o.clone() for o in outs] if outs is not None else [moe_out["y"].clone()]
     graphs = {}
-    if not args.eager:
+    if args.graphs:
         for name, fn, ncp, _, _ in plan:
             for cp in range(ncp):
                 g = torch.cuda.CUDAGraph()
@@ -206,29 +219,18 @@ def main():
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
-    # The batch-1 row is one kernel launch: it is launched directly (its
-    # arguments marshalled once), so that the events around it, on the
-    # kernel's own stream, bracket the kernel rather than a graph launch.
-    direct = {"decode_b1"}
-
     def step(i, timed):
         marks = {}
         for name, fn, ncp, pick, _ in plan:
-            if name in direct:
-                a = ev()
-                b = ev()
-                a.record()
-                fn(pick(args.warmup + i if timed else i))
-                b.record()
+            cp = pick(args.warmup + i if timed else i)
+            a = ev()
+            b = ev()
+            a.record()
+            if args.graphs:
+                graphs[(name, cp)].replay()
             else:
-                a = ev()
-                b = ev()
-                a.record()
-                if args.eager:
-                    fn(pick(args.warmup + i if timed else i))
-                else:
-                    graphs[(name, pick(args.warmup + i if timed else i))].replay()
-                b.record()
+                fn(cp)
+            b.record()
             marks[name] = (a, b)
         return marks
 

@@ -234,11 +234,13 @@ def gemv_batched_prepared(items, ws=None, stream=None):
     check(L.nvfp4_gemv_batched_workspace_bytes(arr, len(items), ctypes.byref(need)))
     if ws is None and items:
         ws = workspace(need.value, items[0][4].device)
-    fn, n, wsp, wsb, st = L.nvfp4_gemv_batched, len(items), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)
+    fn, n, wsp, wsb = L.nvfp4_gemv_batched, len(items), _ptr(ws), 0 if ws is None else ws.numel()
     keep = (items, ws)  # the tensors must outlive the callable
 
     def call():
-        check(fn(arr, n, wsp, wsb, st))
+        # The stream is looked up per call (None: the current one), so that a
+        # call under graph capture lands on the capturing stream.
+        check(fn(arr, n, wsp, wsb, _stream(stream)))
         return keep
 
     return call
@@ -263,6 +265,27 @@ def gemm_batched(items, ws=None, stream=None):
     if ws is None and items:
         ws = workspace(need.value, items[0][4].device)
     check(L.nvfp4_gemm_batched(arr, len(items), m, dt, _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def gemm_batched_prepared(items, ws=None, stream=None):
+    """nvfp4_gemm_batched with its arguments marshalled once: returns a
+    zero-argument callable that only makes the library call."""
+    arr = problems(items)
+    L = lib()
+    m = items[0][4].shape[0] if items else 0
+    dt = NVFP4_BF16 if items and items[0][5].dtype == torch.bfloat16 else NVFP4_F32
+    need = ctypes.c_size_t()
+    check(L.nvfp4_gemm_batched_workspace_bytes(arr, len(items), m, ctypes.byref(need)))
+    if ws is None and items:
+        ws = workspace(need.value, items[0][4].device)
+    fn, n, wsp, wsb = L.nvfp4_gemm_batched, len(items), _ptr(ws), 0 if ws is None else ws.numel()
+    keep = (items, ws)
+
+    def call():
+        check(fn(arr, n, m, dt, wsp, wsb, _stream(stream)))
+        return keep
+
+    return call
 
 
 def moe_args(**kw):
@@ -315,3 +338,34 @@ def moe_grouped(x, logits, top_k, w_gate, w_up, w_down, stride_gate, stride_up, 
     )
     check(lib().nvfp4_moe_grouped(ctypes.byref(a), _stream(stream)))
     return o
+
+
+def moe_grouped_prepared(*args, **kw):
+    """moe_grouped with its arguments marshalled once (same arguments):
+    returns (call, outputs), call() making only the library call."""
+    o = moe_grouped(*args, **kw)   # one real call builds and validates everything
+    x, logits, top_k = args[0], args[1], args[2]
+    tokens, hidden = x.shape
+    experts = logits.shape[1]
+    inter = args[12]
+    ws = kw.get("ws")
+    if ws is None:
+        ws = workspace(moe_workspace_bytes(tokens, experts, top_k, hidden, inter), x.device, kind="moe")
+    a = moe_args(
+        tokens=tokens, experts=experts, top_k=top_k, hidden=hidden, inter=inter, x=x, router_logits=logits,
+        w_gate=args[3], w_up=args[4], w_down=args[5], stride_gate=args[6], stride_up=args[7],
+        stride_down=args[8], scale_gate=args[9], scale_up=args[10], scale_down=args[11],
+        y=o["y"], y_dtype=NVFP4_BF16 if o["y"].dtype == torch.bfloat16 else NVFP4_F32,
+        topk_ids=o["topk_ids"], topk_weights=o["topk_weights"], expert_counts=o["expert_counts"],
+        expert_offsets=o["expert_offsets"], perm=o["perm"],
+        dbg_gate=o.get("dbg_gate"), dbg_up=o.get("dbg_up"), dbg_h=o.get("dbg_h"), dbg_down=o.get("dbg_down"),
+        workspace=ws, workspace_bytes=ws.numel(),
+    )
+    fn, ref, stream = lib().nvfp4_moe_grouped, ctypes.byref(a), kw.get("stream")
+    keep = (args, kw, o, ws, a)
+
+    def call():
+        check(fn(ref, _stream(stream)))
+        return keep
+
+    return call, o

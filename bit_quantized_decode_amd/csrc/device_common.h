@@ -80,6 +80,34 @@ __device__ __forceinline__ uint16_t to_bf16(float v) {
   return __builtin_bit_cast(uint16_t, a);
 }
 
+// One 16-byte-per-lane load from memory straight into LDS: lane l's 16
+// bytes land at dst + 16 l (dst is the same for the whole wavefront).  Kept
+// out of lambdas: a lambda body is also compiled for the host, where this
+// builtin does not exist.  Its completion is counted by vmcnt like any load.
+__device__ __forceinline__ void load_lds16(const void* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(const_cast<void*>(src), (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
+// vmcnt-only wait (gfx9 s_waitcnt encoding; expcnt and lgkmcnt left free).
+// Vector memory operations of a wavefront complete in issue order, so
+// vmcnt <= N means that all but the N most recently issued have completed.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// vmcnt <= N and lgkmcnt == 0.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+// Workgroup barrier that adds no waits of its own: loads into LDS that the
+// other wavefronts read after it are waited for explicitly (wait_vmcnt) first.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
 // Exchange between the wavefront halves: afterwards lanes 32..63 of `hi_dst`
 // hold what lanes 0..31 of `lo_src` held, and lanes 0..31 of `lo_src` hold what
 // lanes 32..63 of `hi_dst` held; the other lanes keep their values.

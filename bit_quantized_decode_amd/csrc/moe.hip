@@ -155,13 +155,17 @@ __global__ __launch_bounds__(1024) void group_kernel(const int32_t* __restrict__
 // tiles 2j, 2j+1 and waves 2/3 the same up row tiles, all over the whole
 // hidden dimension with one shared activation tile per k tile; the up results
 // go through LDS to the gate waves, which form h = bf16(silu(G) * U).
-__global__ __launch_bounds__(256) void gate_up_kernel(
+template <bool KFULL>
+__global__ __launch_bounds__(256, 1) void gate_up_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ active, const int32_t* __restrict__ n_active, int top_k, int hidden, int inter,
     const uint8_t* __restrict__ w_gate, const uint8_t* __restrict__ w_up, size_t stride_gate, size_t stride_up,
     const float* __restrict__ scale_gate, const float* __restrict__ scale_up, uint16_t* __restrict__ h,
     float* __restrict__ dbg_gate, float* __restrict__ dbg_up) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds_x[2 * kXTileElems];
+  __shared__ __attribute__((aligned(16))) uint8_t xb0[kXTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t xb1[kXTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t xb2[kXTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t xb3[kXTileBytes];
   __shared__ float lds_u[2][32][65];
   const int nrt = (inter + 63) / 64;
   const int npairs = (nrt + 1) / 2;
@@ -175,16 +179,22 @@ __global__ __launch_bounds__(256) void gate_up_kernel(
   const int lane = threadIdx.x & 63;
   const bool is_up = wave >= 2;
   const int rt = 2 * pair + (wave & 1);
-  const uint8_t* wtile = nullptr;
-  if (rt < nrt)
-    wtile = (is_up ? w_up + e * stride_up : w_gate + e * stride_gate) + (size_t)rt * nkt * kTileBytes;
+  // A wavefront past the last row tile streams the last one (not stored).
+  const uint8_t* wrow = (is_up ? w_up + e * stride_up : w_gate + e * stride_gate) +
+                        (size_t)(rt < nrt ? rt : nrt - 1) * nkt * kTileBytes;
   const float sg = scale_gate[e], su = scale_up[e];
   const int tok = lane & 31;
   for (int c0 = p0; c0 < p1; c0 += 32) {
-    const int ps = c0 + (threadIdx.x >> 3);
-    const uint16_t* xrow = ps < p1 ? x + (int64_t)(perm[ps] / top_k) * hidden : nullptr;
+    // Activation rows of this chunk, gathered through perm; rows past the
+    // expert's last repeat it (their outputs are not stored).
+    const uint16_t* rowp[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ps = c0 + stage_row(wave, j, lane);
+      rowp[j] = x + (int64_t)(perm[ps < p1 ? ps : p1 - 1] / top_k) * hidden;
+    }
     f32x16 acc_a = {}, acc_b = {};
-    wg_skinny(wtile, 0, nkt, hidden, xrow, lds_x, lane, acc_a, acc_b);
+    skinny_stream<4, KFULL>(wrow, 0, nkt, hidden, rowp, xb0, xb1, xb2, xb3, wave, lane, acc_a, acc_b);
     if (is_up) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -218,12 +228,17 @@ __global__ __launch_bounds__(256) void gate_up_kernel(
 
 // a7: per workgroup (active expert a, row quad j): four down row tiles over the
 // expert width, activation rows = the expert's rows of h.
-__global__ __launch_bounds__(256) void down_kernel(const uint16_t* __restrict__ h, const int32_t* __restrict__ offsets,
-                                                   const int32_t* __restrict__ active,
-                                                   const int32_t* __restrict__ n_active, int hidden, int inter,
-                                                   const uint8_t* __restrict__ w_down, size_t stride_down,
-                                                   const float* __restrict__ scale_down, float* __restrict__ d) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds_x[2 * kXTileElems];
+template <bool KFULL>
+__global__ __launch_bounds__(256, 1) void down_kernel(const uint16_t* __restrict__ h,
+                                                      const int32_t* __restrict__ offsets,
+                                                      const int32_t* __restrict__ active,
+                                                      const int32_t* __restrict__ n_active, int hidden, int inter,
+                                                      const uint8_t* __restrict__ w_down, size_t stride_down,
+                                                      const float* __restrict__ scale_down, float* __restrict__ d) {
+  __shared__ __attribute__((aligned(16))) uint8_t xb0[kXTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t xb1[kXTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t xb2[kXTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t xb3[kXTileBytes];
   const int nrt = (hidden + 63) / 64;
   const int nquads = (nrt + 3) / 4;
   const int a = blockIdx.x / nquads;
@@ -235,14 +250,18 @@ __global__ __launch_bounds__(256) void down_kernel(const uint16_t* __restrict__ 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int rt = 4 * quad + wave;
-  const uint8_t* wtile = rt < nrt ? w_down + e * stride_down + (size_t)rt * nkt * kTileBytes : nullptr;
+  const uint8_t* wrow = w_down + e * stride_down + (size_t)(rt < nrt ? rt : nrt - 1) * nkt * kTileBytes;
   const float sd = scale_down[e];
   const int tok = lane & 31;
   for (int c0 = p0; c0 < p1; c0 += 32) {
-    const int ps = c0 + (threadIdx.x >> 3);
-    const uint16_t* xrow = ps < p1 ? h + (int64_t)ps * inter : nullptr;
+    const uint16_t* rowp[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ps = c0 + stage_row(wave, j, lane);
+      rowp[j] = h + (int64_t)(ps < p1 ? ps : p1 - 1) * inter;
+    }
     f32x16 acc_a = {}, acc_b = {};
-    wg_skinny(wtile, 0, nkt, inter, xrow, lds_x, lane, acc_a, acc_b);
+    skinny_stream<4, KFULL>(wrow, 0, nkt, inter, rowp, xb0, xb1, xb2, xb3, wave, lane, acc_a, acc_b);
     const int p = c0 + tok;
     if (rt < nrt && p < p1) {
       float* drow = d + (int64_t)p * hidden;
@@ -336,15 +355,28 @@ hipError_t launch_moe(const MoeLaunch& a, hipStream_t s) {
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const int64_t max_active = a.experts < flat ? a.experts : flat;
   const int64_t pairs_i = ((a.inter + 63) / 64 + 1) / 2;
-  hipLaunchKernelGGL(gate_up_kernel, dim3((unsigned)(max_active * pairs_i)), dim3(256), 0, s, a.x, a.perm, a.offsets,
-                     w.active, w.n_active, (int)a.top_k, (int)a.hidden, (int)a.inter, a.w_gate, a.w_up,
-                     a.stride_gate, a.stride_up, a.scale_gate, a.scale_up, w.h, a.dbg_gate, a.dbg_up);
+  const dim3 gu_grid((unsigned)(max_active * pairs_i));
+  if (a.hidden % kTileK == 0)
+    gate_up_kernel<true><<<gu_grid, dim3(256), 0, s>>>(a.x, a.perm, a.offsets, w.active, w.n_active, (int)a.top_k,
+                                                       (int)a.hidden, (int)a.inter, a.w_gate, a.w_up, a.stride_gate,
+                                                       a.stride_up, a.scale_gate, a.scale_up, w.h, a.dbg_gate,
+                                                       a.dbg_up);
+  else
+    gate_up_kernel<false><<<gu_grid, dim3(256), 0, s>>>(a.x, a.perm, a.offsets, w.active, w.n_active, (int)a.top_k,
+                                                        (int)a.hidden, (int)a.inter, a.w_gate, a.w_up, a.stride_gate,
+                                                        a.stride_up, a.scale_gate, a.scale_up, w.h, a.dbg_gate,
+                                                        a.dbg_up);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const int64_t nrt_h = (a.hidden + 63) / 64;
   const int64_t wgs_h = (nrt_h + 3) / 4;
   float* d = a.dbg_down ? a.dbg_down : w.d;
-  hipLaunchKernelGGL(down_kernel, dim3((unsigned)(max_active * wgs_h)), dim3(256), 0, s, w.h, a.offsets, w.active,
-                     w.n_active, (int)a.hidden, (int)a.inter, a.w_down, a.stride_down, a.scale_down, d);
+  const dim3 dn_grid((unsigned)(max_active * wgs_h));
+  if (a.inter % kTileK == 0)
+    down_kernel<true><<<dn_grid, dim3(256), 0, s>>>(w.h, a.offsets, w.active, w.n_active, (int)a.hidden,
+                                                    (int)a.inter, a.w_down, a.stride_down, a.scale_down, d);
+  else
+    down_kernel<false><<<dn_grid, dim3(256), 0, s>>>(w.h, a.offsets, w.active, w.n_active, (int)a.hidden,
+                                                     (int)a.inter, a.w_down, a.stride_down, a.scale_down, d);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const int64_t outs = a.tokens * a.hidden;
   hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, s, d, a.g, w.pos, a.tokens,

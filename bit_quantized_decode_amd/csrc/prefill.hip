@@ -177,14 +177,6 @@ __device__ __forceinline__ void interleave_ks() {
 }
 
 
-// One 16-byte-per-lane load from memory straight into LDS: lane l's 16
-// bytes land at dst + 16 l (dst is the same for the whole wavefront).  Kept
-// out of lambdas: a lambda body is also compiled for the host, where this
-// builtin does not exist.
-__device__ __forceinline__ void load_lds16(const void* src, uint8_t* dst) {
-  __builtin_amdgcn_global_load_lds(const_cast<void*>(src), (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-}
-
 // Float4 u (0 .. 8 JT - 1) of a lane's accumulators: tile t = u / 4 (half
 // t / JT, activation tile t % JT), elements 4 (u % 4) .. + 3.
 template <int JT>
@@ -217,23 +209,6 @@ __device__ __forceinline__ void stage_half(const f32x16 (&acc)[2][JT], uint8_t* 
     }
 }
 
-// vmcnt-only wait (gfx9 s_waitcnt encoding; expcnt and lgkmcnt left free).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// vmcnt <= N and lgkmcnt == 0.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_lgkm0() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
-}
-
-// Workgroup barrier that adds no waits of its own: the loads into LDS that
-// the next iteration reads are waited for explicitly (wait_vmcnt) before it.
-__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
 template <int JT, bool KFULL>
 __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillBatch b, unsigned* __restrict__ counters,

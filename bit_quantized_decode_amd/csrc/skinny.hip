@@ -72,10 +72,13 @@ struct SkinnyBatch {
   int64_t partial_base[kMaxBatch];  // floats
 };
 
-__global__ __launch_bounds__(256) void skinny_kernel(const SkinnyBatch b, int64_t m, int y_bf16,
-                                                     unsigned* __restrict__ counters,
-                                                     float* __restrict__ partial_all) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds_x[2 * kXTileElems];
+template <bool KFULL>
+__global__ __launch_bounds__(256, 2) void skinny_kernel(const SkinnyBatch b, int64_t m, int y_bf16,
+                                                        unsigned* __restrict__ counters,
+                                                        float* __restrict__ partial_all) {
+  __shared__ __attribute__((aligned(16))) uint8_t xb0[kXTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t xb1[kXTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t xb2[kXTileBytes];
   int p = 0;
   while (p + 1 < b.count && (int)blockIdx.x >= b.wg_begin[p + 1]) ++p;
   const int groups = b.groups[p], nkt = b.nkt[p], nrt = b.nrt[p];
@@ -89,11 +92,17 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyBatch b, int64_
   const int lane = threadIdx.x & 63;
   const int rt = rg * kWaves + wave;
   const int kt0 = part_begin(grp, nkt, groups), kt1 = part_begin(grp + 1, nkt, groups);
-  const int stage_row = threadIdx.x >> 3;
-  const uint16_t* xrow = stage_row < m ? b.x[p] + stage_row * ldx : nullptr;
+  // Activation rows past m repeat row m - 1; a wavefront past the last row
+  // tile streams the last one (neither result is stored).
+  const uint16_t* rowp[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = stage_row(wave, j, lane);
+    rowp[j] = b.x[p] + (int64_t)(r < m ? r : m - 1) * ldx;
+  }
+  const uint8_t* wrow = b.packed[p] + (size_t)(rt < nrt ? rt : nrt - 1) * nkt * kTileBytes;
   f32x16 acc_a = {}, acc_b = {};
-  wg_skinny(rt < nrt ? b.packed[p] + (size_t)rt * nkt * kTileBytes : nullptr, kt0, kt1, k, xrow, lds_x, lane,
-            acc_a, acc_b);
+  skinny_stream<3, KFULL>(wrow, kt0, kt1 - kt0, k, rowp, xb0, xb1, xb2, xb2, wave, lane, acc_a, acc_b);
 
   const int tok = lane & 31;
   const bool vec = (ldy & 3) == 0;
@@ -279,7 +288,12 @@ hipError_t launch_skinny_batch(const Problem* p, int count, int64_t m, bool y_bf
     b.wg_begin[b.count] = wgs;
     unsigned* cnt_ptr = static_cast<unsigned*>(ws);
     float* partial = ws ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kCounterBytes) : nullptr;
-    hipLaunchKernelGGL(skinny_kernel, dim3((unsigned)wgs), dim3(256), 0, s, b, m, y_bf16 ? 1 : 0, cnt_ptr, partial);
+    bool kfull = true;
+    for (int j = 0; j < b.count; ++j) kfull = kfull && (b.k[j] % kTileK) == 0;
+    if (kfull)
+      skinny_kernel<true><<<dim3((unsigned)wgs), dim3(256), 0, s>>>(b, m, y_bf16 ? 1 : 0, cnt_ptr, partial);
+    else
+      skinny_kernel<false><<<dim3((unsigned)wgs), dim3(256), 0, s>>>(b, m, y_bf16 ? 1 : 0, cnt_ptr, partial);
   }
   return hipGetLastError();
 }

@@ -5,11 +5,9 @@
 // activation rows, on the bf16 matrix cores.
 //
 // Data flow per 256-k tile:
-//  - the activation tile (32 rows x 256 k, 16 KB) is loaded once per
-//    workgroup into LDS (double-buffered, one barrier per tile), so every
-//    wavefront reads it from LDS instead of from memory;
-//  - each wavefront keeps the next weight tile's nine 16-byte loads in flight
-//    while it multiplies the current one;
+//  - the activation tile (32 rows x 256 k, 16 KB) goes from memory straight
+//    into LDS (one 16-byte load per lane per 1 KB), once per workgroup, so
+//    every wavefront reads it from LDS;
 //  - one 1 KB wavefront load of a tile chunk (64 rows x 32 k) is already the
 //    A operands of four v_mfma_f32_32x32x16_bf16 (rows 0-31 and 32-63, two k
 //    steps of 16): lane l holds 8 consecutive k of rows l%32 and 32 + l%32
@@ -25,9 +23,6 @@
 #include "device_common.h"
 
 namespace nvfp4 {
-
-constexpr int kXStride = kTileK + 8;  // bf16 per LDS activation row (16-byte pad: conflict-free reads)
-constexpr int kXTileElems = 32 * kXStride;
 
 // Eight weights of one k step: code word `w` (8 nibbles, k ascending) times
 // scale `s`, as bf16.  Each product has at most 6 significant bits, so the
@@ -66,95 +61,167 @@ __device__ __forceinline__ void chunk_mfma(u32x4 q, u32x4 sa, u32x4 sb, bf16x8 x
   tb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dequant8(q[3], e4m3<(2 * C + 1) % 4>(sb[C / 2])), xb, tb, 0, 0, 0);
 }
 
-// Multiply the resident weight tile `w` by the activation tile in LDS (`xt`,
-// 32 rows of kXStride bf16) into acc_a / acc_b.  As soon as chunk C's codes
-// have been consumed, the registers take the load of chunk C of the tile at
-// `next` (two tiles ahead), and after the last chunk the scale bytes follow:
-// the weight stream stays two tiles deep with only two register sets.
-__device__ __forceinline__ void tile_mfma_prefetch(WTile& w, const uint16_t* xt, int lane, const uint8_t* next,
-                                                   f32x16& acc_a, f32x16& acc_b) {
-  const uint16_t* xl = xt + (lane & 31) * kXStride + 8 * (lane >> 5);
-  f32x16 ta = {}, tb = {};
-#define NVFP4_CHUNK(C)                                                                                         \
-  chunk_mfma<C>(w.q[C], w.sa, w.sb, __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xl + 32 * C)), \
-                __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xl + 32 * C + 16)), ta, tb);        \
-  if (next) w.q[C] = load16(next + C * 1024 + lane * 16);
-  NVFP4_CHUNK(0) NVFP4_CHUNK(1) NVFP4_CHUNK(2) NVFP4_CHUNK(3)
-  NVFP4_CHUNK(4) NVFP4_CHUNK(5) NVFP4_CHUNK(6) NVFP4_CHUNK(7)
-#undef NVFP4_CHUNK
-  if (next) {
-    w.sa = load16(next + kScaleOffset + 32 * (lane & 31));
-    w.sb = load16(next + kScaleOffset + 32 * (lane & 31) + 16);
-  }
-  acc_a += ta;
-  acc_b += tb;
+// ---- activation tiles in LDS --------------------------------------------
+// One tile is 16 KB: activation row r (of 32) at byte 512 r, its 16-byte
+// chunk c (k 8c .. 8c+7 of the 256-k tile) at physical chunk c ^ (r % 16).
+// Rows are contiguous, as the LDS loads write them, and the B-operand reads
+// (rows 0-15 at one logical chunk) land in sixteen distinct bank groups.
+constexpr int kXTileBytes = 32 * 512;
+
+// B operands of chunk C (k 32C .. 32C+31) for this lane: row r = lane % 32,
+// logical chunks 4C + lane/32 (xa) and 4C + 2 + lane/32 (xb).  With
+// c = 4C + j (j < 4) the physical chunk is 4 (C ^ (r%16)/4) + (j ^ r%4):
+// `abase_a` / `abase_b` hold 512 r + 16 (j ^ r%4) for the two j, `sw` holds
+// 64 ((r%16)/4).
+template <int C>
+__device__ __forceinline__ void load_bops(const uint8_t* buf, uint32_t abase_a, uint32_t abase_b, uint32_t sw,
+                                          bf16x8& xa, bf16x8& xb) {
+  const uint32_t cofs = (uint32_t)(64 * C) ^ sw;
+  xa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(buf + cofs + abase_a));
+  xb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(buf + cofs + abase_b));
 }
 
-// Activation staging: thread t (of 256) moves row t/8, k segment (t%8)*32 .. +32
-// of a 256-k tile: four 16-byte loads, zero for absent rows and k >= K.
-struct XStage {
-  u32x4 v[4];
-};
+// Staging assignment: LDS load j (0..3) of wavefront w fills activation rows
+// 8w + 2j (lanes 0-31) and 8w + 2j + 1 (lanes 32-63) of a tile; lane l
+// fetches the logical chunk stored at physical chunk l % 32 of its row.
+__device__ __forceinline__ int stage_row(int wave, int j, int lane) { return 8 * wave + 2 * j + (lane >> 5); }
 
-__device__ __forceinline__ void load_xstage(const uint16_t* xrow, int64_t kb, int64_t k, XStage& s) {
-  const int seg = (threadIdx.x & 7) * 32;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t kk = kb + seg + 8 * i;
-    s.v[i] = (xrow != nullptr && kk < k) ? load16(xrow + kk) : u32x4{0u, 0u, 0u, 0u};
-  }
+// Sixteen zero bytes: the source of activation chunks past K.
+static __device__ u32x4 g_zero_chunk;
+
+template <int I>
+__device__ __forceinline__ uint8_t* pick_buf(uint8_t* b0, uint8_t* b1, uint8_t* b2, uint8_t* b3) {
+  return I == 0 ? b0 : I == 1 ? b1 : I == 2 ? b2 : b3;
 }
 
-__device__ __forceinline__ void store_xstage(uint16_t* xt, const XStage& s) {
-  u32x4* dst = reinterpret_cast<u32x4*>(xt + (threadIdx.x >> 3) * kXStride + (threadIdx.x & 7) * 32);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) dst[i] = s.v[i];
-}
-
-// Workgroup-cooperative skinny product (all 256 threads must call it).
-//   wtile : this wavefront's 64-row tile (its k tile 0), or nullptr if idle
-//   xrow  : this thread's staging row (row threadIdx.x/8 of the 32), nullptr = zeros
-//   lds_x : 2 * kXTileElems bf16 of LDS
+// Workgroup-cooperative skinny product (all 256 threads call it, with the
+// same kt0 / ntile).
+//   wrow   : this wavefront's 64-row tile at k tile 0 (tile t at wrow + t * 9216)
+//   kt0, ntile : k tiles [kt0, kt0 + ntile), ntile >= 1
+//   k      : the product's K (activations past K load as zeros when !KFULL)
+//   rowp   : for LDS load j, the activation row stage_row(wave, j, lane)
+//            (rows past the real ones may repeat any real row: their
+//            outputs are not used)
+//   xb0..  : D distinct LDS arrays of kXTileBytes (distinct objects, so that
+//            reads of one are not ordered after loads into another)
 // acc_a / acc_b receive the tile rows 0-31 / 32-63 (see acc_row) for the 32
-// activation rows (lane%32), summed over k tiles [kt0, kt1).
+// activation rows (lane%32), summed over the k tiles.
 //
-// Pipeline: two weight register sets (wa, wb) hold tiles t and t+1 while
-// tile t+2 streams into wa chunk by chunk as tile t is consumed; two LDS
-// buffers hold the activations of tiles t and t+1, and the activations of
-// t+2 wait in registers.  Every stage issues its activation loads before its
-// weight loads, so storing activations to LDS never waits for weights.
-// Prefetches past the range re-read the range's last tile (harmless, and it
-// keeps the unrolled code free of branches).
-__device__ __forceinline__ void wg_skinny(const uint8_t* wtile, int kt0, int kt1, int64_t k, const uint16_t* xrow,
-                                          uint16_t* lds_x, int lane, f32x16& acc_a, f32x16& acc_b) {
-  if (kt0 >= kt1) return;
-  const int last = kt1 - 1;
-  auto wptr = [&](int kt) -> const uint8_t* {
-    return wtile ? wtile + (size_t)(kt < last ? kt : last) * kTileBytes : nullptr;
+// Pipeline (D = 3 or 4 steps deep, one step per k tile): the weights of tile
+// i + D stream into the registers of tile i chunk by chunk as tile i is
+// consumed (D register sets); the activations of tile i + D - 1 load into
+// the LDS buffer that tile i - 1 used.  Per step a wavefront issues 4
+// activation loads and then 10 weight loads, and memory operations complete
+// in issue order: before the barrier that ends step i it waits for its loads
+// of activation tile i + 1, which leaves the 10 + 14 (D - 2) operations
+// issued after them in flight -- the weights of the next D - 1 tiles are not
+// waited for.  Loads past the range re-read its last tile, so every step
+// issues the same operations and the counts hold.
+template <int D, bool KFULL>
+__device__ __forceinline__ void skinny_stream(const uint8_t* wrow, int kt0, int ntile, int64_t k,
+                                              const uint16_t* const (&rowp)[4], uint8_t* xb0, uint8_t* xb1,
+                                              uint8_t* xb2, uint8_t* xb3, int wave, int lane, f32x16& acc_a,
+                                              f32x16& acc_b) {
+  static_assert(D == 3 || D == 4, "pipeline depth");
+  constexpr int kAfterX = 10 + 14 * (D - 2);
+  int cofs[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) cofs[j] = 8 * ((lane & 31) ^ (stage_row(wave, j, lane) & 15));
+  const int last = ntile - 1;
+  auto tile_of = [&](int i) __attribute__((always_inline)) { return kt0 + (i < last ? i : last); };
+  // K <= 2^30 (checked by the callers' argument validation): 32-bit k offsets.
+  // Chunks at k >= K (a ragged last tile) are loaded from a zero block.
+  const int k32 = (int)k;
+  auto load_x = [&](int i, uint8_t* buf) __attribute__((always_inline)) {
+    const int kb = tile_of(i) * kTileK;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint16_t* src = rowp[j] + kb + cofs[j];
+      if (!KFULL && kb + cofs[j] >= k32) src = reinterpret_cast<const uint16_t*>(&g_zero_chunk);
+      load_lds16(src, buf + 512 * (8 * wave + 2 * j));
+    }
   };
-  auto xk = [&](int kt) -> int64_t { return (int64_t)(kt < last ? kt : last) * kTileK; };
-  uint16_t* lds0 = lds_x;
-  uint16_t* lds1 = lds_x + kXTileElems;
-  XStage xs;
-  WTile wa, wb;
-  load_xstage(xrow, xk(kt0), k, xs);
-  if (wtile) load_wtile(wptr(kt0), lane, wa);
-  store_xstage(lds0, xs);
-  load_xstage(xrow, xk(kt0 + 1), k, xs);
-  if (wtile) load_wtile(wptr(kt0 + 1), lane, wb);
-  for (int kt = kt0; kt < kt1; kt += 2) {
-    __syncthreads();  // lds0 holds tile kt
-    if (wtile) tile_mfma_prefetch(wa, lds0, lane, kt + 2 < kt1 ? wptr(kt + 2) : nullptr, acc_a, acc_b);
-    if (kt + 1 >= kt1) break;
-    store_xstage(lds1, xs);  // tile kt+1; lds1 was last read before the barrier above
-    load_xstage(xrow, xk(kt + 2), k, xs);
-    __syncthreads();  // lds1 holds tile kt+1
-    if (wtile) tile_mfma_prefetch(wb, lds1, lane, kt + 3 < kt1 ? wptr(kt + 3) : nullptr, acc_a, acc_b);
-    if (kt + 2 >= kt1) break;
-    store_xstage(lds0, xs);  // tile kt+2; lds0 was last read before the barrier above
-    load_xstage(xrow, xk(kt + 3), k, xs);
+  const uint32_t lane_code = lane * 16, lane_scale = kScaleOffset + 32 * (lane & 31);
+  auto load_w = [&](int i, WTile& w) __attribute__((always_inline)) {
+    const uint8_t* t = wrow + (size_t)tile_of(i) * kTileBytes;
+    w.sa = load16(t + lane_scale);
+    w.sb = load16(t + lane_scale + 16);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) w.q[c] = load16(t + c * 1024 + lane_code);
+  };
+  const int br = lane & 31, bh = lane >> 5;
+  const uint32_t abase_a = 512 * br + 16 * (bh ^ (br & 3));
+  const uint32_t abase_b = 512 * br + 16 * ((2 + bh) ^ (br & 3));
+  const uint32_t sw0 = 64 * ((br & 15) >> 2);
+  auto compute = [&](WTile& w, const uint8_t* buf, int inext) __attribute__((always_inline)) {
+    const uint8_t* t = wrow + (size_t)tile_of(inext) * kTileBytes;
+    uint32_t sw = sw0;
+    asm volatile("" : "+v"(sw));  // formed per tile: keeps the 16 chunk addresses out of registers
+    f32x16 ta = {}, tb = {};
+    bf16x8 xa, xb;
+#define NVFP4_SK_CHUNK(C)                                 \
+  load_bops<C>(buf, abase_a, abase_b, sw, xa, xb);        \
+  chunk_mfma<C>(w.q[C], w.sa, w.sb, xa, xb, ta, tb);      \
+  w.q[C] = load16(t + C * 1024 + lane_code);
+    NVFP4_SK_CHUNK(0) NVFP4_SK_CHUNK(1) NVFP4_SK_CHUNK(2) NVFP4_SK_CHUNK(3)
+    NVFP4_SK_CHUNK(4) NVFP4_SK_CHUNK(5) NVFP4_SK_CHUNK(6) NVFP4_SK_CHUNK(7)
+#undef NVFP4_SK_CHUNK
+    w.sa = load16(t + lane_scale);
+    w.sb = load16(t + lane_scale + 16);
+    acc_a += ta;
+    acc_b += tb;
+  };
+  // Prologue in steady-state order: W(0), then x(j), W(j + 1) for j < D - 1.
+  WTile w0, w1, w2, w3;
+  load_w(0, w0);
+  load_x(0, xb0);
+  load_w(1, w1);
+  load_x(1, xb1);
+  load_w(2, w2);
+  if (D == 4) {
+    load_x(2, xb2);
+    load_w(3, w3);
   }
-  __syncthreads();  // the LDS buffers may be reused by the caller
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt_lgkm0<kAfterX>();
+  barrier_only();
+  __builtin_amdgcn_sched_barrier(0);
+#define NVFP4_SK_STEP(S, W)                                                 \
+  {                                                                         \
+    const int i = i0 + (S);                                                 \
+    load_x(i + D - 1, pick_buf<((S) + D - 1) % D>(xb0, xb1, xb2, xb3));     \
+    __builtin_amdgcn_sched_barrier(0);                                      \
+    compute(W, pick_buf<(S)>(xb0, xb1, xb2, xb3), i + D);                   \
+    __builtin_amdgcn_sched_barrier(0);                                      \
+    wait_vmcnt_lgkm0<kAfterX>();                                            \
+    barrier_only();                                                         \
+    __builtin_amdgcn_sched_barrier(0);                                      \
+  }
+  int i0 = 0;
+  if (D == 3) {
+    for (; i0 + 3 <= ntile; i0 += 3) {
+      NVFP4_SK_STEP(0, w0)
+      NVFP4_SK_STEP(1, w1)
+      NVFP4_SK_STEP(2, w2)
+    }
+    if (i0 < ntile) NVFP4_SK_STEP(0, w0)
+    if (i0 + 1 < ntile) NVFP4_SK_STEP(1, w1)
+  } else {
+    for (; i0 + 4 <= ntile; i0 += 4) {
+      NVFP4_SK_STEP(0, w0)
+      NVFP4_SK_STEP(1, w1)
+      NVFP4_SK_STEP(2, w2)
+      NVFP4_SK_STEP(3, w3)
+    }
+    if (i0 < ntile) NVFP4_SK_STEP(0, w0)
+    if (i0 + 1 < ntile) NVFP4_SK_STEP(1, w1)
+    if (i0 + 2 < ntile) NVFP4_SK_STEP(2, w2)
+  }
+#undef NVFP4_SK_STEP
+  // Loads past the range still target LDS and registers; the caller may
+  // reuse the buffers once every wavefront is past this point.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 }
 
 // Row (within the 64-row tile) of accumulator element i held by `lane`.
