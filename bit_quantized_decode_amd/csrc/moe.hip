@@ -2,21 +2,23 @@
 //
 // Each token is routed to `top_k` of `experts` experts and only the routed
 // experts' weights are read (CHImp-Alpha-v1.0 model card, "How it fits on one
-// GPU": 10 of 512 experts per token).  Five launches on the caller's stream:
+// GPU": 10 of 512 experts per token).  Launches on the caller's stream:
 //   1. route    one wavefront per token: top_k rounds of a wavefront-wide
-//               (logit desc, id asc) argmax, then the softmax over the
+//               (logit desc, id asc) maximum, then the softmax over the
 //               selected logits (fp32);
 //   2. group    one workgroup: expert histogram, exclusive scan, the stable
 //               counting sort of the flat (t*top_k + j) indices by expert, and
-//               the ascending list of active experts -- integer only, so
+//               the work list of the expert GEMMs: each active expert's rows
+//               in chunks of 32 with their token indices -- integer only, so
 //               bit-exact and independent of scheduling;
-//   3. gate/up  per (active expert, pair of 64-row tiles): the skinny core on
-//               the expert's gate and up tiles, activation rows gathered
-//               through perm, then h = bf16(silu(s_g Wg x) * (s_u Wu x));
-//   4. down     per (active expert, four 64-row tiles): d = s_d Wd h (fp32);
+//   3. gate/up  per (chunk, 64-row tile): the expert's gate and up tiles over
+//               k slots, activation rows gathered by the chunk's token list,
+//               then h = bf16(silu(s_g Wg x) * (s_u Wu x));
+//   4. down     per (chunk, four 64-row tiles): d = s_d Wd h (fp32);
 //   5. scatter  y[t] = sum_j g[t][j] * d[pos(t, j)], j ascending.
-// Launch grids cover the worst case (min(experts, tokens*top_k) active
-// experts); workgroups past the active count return at once.
+// Launch grids cover the work list's worst-case length; workgroups past its
+// actual length return at once.  A chunk's record holds everything a GEMM
+// workgroup needs, so its weight loads wait on one load only.
 #include "device_common.h"
 #include "launchers.h"
 #include "skinny_core.h"
@@ -26,91 +28,174 @@ namespace {
 
 constexpr int kMaxExperts = 2048;
 constexpr int kMaxTopK = 64;
+constexpr int kChunkRows = 32;               // activation rows per expert-GEMM workgroup
+constexpr int kChunkInts = 4 + kChunkRows;   // one work-list record
 
-__device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
-  if (ai < 0) return false;
-  if (bi < 0) return true;
-  return av > bv || (av == bv && ai < bi);
+// Routing key of one logit: larger logit first, then the smaller expert id
+// (-0 counts as +0); unsigned 64-bit order = (logit desc, id asc).
+__device__ __forceinline__ uint64_t route_key(float v, int id) {
+  uint32_t b = v == 0.0f ? 0u : __float_as_uint(v);
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)b << 32) | (uint32_t)~id;
+}
+__device__ __forceinline__ float key_logit(uint64_t k) {
+  const uint32_t b = (uint32_t)(k >> 32);
+  return __uint_as_float((b & 0x80000000u) ? (b & 0x7fffffffu) : ~b);
 }
 
+// Wavefront-wide maximum of a 32-bit value, in every lane: shifts within
+// each row of 16 leave the row maximum in its lane 15, two row broadcasts
+// gather it in lane 63, which is then read out.  (DPP lane moves; a lane
+// without a source keeps its own value.)
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t max_step(uint32_t v) {
+  const uint32_t o = __builtin_amdgcn_update_dpp(v, v, CTRL, ROWS, 0xf, false);
+  return o > v ? o : v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max_step<0x111, 0xf>(v);  // row_shr:1
+  v = max_step<0x112, 0xf>(v);  // row_shr:2
+  v = max_step<0x114, 0xf>(v);  // row_shr:4
+  v = max_step<0x118, 0xf>(v);  // row_shr:8
+  v = max_step<0x142, 0xa>(v);  // row_bcast:15 into rows 1, 3
+  v = max_step<0x143, 0xc>(v);  // row_bcast:31 into rows 2, 3
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// The maximum 64-bit key of the wavefront: the maximum upper half first;
+// only if several lanes hold it (tied logits) the lower halves decide.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+  const uint32_t hi = (uint32_t)(k >> 32), lo = (uint32_t)k;
+  const uint32_t mh = wave_max_u32(hi);
+  const uint64_t tied = __ballot(hi == mh);
+  uint32_t ml;
+  if ((tied & (tied - 1)) == 0) ml = __builtin_amdgcn_readlane(lo, __builtin_ctzll(tied));  // one lane
+  else ml = wave_max_u32(hi == mh ? lo : 0u);
+  return ((uint64_t)mh << 32) | ml;
+}
+
+// Route one token (one wavefront): top_k rounds of the wavefront-wide
+// (logit desc, id asc) maximum, then the softmax over the selected logits
+// (fp32, exponentials relative to the largest, summed in selection order).
+// Lane l holds the logits of experts l + 64 i (i < NPL); each lane keeps its
+// best remaining key, and only the round's winner recomputes its own.
 template <int NPL>
-__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int64_t tokens, int experts,
-                                                    int top_k, int32_t* __restrict__ ids, float* __restrict__ g) {
-  __shared__ float s_val[4][kMaxTopK];
-  __shared__ int s_id[4][kMaxTopK];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
-  if (t >= tokens) return;
-  const float* lt = logits + t * experts;
+__device__ __forceinline__ void route_token(const float* __restrict__ lt, int experts, int top_k, int lane,
+                                            float* s_val /* [top_k], this wavefront's */, int32_t* ids_out,
+                                            float* g_out) {
+  // All loads first (addresses clamped into the row), then the keys: a
+  // load under a branch would be waited for on its own.
   float v[NPL];
-  uint32_t avail = 0;
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + 64 * i;
-    v[i] = e < experts ? lt[e] : 0.0f;
-    if (e < experts) avail |= 1u << i;
+    v[i] = lt[e < experts ? e : experts - 1];
   }
+  uint64_t key[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = e < experts ? route_key(v[i], e) : 0ull;
+  }
+  auto local_best = [&]() __attribute__((always_inline)) {
+    uint64_t b = key[0];
+#pragma unroll
+    for (int i = 1; i < NPL; ++i) b = key[i] > b ? key[i] : b;
+    return b;
+  };
+  uint64_t best = local_best();
+  int win_id = 0;
   for (int r = 0; r < top_k; ++r) {
-    float bv = 0.0f;
-    int bi = -1;
+    const uint64_t wk = wave_max_key(best);
+    const int id = (int)~(uint32_t)wk;
+    if (lane == 0) s_val[r] = key_logit(wk);
+    if (lane == r) win_id = id;
+    if (lane == (id & 63)) {
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-      const int e = lane + 64 * i;
-      if (((avail >> i) & 1u) && better(v[i], e, bv, bi)) { bv = v[i]; bi = e; }
+      for (int i = 0; i < NPL; ++i)
+        if (i == (id >> 6)) key[i] = 0ull;
+      best = local_best();
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, 64);
-      const int oi = __shfl_xor(bi, off, 64);
-      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-    }
-    if (bi >= 0 && lane == (bi & 63)) avail &= ~(1u << (bi >> 6));
-    if (lane == 0) { s_val[wave][r] = bv; s_id[wave][r] = bi; }
   }
-  // Lane 0 wrote s_val / s_id and lane 0 reads them: no barrier needed.
-  if (lane == 0) {
-    const float l0 = s_val[wave][0];
-    float sum = 0.0f;
-    for (int j = 0; j < top_k; ++j) sum += expf(s_val[wave][j] - l0);
-    for (int j = 0; j < top_k; ++j) {
-      ids[t * top_k + j] = s_id[wave][j];
-      g[t * top_k + j] = expf(s_val[wave][j] - l0) / sum;
-    }
+  // Lanes j < top_k: exponential of selection j; lane 0 adds them in order.
+  // (LDS operations of one wavefront are performed in order.)
+  const float l0 = s_val[0];
+  float ex = 0.0f;
+  if (lane < top_k) {
+    ex = expf(s_val[lane] - l0);
+    s_val[lane] = ex;
+  }
+  __builtin_amdgcn_wave_barrier();
+  float sum = 0.0f;
+  if (lane == 0)
+    for (int j = 0; j < top_k; ++j) sum += s_val[j];
+  sum = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(sum), 0));
+  if (lane < top_k) {
+    ids_out[lane] = win_id;
+    g_out[lane] = ex / sum;
   }
 }
 
-// Exclusive scan of `in[0..n)` (n <= 2048) by a 1024-thread workgroup; returns the total.
-__device__ int block_exclusive_scan(const int* in, int* out, int n, int* s_tmp /* [1024] */) {
-  const int tid = threadIdx.x;
+// One token per 64-thread workgroup: a small batch spreads over many CUs.
+template <int NPL>
+__global__ __launch_bounds__(64) void route_kernel(const float* __restrict__ logits, int64_t tokens, int experts,
+                                                   int top_k, int32_t* __restrict__ ids, float* __restrict__ g) {
+  __shared__ float s_val[kMaxTopK];
+  const int64_t t = blockIdx.x;
+  route_token<NPL>(logits + t * experts, experts, top_k, threadIdx.x, s_val, ids + t * top_k, g + t * top_k);
+}
+
+// Inclusive sum over the lanes of a wavefront (DPP: shifts within each row
+// of 16, then row broadcasts; a lane without a source adds 0).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int scan_step(int v) {
+  return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xf, false);
+}
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  v = scan_step<0x111, 0xf>(v);  // row_shr:1
+  v = scan_step<0x112, 0xf>(v);  // row_shr:2
+  v = scan_step<0x114, 0xf>(v);  // row_shr:4
+  v = scan_step<0x118, 0xf>(v);  // row_shr:8
+  v = scan_step<0x142, 0xa>(v);  // row_bcast:15 into rows 1, 3
+  v = scan_step<0x143, 0xc>(v);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
+// Exclusive scan of `in[0..n)` (n <= 2048) by a 1024-thread workgroup
+// (thread t owns elements 2t, 2t+1); returns the total.  `in` and `out` may
+// be the same array.
+__device__ int block_exclusive_scan(const int* in, int* out, int n, int* s_tmp /* [32] */) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int a0 = 2 * tid < n ? in[2 * tid] : 0;
   const int a1 = 2 * tid + 1 < n ? in[2 * tid + 1] : 0;
-  s_tmp[tid] = a0 + a1;
+  const int incl = wave_inclusive_sum(a0 + a1);
+  if (lane == 63) s_tmp[wave] = incl;
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = tid >= off ? s_tmp[tid - off] : 0;
-    __syncthreads();
-    s_tmp[tid] += v;
-    __syncthreads();
+  if (tid < 64) {
+    const int t = lane < 16 ? s_tmp[lane] : 0;
+    const int ti = wave_inclusive_sum(t);
+    if (lane < 16) s_tmp[16 + lane] = ti - t;  // exclusive prefix of the wavefront totals
+    if (lane == 15) s_tmp[32] = ti;
   }
-  const int incl = s_tmp[tid];
-  const int excl = incl - (a0 + a1);
+  __syncthreads();
+  const int excl = s_tmp[16 + wave] + incl - (a0 + a1);
   if (2 * tid < n) out[2 * tid] = excl;
   if (2 * tid + 1 < n) out[2 * tid + 1] = excl + a0;
-  const int total = s_tmp[1023];
+  const int total = s_tmp[32];
   __syncthreads();
   return total;
 }
 
-__global__ __launch_bounds__(1024) void group_kernel(const int32_t* __restrict__ ids, int total, int experts,
-                                                     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                                     int32_t* __restrict__ perm, int32_t* __restrict__ pos,
-                                                     int32_t* __restrict__ active, int32_t* __restrict__ n_active) {
+// Grouping by one 1024-thread workgroup (ids: global or LDS).
+__device__ __forceinline__ void group_body(const int32_t* ids, int total, int experts, int top_k,
+                                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                           int32_t* __restrict__ perm, int32_t* __restrict__ pos,
+                                           int32_t* __restrict__ chunks, int32_t* __restrict__ n_chunks) {
   __shared__ int s_cnt[kMaxExperts];
   __shared__ int s_off[kMaxExperts];
   __shared__ int s_run[kMaxExperts];
-  __shared__ int s_tmp[1024];
-  __shared__ int s_chunk[1024];
+  __shared__ int s_chb[kMaxExperts];
+  __shared__ int s_tmp[64];
   const int tid = threadIdx.x;
   for (int e = tid; e < experts; e += 1024) { s_cnt[e] = 0; s_run[e] = 0; }
   __syncthreads();
@@ -120,165 +205,254 @@ __global__ __launch_bounds__(1024) void group_kernel(const int32_t* __restrict__
   for (int e = tid; e < experts; e += 1024) {
     counts[e] = s_cnt[e];
     offsets[e] = s_off[e];
+    s_chb[e] = (s_cnt[e] + kChunkRows - 1) / kChunkRows;
   }
   if (tid == 0) offsets[experts] = all;
-  // Active experts, ascending: scan of (count > 0).
-  for (int e = tid; e < experts; e += 1024) s_run[e] = s_cnt[e] > 0 ? 1 : 0;
   __syncthreads();
-  const int na = block_exclusive_scan(s_run, s_run, experts, s_tmp);
-  for (int e = tid; e < experts; e += 1024)
-    if (s_cnt[e] > 0) active[s_run[e]] = e;
-  if (tid == 0) *n_active = na;
-  __syncthreads();
-  for (int e = tid; e < experts; e += 1024) s_run[e] = 0;
-  __syncthreads();
-  // Stable counting sort, 1024 flat indices at a time.
+  // Work list of the expert GEMMs: each expert's rows in chunks of 32, in
+  // expert order; record j = {expert, first row slot, rows, 0, the token of
+  // each of its 32 rows (the last one repeated past the end)}.
+  const int nch = block_exclusive_scan(s_chb, s_chb, experts, s_tmp);
+  if (tid == 0) *n_chunks = nch;
+  // Stable counting sort, 1024 flat indices at a time; each row's token goes
+  // straight into its chunk record.  Within a wavefront a row's rank among
+  // equal experts comes from lane masks (one round per distinct expert);
+  // the wavefronts then take their rows in order.
+  const int wave = tid >> 6, lane = tid & 63;
+  const uint64_t lanes_below = (1ull << lane) - 1ull;
   for (int base = 0; base < total; base += 1024) {
     const int f = base + tid;
     const int e = f < total ? ids[f] : -1;
-    s_chunk[tid] = e;
-    __syncthreads();
-    if (e >= 0) {
-      int rank = 0;
-      for (int j = 0; j < tid; ++j) rank += s_chunk[j] == e ? 1 : 0;
-      const int p = s_off[e] + s_run[e] + rank;
-      perm[p] = f;
-      pos[f] = p;
+    uint64_t todo = __ballot(e >= 0);
+    int rank_w = 0, cnt_w = 0;
+    while (todo) {
+      const int le = __builtin_amdgcn_readlane(e, __builtin_ctzll(todo));
+      const uint64_t m = __ballot(e == le);
+      if (e == le) {
+        rank_w = __builtin_popcountll(m & lanes_below);
+        cnt_w = __builtin_popcountll(m);
+      }
+      todo &= ~m;
     }
-    __syncthreads();
-    if (e >= 0) atomicAdd(&s_run[e], 1);
-    __syncthreads();
+    const int nw = (total - base + 63) / 64 < 16 ? (total - base + 63) / 64 : 16;
+    for (int w = 0; w < nw; ++w) {
+      if (wave == w && e >= 0) {
+        const int r = s_run[e] + rank_w;  // row within the expert
+        const int p = s_off[e] + r;
+        perm[p] = f;
+        pos[f] = p;
+        chunks[(size_t)(s_chb[e] + r / kChunkRows) * kChunkInts + 4 + r % kChunkRows] = f / top_k;
+      }
+      __syncthreads();
+      if (wave == w && e >= 0 && rank_w == 0) s_run[e] += cnt_w;
+      __syncthreads();
+    }
+  }
+  // Headers, and the unused rows of each expert's last chunk.
+  for (int e = tid; e < experts; e += 1024) {
+    const int cnt = s_cnt[e];
+    for (int c = 0; c * kChunkRows < cnt; ++c) {
+      int32_t* r = chunks + (size_t)(s_chb[e] + c) * kChunkInts;
+      const int rows = cnt - c * kChunkRows < kChunkRows ? cnt - c * kChunkRows : kChunkRows;
+      r[0] = e;
+      r[1] = s_off[e] + c * kChunkRows;
+      r[2] = rows;
+      r[3] = 0;
+      if (rows < kChunkRows) {
+        const int tok = r[4 + rows - 1];  // written above by this workgroup
+        for (int q = rows; q < kChunkRows; ++q) r[4 + q] = tok;
+      }
+    }
   }
 }
 
-// a6: per workgroup (active expert a, row pair j): waves 0/1 take gate row
-// tiles 2j, 2j+1 and waves 2/3 the same up row tiles, all over the whole
-// hidden dimension with one shared activation tile per k tile; the up results
-// go through LDS to the gate waves, which form h = bf16(silu(G) * U).
-template <bool KFULL>
-__global__ __launch_bounds__(256, 1) void gate_up_kernel(
-    const uint16_t* __restrict__ x, const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ active, const int32_t* __restrict__ n_active, int top_k, int hidden, int inter,
-    const uint8_t* __restrict__ w_gate, const uint8_t* __restrict__ w_up, size_t stride_gate, size_t stride_up,
-    const float* __restrict__ scale_gate, const float* __restrict__ scale_up, uint16_t* __restrict__ h,
-    float* __restrict__ dbg_gate, float* __restrict__ dbg_up) {
-  __shared__ __attribute__((aligned(16))) uint8_t xb0[kXTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t xb1[kXTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t xb2[kXTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t xb3[kXTileBytes];
-  __shared__ float lds_u[2][32][65];
+__global__ __launch_bounds__(1024) void group_kernel(const int32_t* __restrict__ ids, int total, int experts,
+                                                     int top_k, int32_t* __restrict__ counts,
+                                                     int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+                                                     int32_t* __restrict__ pos, int32_t* __restrict__ chunks,
+                                                     int32_t* __restrict__ n_chunks) {
+  group_body(ids, total, experts, top_k, counts, offsets, perm, pos, chunks, n_chunks);
+}
+
+// ---- expert GEMMs --------------------------------------------------------
+// One workgroup of 8 wavefronts per (work-list chunk, output rows); each
+// wavefront multiplies one 64-row weight tile by one 256-k activation tile
+// per round.  Each round stages
+// the chunk's activation tiles of the k slots in LDS once for all eight
+// (activations past K load as zeros).  The products of the k slots then meet
+// in LDS and are added in slot order.  This spreads a small expert batch
+// over the whole chip -- two workgroups per CU, four wavefronts per SIMD,
+// which the dequantisation needs to keep a SIMD busy.
+constexpr int kExpertWaves = 8;
+constexpr int kExpertLds = 64 * 1024;  // 4 activation tiles, later 8 wavefronts' partial sums
+
+// This wavefront's share of staging k tiles t0 .. t0 + KS - 1 of a chunk:
+// activation rows 4 w .. 4 w + 3 of each (row 4 w + 2 j + lane / 32 from
+// `xrow[j]`), swizzled as skinny_core.h lays tiles out.
+template <int KS>
+__device__ __forceinline__ void stage_k_tiles(const uint16_t* const (&xrow)[2], int t0, int k, int wave, int lane,
+                                              uint8_t* lds) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int srow = 4 * wave + 2 * j + (lane >> 5);
+    const int cofs = 8 * ((lane & 31) ^ (srow & 15));
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      const int kk = (t0 + t) * kTileK + cofs;
+      const uint16_t* src = kk < k ? xrow[j] + kk : reinterpret_cast<const uint16_t*>(&g_zero_chunk);
+      load_lds16(src, lds + t * kXTileBytes + (4 * wave + 2 * j) * 512);
+    }
+  }
+}
+
+// Rounds over the k tiles: wavefront slot `slot` of KS takes tiles slot,
+// slot + KS, ...; its 64-row tile at `wrow` (null: no rows, stages only).
+// The running sums acc_a / acc_b continue one matrix chain across rounds.
+// (A round's weights load with its activations: holding the next round's
+// weights as well would not fit four wavefronts per SIMD.)
+template <int KS>
+__device__ __forceinline__ void expert_rounds(const uint8_t* wrow, int nkt, int k, int slot,
+                                              const uint16_t* const (&xrow)[2], int wave, int lane, uint8_t* lds,
+                                              f32x16& acc_a, f32x16& acc_b) {
+  for (int g0 = 0; g0 < nkt; g0 += KS) {
+    const int kt = g0 + slot;
+    const bool mine = wrow && kt < nkt;
+    WTile w;
+    if (mine) load_wtile(wrow + (size_t)kt * kTileBytes, lane, w);
+    stage_k_tiles<KS>(xrow, g0, k, wave, lane, lds);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (mine) tile_product(w, lds + slot * kXTileBytes, lane, acc_a, acc_b);
+    __syncthreads();  // the tiles are consumed before they are overwritten
+  }
+}
+
+__device__ __forceinline__ void store_partials(float* red, int wave, int lane, const f32x16& acc_a,
+                                               const f32x16& acc_b) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    red[(32 * wave + i) * 64 + lane] = acc_a[i];
+    red[(32 * wave + 16 + i) * 64 + lane] = acc_b[i];
+  }
+}
+
+// a6: gate/up.  Workgroup (chunk, row tile rt): wavefronts 0-3 take the gate
+// matrix's tile rt at k slots 0-3, wavefronts 4-7 the up matrix's; then
+// h = bf16(silu(s_g Wg x) * (s_u Wu x)) for the tile's 64 rows.
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void gate_up_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ chunks, const int32_t* __restrict__ n_chunks,
+    int hidden, int inter, const uint8_t* __restrict__ w_gate, const uint8_t* __restrict__ w_up,
+    size_t stride_gate, size_t stride_up, const float* __restrict__ scale_gate, const float* __restrict__ scale_up,
+    uint16_t* __restrict__ h, float* __restrict__ dbg_gate, float* __restrict__ dbg_up) {
+  constexpr int KS = 4;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kExpertLds];
   const int nrt = (inter + 63) / 64;
-  const int npairs = (nrt + 1) / 2;
-  const int a = blockIdx.x / npairs;
-  const int pair = blockIdx.x % npairs;
-  if (a >= *n_active) return;
-  const int e = active[a];
-  const int p0 = offsets[e], p1 = offsets[e + 1];
+  const int jc = blockIdx.x / nrt;
+  const int rt = blockIdx.x % nrt;
+  // The record is loaded together with the count (it lies inside the list
+  // for every launched workgroup).
+  const int32_t* rec = chunks + (size_t)jc * kChunkInts;
+  const int nch = *n_chunks;
+  const int e = rec[0], p0 = rec[1], rows = rec[2];
+  if (jc >= nch) return;
   const int nkt = (hidden + 255) / 256;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const bool is_up = wave >= 2;
-  const int rt = 2 * pair + (wave & 1);
-  // A wavefront past the last row tile streams the last one (not stored).
-  const uint8_t* wrow = (is_up ? w_up + e * stride_up : w_gate + e * stride_gate) +
-                        (size_t)(rt < nrt ? rt : nrt - 1) * nkt * kTileBytes;
+  const int slot = wave % KS;
+  const uint8_t* wrow = (wave >= KS ? w_up + e * stride_up : w_gate + e * stride_gate) + (size_t)rt * nkt * kTileBytes;
+  const uint16_t* xrow[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) xrow[j] = x + (int64_t)rec[4 + 4 * wave + 2 * j + (lane >> 5)] * hidden;
+  f32x16 acc_a = {}, acc_b = {};
+  expert_rounds<KS>(wrow, nkt, hidden, slot, xrow, wave, lane, lds, acc_a, acc_b);
+  float* red = reinterpret_cast<float*>(lds);
+  store_partials(red, wave, lane, acc_a, acc_b);
+  __syncthreads();
+  // Thread t: accumulator elements i0 + 8 q (i0 = t / 64) of lane t % 64, gate and up.
+  const int l = threadIdx.x & 63, i0 = threadIdx.x >> 6;
+  const int slots = nkt < KS ? nkt : KS;
   const float sg = scale_gate[e], su = scale_up[e];
-  const int tok = lane & 31;
-  for (int c0 = p0; c0 < p1; c0 += 32) {
-    // Activation rows of this chunk, gathered through perm; rows past the
-    // expert's last repeat it (their outputs are not stored).
-    const uint16_t* rowp[4];
+  const int tok = l & 31;
+  if (tok >= rows) return;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int ps = c0 + stage_row(wave, j, lane);
-      rowp[j] = x + (int64_t)(perm[ps < p1 ? ps : p1 - 1] / top_k) * hidden;
+  for (int q = 0; q < 4; ++q) {
+    const int i = i0 + 8 * q;
+    float g = 0.0f, u = 0.0f;
+    for (int sl = 0; sl < slots; ++sl) {
+      g += red[(32 * sl + i) * 64 + l];
+      u += red[(32 * (KS + sl) + i) * 64 + l];
     }
-    f32x16 acc_a = {}, acc_b = {};
-    skinny_stream<4, KFULL>(wrow, 0, nkt, hidden, rowp, xb0, xb1, xb2, xb3, wave, lane, acc_a, acc_b);
-    if (is_up) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        lds_u[wave & 1][tok][acc_row(0, i, lane)] = acc_a[i] * su;
-        lds_u[wave & 1][tok][acc_row(1, i, lane)] = acc_b[i] * su;
-      }
+    const int row = rt * 64 + acc_row(i >> 4, i & 15, l);
+    if (row < inter) {
+      const int64_t at = (int64_t)(p0 + tok) * inter + row;
+      const float gv = g * sg, uv = u * su;
+      h[at] = to_bf16((gv / (1.0f + expf(-gv))) * uv);
+      if (dbg_gate) dbg_gate[at] = gv;
+      if (dbg_up) dbg_up[at] = uv;
     }
-    __syncthreads();
-    const int p = c0 + tok;
-    if (!is_up && rt < nrt && p < p1) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = acc_row(hh, i, lane);
-          const int row = rt * 64 + r;
-          if (row < inter) {
-            const float gv = (hh ? acc_b[i] : acc_a[i]) * sg;
-            const float uv = lds_u[wave & 1][tok][r];
-            const float hv = (gv / (1.0f + expf(-gv))) * uv;
-            h[(int64_t)p * inter + row] = to_bf16(hv);
-            if (dbg_gate) dbg_gate[(int64_t)p * inter + row] = gv;
-            if (dbg_up) dbg_up[(int64_t)p * inter + row] = uv;
-          }
-        }
-      }
-    }
-    __syncthreads();  // lds_u is rewritten by the next chunk
   }
 }
 
-// a7: per workgroup (active expert a, row quad j): four down row tiles over the
-// expert width, activation rows = the expert's rows of h.
-template <bool KFULL>
-__global__ __launch_bounds__(256, 1) void down_kernel(const uint16_t* __restrict__ h,
-                                                      const int32_t* __restrict__ offsets,
-                                                      const int32_t* __restrict__ active,
-                                                      const int32_t* __restrict__ n_active, int hidden, int inter,
+// a7: down.  Workgroup (chunk, row tiles 4 q .. 4 q + 3): wavefront w takes
+// row tile 4 q + w / 2 at k slot w % 2; d = s_d Wd h (fp32) for those rows.
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void down_kernel(const uint16_t* __restrict__ hin,
+                                                      const int32_t* __restrict__ chunks,
+                                                      const int32_t* __restrict__ n_chunks, int hidden, int inter,
                                                       const uint8_t* __restrict__ w_down, size_t stride_down,
                                                       const float* __restrict__ scale_down, float* __restrict__ d) {
-  __shared__ __attribute__((aligned(16))) uint8_t xb0[kXTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t xb1[kXTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t xb2[kXTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t xb3[kXTileBytes];
+  constexpr int KS = 2;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kExpertLds];
   const int nrt = (hidden + 63) / 64;
-  const int nquads = (nrt + 3) / 4;
-  const int a = blockIdx.x / nquads;
-  const int quad = blockIdx.x % nquads;
-  if (a >= *n_active) return;
-  const int e = active[a];
-  const int p0 = offsets[e], p1 = offsets[e + 1];
+  const int ngrp = (nrt + 3) / 4;
+  const int jc = blockIdx.x / ngrp;
+  const int grp = blockIdx.x % ngrp;
+  const int32_t* rec = chunks + (size_t)jc * kChunkInts;
+  const int nch = *n_chunks;
+  const int e = rec[0], p0 = rec[1], rows = rec[2];
+  if (jc >= nch) return;
   const int nkt = (inter + 255) / 256;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int rt = 4 * quad + wave;
-  const uint8_t* wrow = w_down + e * stride_down + (size_t)(rt < nrt ? rt : nrt - 1) * nkt * kTileBytes;
-  const float sd = scale_down[e];
+  const int slot = wave % KS;
+  const int rt = 4 * grp + wave / KS;
+  const bool has_rows = rt < nrt;
+  const uint8_t* wrow = has_rows ? w_down + e * stride_down + (size_t)rt * nkt * kTileBytes : nullptr;
+  // The chunk's rows of h are contiguous (the last repeated past the end).
+  const uint16_t* xrow[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int srow = 4 * wave + 2 * j + (lane >> 5);
+    xrow[j] = hin + (int64_t)(p0 + (srow < rows ? srow : rows - 1)) * inter;
+  }
+  f32x16 acc_a = {}, acc_b = {};
+  expert_rounds<KS>(wrow, nkt, inter, slot, xrow, wave, lane, lds, acc_a, acc_b);
+  float* red = reinterpret_cast<float*>(lds);
+  store_partials(red, wave, lane, acc_a, acc_b);
+  __syncthreads();
+  // The slot-0 wavefront of each row tile adds its tile's slots in order.
   const int tok = lane & 31;
-  for (int c0 = p0; c0 < p1; c0 += 32) {
-    const uint16_t* rowp[4];
+  if (slot != 0 || !has_rows || tok >= rows) return;
+  const int slots = nkt < KS ? nkt : KS;
+  const float sd = scale_down[e];
+  float* drow = d + (int64_t)(p0 + tok) * hidden;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int ps = c0 + stage_row(wave, j, lane);
-      rowp[j] = h + (int64_t)(ps < p1 ? ps : p1 - 1) * inter;
-    }
-    f32x16 acc_a = {}, acc_b = {};
-    skinny_stream<4, KFULL>(wrow, 0, nkt, inter, rowp, xb0, xb1, xb2, xb3, wave, lane, acc_a, acc_b);
-    const int p = c0 + tok;
-    if (rt < nrt && p < p1) {
-      float* drow = d + (int64_t)p * hidden;
+  for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
+    for (int e4 = 0; e4 < 4; ++e4) {
+      float v[4];
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          const int row = rt * 64 + acc_row(hh, 4 * e4, lane);
-          const f32x16& acc = hh ? acc_b : acc_a;
-          if (row + 4 <= hidden) {
-            *reinterpret_cast<f32x4*>(drow + row) =
-                f32x4{acc[4 * e4] * sd, acc[4 * e4 + 1] * sd, acc[4 * e4 + 2] * sd, acc[4 * e4 + 3] * sd};
-          } else {
-            for (int i = 0; i < 4; ++i)
-              if (row + i < hidden) drow[row + i] = acc[4 * e4 + i] * sd;
-          }
-        }
+      for (int c = 0; c < 4; ++c) {
+        const int i = 16 * hh + 4 * e4 + c;
+        float acc = 0.0f;
+        for (int sl = 0; sl < slots; ++sl) acc += red[(32 * (wave + sl) + i) * 64 + lane];
+        v[c] = acc * sd;
+      }
+      const int row = rt * 64 + acc_row(hh, 4 * e4, lane);
+      if (row + 4 <= hidden) {
+        *reinterpret_cast<f32x4*>(drow + row) = f32x4{v[0], v[1], v[2], v[3]};
+      } else {
+        for (int c = 0; c < 4; ++c)
+          if (row + c < hidden) drow[row + c] = v[c];
       }
     }
   }
@@ -302,12 +476,19 @@ __global__ __launch_bounds__(256) void scatter_kernel(const float* __restrict__ 
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Upper bound on the work-list length: every active expert (at most
+// min(experts, tokens * top_k)) has one partial chunk, plus the full ones.
+int64_t max_chunks(int64_t tokens, int64_t experts, int64_t top_k) {
+  const int64_t flat = tokens * top_k;
+  return (experts < flat ? experts : flat) + flat / kChunkRows;
+}
+
 struct MoeWs {
   int32_t* pos;
-  int32_t* active;
-  int32_t* n_active;
   uint16_t* h;
   float* d;
+  int32_t* chunks;
+  int32_t* n_chunks;
 };
 
 MoeWs carve(void* ws, int64_t tokens, int64_t experts, int64_t top_k, int64_t hidden, int64_t inter, size_t* total) {
@@ -316,10 +497,10 @@ MoeWs carve(void* ws, int64_t tokens, int64_t experts, int64_t top_k, int64_t hi
   MoeWs w;
   const int64_t f = tokens * top_k;
   w.pos = reinterpret_cast<int32_t*>(p + off); off = align256(off + (size_t)f * 4);
-  w.active = reinterpret_cast<int32_t*>(p + off); off = align256(off + (size_t)experts * 4);
-  w.n_active = reinterpret_cast<int32_t*>(p + off); off = align256(off + 16);
   w.h = reinterpret_cast<uint16_t*>(p + off); off = align256(off + (size_t)f * inter * 2);
   w.d = reinterpret_cast<float*>(p + off); off = align256(off + (size_t)f * hidden * 4);
+  w.chunks = reinterpret_cast<int32_t*>(p + off); off = align256(off + (size_t)max_chunks(tokens, experts, top_k) * kChunkInts * 4);
+  w.n_chunks = reinterpret_cast<int32_t*>(p + off); off = align256(off + 16);
   if (total) *total = off;
   return w;
 }
@@ -338,45 +519,30 @@ hipError_t launch_moe(const MoeLaunch& a, hipStream_t s) {
   if (a.tokens == 0) return hipSuccess;
   MoeWs w = carve(a.ws, a.tokens, a.experts, a.top_k, a.hidden, a.inter, nullptr);
   const int64_t flat = a.tokens * a.top_k;
-  const unsigned route_blocks = (unsigned)((a.tokens + 3) / 4);
-  if (a.experts <= 512)
-    hipLaunchKernelGGL(route_kernel<8>, dim3(route_blocks), dim3(256), 0, s, a.logits, a.tokens, (int)a.experts,
-                       (int)a.top_k, a.ids, a.g);
-  else if (a.experts <= 1024)
-    hipLaunchKernelGGL(route_kernel<16>, dim3(route_blocks), dim3(256), 0, s, a.logits, a.tokens, (int)a.experts,
-                       (int)a.top_k, a.ids, a.g);
-  else
-    hipLaunchKernelGGL(route_kernel<32>, dim3(route_blocks), dim3(256), 0, s, a.logits, a.tokens, (int)a.experts,
-                       (int)a.top_k, a.ids, a.g);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(1024), 0, s, a.ids, (int)flat, (int)a.experts, a.counts, a.offsets,
-                     a.perm, w.pos, w.active, w.n_active);
+  hipError_t err = hipSuccess;
+#define NVFP4_R(NPL)                                                                                        \
+  hipLaunchKernelGGL(route_kernel<NPL>, dim3((unsigned)a.tokens), dim3(64), 0, s, a.logits, a.tokens, (int)a.experts, \
+                     (int)a.top_k, a.ids, a.g)
+  if (a.experts <= 512) NVFP4_R(8);
+  else if (a.experts <= 1024) NVFP4_R(16);
+  else NVFP4_R(32);
+#undef NVFP4_R
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  const int64_t max_active = a.experts < flat ? a.experts : flat;
-  const int64_t pairs_i = ((a.inter + 63) / 64 + 1) / 2;
-  const dim3 gu_grid((unsigned)(max_active * pairs_i));
-  if (a.hidden % kTileK == 0)
-    gate_up_kernel<true><<<gu_grid, dim3(256), 0, s>>>(a.x, a.perm, a.offsets, w.active, w.n_active, (int)a.top_k,
-                                                       (int)a.hidden, (int)a.inter, a.w_gate, a.w_up, a.stride_gate,
-                                                       a.stride_up, a.scale_gate, a.scale_up, w.h, a.dbg_gate,
-                                                       a.dbg_up);
-  else
-    gate_up_kernel<false><<<gu_grid, dim3(256), 0, s>>>(a.x, a.perm, a.offsets, w.active, w.n_active, (int)a.top_k,
-                                                        (int)a.hidden, (int)a.inter, a.w_gate, a.w_up, a.stride_gate,
-                                                        a.stride_up, a.scale_gate, a.scale_up, w.h, a.dbg_gate,
-                                                        a.dbg_up);
+  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(1024), 0, s, a.ids, (int)flat, (int)a.experts, (int)a.top_k,
+                     a.counts, a.offsets, a.perm, w.pos, w.chunks, w.n_chunks);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  const int64_t nrt_h = (a.hidden + 63) / 64;
-  const int64_t wgs_h = (nrt_h + 3) / 4;
+  // Expert GEMM grids cover the work list's bound; workgroups past its
+  // length return at once.
+  const int64_t mch = max_chunks(a.tokens, a.experts, a.top_k);
+  const int64_t nrt_i = (a.inter + 63) / 64;
+  hipLaunchKernelGGL(gate_up_kernel, dim3((unsigned)(mch * nrt_i)), dim3(64 * kExpertWaves), 0, s, a.x, w.chunks, w.n_chunks,
+                     (int)a.hidden, (int)a.inter, a.w_gate, a.w_up, a.stride_gate, a.stride_up, a.scale_gate,
+                     a.scale_up, w.h, a.dbg_gate, a.dbg_up);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  const int64_t grp_h = ((a.hidden + 63) / 64 + 3) / 4;
   float* d = a.dbg_down ? a.dbg_down : w.d;
-  const dim3 dn_grid((unsigned)(max_active * wgs_h));
-  if (a.inter % kTileK == 0)
-    down_kernel<true><<<dn_grid, dim3(256), 0, s>>>(w.h, a.offsets, w.active, w.n_active, (int)a.hidden,
-                                                    (int)a.inter, a.w_down, a.stride_down, a.scale_down, d);
-  else
-    down_kernel<false><<<dn_grid, dim3(256), 0, s>>>(w.h, a.offsets, w.active, w.n_active, (int)a.hidden,
-                                                     (int)a.inter, a.w_down, a.stride_down, a.scale_down, d);
+  hipLaunchKernelGGL(down_kernel, dim3((unsigned)(mch * grp_h)), dim3(64 * kExpertWaves), 0, s, w.h, w.chunks, w.n_chunks,
+                     (int)a.hidden, (int)a.inter, a.w_down, a.stride_down, a.scale_down, d);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const int64_t outs = a.tokens * a.hidden;
   hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, s, d, a.g, w.pos, a.tokens,

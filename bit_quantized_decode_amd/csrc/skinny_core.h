@@ -86,6 +86,24 @@ __device__ __forceinline__ void load_bops(const uint8_t* buf, uint32_t abase_a, 
 // fetches the logical chunk stored at physical chunk l % 32 of its row.
 __device__ __forceinline__ int stage_row(int wave, int j, int lane) { return 8 * wave + 2 * j + (lane >> 5); }
 
+// A resident weight tile times one activation tile in LDS into fresh
+// accumulators ta / tb (16 matrix steps, chunk order -- the same arithmetic
+// as one step of skinny_stream).
+__device__ __forceinline__ void tile_product(const WTile& w, const uint8_t* buf, int lane, f32x16& ta,
+                                             f32x16& tb) {
+  const int br = lane & 31, bh = lane >> 5;
+  const uint32_t abase_a = 512 * br + 16 * (bh ^ (br & 3));
+  const uint32_t abase_b = 512 * br + 16 * ((2 + bh) ^ (br & 3));
+  const uint32_t sw = 64 * ((br & 15) >> 2);
+  bf16x8 xa, xb;
+#define NVFP4_TP_CHUNK(C)                          \
+  load_bops<C>(buf, abase_a, abase_b, sw, xa, xb); \
+  chunk_mfma<C>(w.q[C], w.sa, w.sb, xa, xb, ta, tb);
+  NVFP4_TP_CHUNK(0) NVFP4_TP_CHUNK(1) NVFP4_TP_CHUNK(2) NVFP4_TP_CHUNK(3)
+  NVFP4_TP_CHUNK(4) NVFP4_TP_CHUNK(5) NVFP4_TP_CHUNK(6) NVFP4_TP_CHUNK(7)
+#undef NVFP4_TP_CHUNK
+}
+
 // Sixteen zero bytes: the source of activation chunks past K.
 static __device__ u32x4 g_zero_chunk;
 
@@ -183,7 +201,7 @@ __device__ __forceinline__ void skinny_stream(const uint8_t* wrow, int kt0, int 
     load_w(3, w3);
   }
   __builtin_amdgcn_sched_barrier(0);
-  wait_vmcnt_lgkm0<kAfterX>();
+  wait_vmcnt_lgkm0<kAfterX>();  // x(0)
   barrier_only();
   __builtin_amdgcn_sched_barrier(0);
 #define NVFP4_SK_STEP(S, W)                                                 \

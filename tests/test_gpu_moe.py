@@ -130,6 +130,8 @@ def small_weights(seed, e, hidden, inter):
     (7, 6, 3, 272, 48),      # ragged against the 256-k and 64-row tiles
     (40, 12, 4, 512, 96),    # an expert can receive more than 32 rows
     (3, 64, 1, 128, 32),
+    (130, 16, 8, 128, 32),   # tokens * top_k > 1024: separate routing and grouping launches
+    (4, 1100, 2, 128, 32),   # more than 1024 experts: separate launches, 32 logits per lane
 ])
 def test_moe_small(t, e, k, hidden, inter):
     w = small_weights(50 + e, e, hidden, inter)
