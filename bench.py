@@ -34,6 +34,53 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+class HipTimingEvents:
+    """HIP events for the per-row intervals, recorded on the stream the rows
+    launch on.  They are created with hipEventDisableSystemFence: recording
+    one then does not write back and invalidate the caches, a cost that would
+    otherwise land inside the interval it closes (several microseconds, more
+    after a row that writes tens of megabytes).  Elapsed times are read only
+    after a device synchronisation."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        # The HIP runtime that torch has loaded (same soname), not a second copy.
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+
+    def new(self):
+        ev = self.ct.c_void_p()
+        rc = self.hip.hipEventCreateWithFlags(self.ct.byref(ev), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self.events.append(ev)
+        return ev
+
+    def record(self, ev, stream):
+        rc = self.hip.hipEventRecord(ev, self.ct.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_ms(self, a, b):
+        ms = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def close(self):
+        for ev in self.events:
+            self.hip.hipEventDestroy(ev)
+        self.events = []
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -218,19 +265,21 @@ def main():
         log(f"captured {len(graphs)} graphs; replays match the eager runs")
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    hev = HipTimingEvents()
+    stream = torch.cuda.current_stream().cuda_stream
 
     def step(i, timed):
         marks = {}
         for name, fn, ncp, pick, _ in plan:
             cp = pick(args.warmup + i if timed else i)
-            a = ev()
-            b = ev()
-            a.record()
+            a = hev.new()
+            b = hev.new()
+            hev.record(a, stream)
             if args.graphs:
                 graphs[(name, cp)].replay()
             else:
                 fn(cp)
-            b.record()
+            hev.record(b, stream)
             marks[name] = (a, b)
         return marks
 
@@ -250,7 +299,8 @@ def main():
     ms_per_step = total_ms / args.steps
     seg = {}
     for name in all_marks[0]:
-        seg[name] = sum(m[name][0].elapsed_time(m[name][1]) for m in all_marks) / args.steps
+        seg[name] = sum(hev.elapsed_ms(m[name][0], m[name][1]) for m in all_marks) / args.steps
+    hev.close()
     gemv_launches = args.steps if "decode_b1" in seg else 0   # one batched launch per step
     gemv_ms = seg.get("decode_b1", 0.0) * args.steps
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step; segments (ms): "
