@@ -16,9 +16,12 @@
 //               then h = bf16(silu(s_g Wg x) * (s_u Wu x));
 //   4. down     per (chunk, four 64-row tiles): d = s_d Wd h (fp32);
 //   5. scatter  y[t] = sum_j g[t][j] * d[pos(t, j)], j ascending.
-// Launch grids cover the work list's worst-case length; workgroups past its
-// actual length return at once.  A chunk's record holds everything a GEMM
-// workgroup needs, so its weight loads wait on one load only.
+// The expert GEMMs run on persistent grids (at most two workgroups per CU,
+// what fits at once) that walk the work list; its actual length is read on
+// the device.  A chunk's record holds everything a GEMM workgroup needs, so
+// its weight loads wait on one load only.
+#include <atomic>
+
 #include "device_common.h"
 #include "launchers.h"
 #include "skinny_core.h"
@@ -341,120 +344,128 @@ __device__ __forceinline__ void store_partials(float* red, int wave, int lane, c
 // h = bf16(silu(s_g Wg x) * (s_u Wu x)) for the tile's 64 rows.
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void gate_up_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ chunks, const int32_t* __restrict__ n_chunks,
-    int hidden, int inter, const uint8_t* __restrict__ w_gate, const uint8_t* __restrict__ w_up,
+    int max_chunks, int hidden, int inter, const uint8_t* __restrict__ w_gate, const uint8_t* __restrict__ w_up,
     size_t stride_gate, size_t stride_up, const float* __restrict__ scale_gate, const float* __restrict__ scale_up,
     uint16_t* __restrict__ h, float* __restrict__ dbg_gate, float* __restrict__ dbg_up) {
   constexpr int KS = 4;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kExpertLds];
   const int nrt = (inter + 63) / 64;
-  const int jc = blockIdx.x / nrt;
-  const int rt = blockIdx.x % nrt;
-  // The record is loaded together with the count (it lies inside the list
-  // for every launched workgroup).
-  const int32_t* rec = chunks + (size_t)jc * kChunkInts;
-  const int nch = *n_chunks;
-  const int e = rec[0], p0 = rec[1], rows = rec[2];
-  if (jc >= nch) return;
   const int nkt = (hidden + 255) / 256;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int slot = wave % KS;
-  const uint8_t* wrow = (wave >= KS ? w_up + e * stride_up : w_gate + e * stride_gate) + (size_t)rt * nkt * kTileBytes;
-  const uint16_t* xrow[2];
+  const int nch = *n_chunks;
+  for (int item = blockIdx.x;; item += gridDim.x) {
+    const int jc = item / nrt;
+    const int rt = item % nrt;
+    // The record's loads do not wait for the count: its index is clamped
+    // into the list's allocation.
+    const int32_t* rec = chunks + (size_t)(jc < max_chunks ? jc : max_chunks - 1) * kChunkInts;
+    const int e = rec[0], p0 = rec[1], rows = rec[2];
+    if (jc >= nch) break;
+    const uint8_t* wrow =
+        (wave >= KS ? w_up + e * stride_up : w_gate + e * stride_gate) + (size_t)rt * nkt * kTileBytes;
+    const uint16_t* xrow[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) xrow[j] = x + (int64_t)rec[4 + 4 * wave + 2 * j + (lane >> 5)] * hidden;
-  f32x16 acc_a = {}, acc_b = {};
-  expert_rounds<KS>(wrow, nkt, hidden, slot, xrow, wave, lane, lds, acc_a, acc_b);
-  float* red = reinterpret_cast<float*>(lds);
-  store_partials(red, wave, lane, acc_a, acc_b);
-  __syncthreads();
-  // Thread t: accumulator elements i0 + 8 q (i0 = t / 64) of lane t % 64, gate and up.
-  const int l = threadIdx.x & 63, i0 = threadIdx.x >> 6;
-  const int slots = nkt < KS ? nkt : KS;
-  const float sg = scale_gate[e], su = scale_up[e];
-  const int tok = l & 31;
-  if (tok >= rows) return;
+    for (int j = 0; j < 2; ++j) xrow[j] = x + (int64_t)rec[4 + 4 * wave + 2 * j + (lane >> 5)] * hidden;
+    f32x16 acc_a = {}, acc_b = {};
+    expert_rounds<KS>(wrow, nkt, hidden, slot, xrow, wave, lane, lds, acc_a, acc_b);
+    float* red = reinterpret_cast<float*>(lds);
+    store_partials(red, wave, lane, acc_a, acc_b);
+    __syncthreads();
+    // Thread t: accumulator elements i0 + 8 q (i0 = t / 64) of lane t % 64, gate and up.
+    const int l = threadIdx.x & 63, i0 = threadIdx.x >> 6;
+    const int slots = nkt < KS ? nkt : KS;
+    const float sg = scale_gate[e], su = scale_up[e];
+    const int tok = l & 31;
+    if (tok < rows) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int i = i0 + 8 * q;
-    float g = 0.0f, u = 0.0f;
-    for (int sl = 0; sl < slots; ++sl) {
-      g += red[(32 * sl + i) * 64 + l];
-      u += red[(32 * (KS + sl) + i) * 64 + l];
+      for (int q = 0; q < 4; ++q) {
+        const int i = i0 + 8 * q;
+        float g = 0.0f, u = 0.0f;
+        for (int sl = 0; sl < slots; ++sl) {
+          g += red[(32 * sl + i) * 64 + l];
+          u += red[(32 * (KS + sl) + i) * 64 + l];
+        }
+        const int row = rt * 64 + acc_row(i >> 4, i & 15, l);
+        if (row < inter) {
+          const int64_t at = (int64_t)(p0 + tok) * inter + row;
+          const float gv = g * sg, uv = u * su;
+          h[at] = to_bf16((gv / (1.0f + expf(-gv))) * uv);
+          if (dbg_gate) dbg_gate[at] = gv;
+          if (dbg_up) dbg_up[at] = uv;
+        }
+      }
     }
-    const int row = rt * 64 + acc_row(i >> 4, i & 15, l);
-    if (row < inter) {
-      const int64_t at = (int64_t)(p0 + tok) * inter + row;
-      const float gv = g * sg, uv = u * su;
-      h[at] = to_bf16((gv / (1.0f + expf(-gv))) * uv);
-      if (dbg_gate) dbg_gate[at] = gv;
-      if (dbg_up) dbg_up[at] = uv;
-    }
+    __syncthreads();  // the sums are read before the next item stages into the LDS
   }
 }
 
 // a7: down.  Workgroup (chunk, row tiles 4 q .. 4 q + 3): wavefront w takes
 // row tile 4 q + w / 2 at k slot w % 2; d = s_d Wd h (fp32) for those rows.
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void down_kernel(const uint16_t* __restrict__ hin,
-                                                      const int32_t* __restrict__ chunks,
-                                                      const int32_t* __restrict__ n_chunks, int hidden, int inter,
-                                                      const uint8_t* __restrict__ w_down, size_t stride_down,
-                                                      const float* __restrict__ scale_down, float* __restrict__ d) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void down_kernel(
+    const uint16_t* __restrict__ hin, const int32_t* __restrict__ chunks, const int32_t* __restrict__ n_chunks,
+    int max_chunks, int hidden, int inter, const uint8_t* __restrict__ w_down, size_t stride_down,
+    const float* __restrict__ scale_down, float* __restrict__ d) {
   constexpr int KS = 2;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kExpertLds];
   const int nrt = (hidden + 63) / 64;
   const int ngrp = (nrt + 3) / 4;
-  const int jc = blockIdx.x / ngrp;
-  const int grp = blockIdx.x % ngrp;
-  const int32_t* rec = chunks + (size_t)jc * kChunkInts;
-  const int nch = *n_chunks;
-  const int e = rec[0], p0 = rec[1], rows = rec[2];
-  if (jc >= nch) return;
   const int nkt = (inter + 255) / 256;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int slot = wave % KS;
-  const int rt = 4 * grp + wave / KS;
-  const bool has_rows = rt < nrt;
-  const uint8_t* wrow = has_rows ? w_down + e * stride_down + (size_t)rt * nkt * kTileBytes : nullptr;
-  // The chunk's rows of h are contiguous (the last repeated past the end).
-  const uint16_t* xrow[2];
+  const int nch = *n_chunks;
+  for (int item = blockIdx.x;; item += gridDim.x) {
+    const int jc = item / ngrp;
+    const int grp = item % ngrp;
+    const int32_t* rec = chunks + (size_t)(jc < max_chunks ? jc : max_chunks - 1) * kChunkInts;
+    const int e = rec[0], p0 = rec[1], rows = rec[2];
+    if (jc >= nch) break;
+    const int rt = 4 * grp + wave / KS;
+    const bool has_rows = rt < nrt;
+    const uint8_t* wrow = has_rows ? w_down + e * stride_down + (size_t)rt * nkt * kTileBytes : nullptr;
+    // The chunk's rows of h are contiguous (the last repeated past the end).
+    const uint16_t* xrow[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int srow = 4 * wave + 2 * j + (lane >> 5);
-    xrow[j] = hin + (int64_t)(p0 + (srow < rows ? srow : rows - 1)) * inter;
-  }
-  f32x16 acc_a = {}, acc_b = {};
-  expert_rounds<KS>(wrow, nkt, inter, slot, xrow, wave, lane, lds, acc_a, acc_b);
-  float* red = reinterpret_cast<float*>(lds);
-  store_partials(red, wave, lane, acc_a, acc_b);
-  __syncthreads();
-  // The slot-0 wavefront of each row tile adds its tile's slots in order.
-  const int tok = lane & 31;
-  if (slot != 0 || !has_rows || tok >= rows) return;
-  const int slots = nkt < KS ? nkt : KS;
-  const float sd = scale_down[e];
-  float* drow = d + (int64_t)(p0 + tok) * hidden;
+    for (int j = 0; j < 2; ++j) {
+      const int srow = 4 * wave + 2 * j + (lane >> 5);
+      xrow[j] = hin + (int64_t)(p0 + (srow < rows ? srow : rows - 1)) * inter;
+    }
+    f32x16 acc_a = {}, acc_b = {};
+    expert_rounds<KS>(wrow, nkt, inter, slot, xrow, wave, lane, lds, acc_a, acc_b);
+    float* red = reinterpret_cast<float*>(lds);
+    store_partials(red, wave, lane, acc_a, acc_b);
+    __syncthreads();
+    // The slot-0 wavefront of each row tile adds its tile's slots in order.
+    const int tok = lane & 31;
+    if (slot == 0 && has_rows && tok < rows) {
+      const int slots = nkt < KS ? nkt : KS;
+      const float sd = scale_down[e];
+      float* drow = d + (int64_t)(p0 + tok) * hidden;
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
+      for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      float v[4];
+        for (int e4 = 0; e4 < 4; ++e4) {
+          float v[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int i = 16 * hh + 4 * e4 + c;
-        float acc = 0.0f;
-        for (int sl = 0; sl < slots; ++sl) acc += red[(32 * (wave + sl) + i) * 64 + lane];
-        v[c] = acc * sd;
-      }
-      const int row = rt * 64 + acc_row(hh, 4 * e4, lane);
-      if (row + 4 <= hidden) {
-        *reinterpret_cast<f32x4*>(drow + row) = f32x4{v[0], v[1], v[2], v[3]};
-      } else {
-        for (int c = 0; c < 4; ++c)
-          if (row + c < hidden) drow[row + c] = v[c];
+          for (int c = 0; c < 4; ++c) {
+            const int i = 16 * hh + 4 * e4 + c;
+            float acc = 0.0f;
+            for (int sl = 0; sl < slots; ++sl) acc += red[(32 * (wave + sl) + i) * 64 + lane];
+            v[c] = acc * sd;
+          }
+          const int row = rt * 64 + acc_row(hh, 4 * e4, lane);
+          if (row + 4 <= hidden) {
+            *reinterpret_cast<f32x4*>(drow + row) = f32x4{v[0], v[1], v[2], v[3]};
+          } else {
+            for (int c = 0; c < 4; ++c)
+              if (row + c < hidden) drow[row + c] = v[c];
+          }
+        }
       }
     }
+    __syncthreads();  // the sums are read before the next item stages into the LDS
   }
 }
 
@@ -475,6 +486,19 @@ __global__ __launch_bounds__(256) void scatter_kernel(const float* __restrict__ 
 }
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Compute units of the current device (queried once per device).
+int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 // Upper bound on the work-list length: every active expert (at most
 // min(experts, tokens * top_k)) has one partial chunk, plus the full ones.
@@ -531,18 +555,24 @@ hipError_t launch_moe(const MoeLaunch& a, hipStream_t s) {
   hipLaunchKernelGGL(group_kernel, dim3(1), dim3(1024), 0, s, a.ids, (int)flat, (int)a.experts, (int)a.top_k,
                      a.counts, a.offsets, a.perm, w.pos, w.chunks, w.n_chunks);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  // Expert GEMM grids cover the work list's bound; workgroups past its
-  // length return at once.
+  // The expert GEMMs run on persistent grids of at most two workgroups per
+  // CU (what fits at once), which walk the work list's items (chunk, output
+  // rows) with a stride; the list's actual length is read on the device.
   const int64_t mch = max_chunks(a.tokens, a.experts, a.top_k);
+  const int64_t resident = 2 * (int64_t)cu_count();
   const int64_t nrt_i = (a.inter + 63) / 64;
-  hipLaunchKernelGGL(gate_up_kernel, dim3((unsigned)(mch * nrt_i)), dim3(64 * kExpertWaves), 0, s, a.x, w.chunks, w.n_chunks,
-                     (int)a.hidden, (int)a.inter, a.w_gate, a.w_up, a.stride_gate, a.stride_up, a.scale_gate,
-                     a.scale_up, w.h, a.dbg_gate, a.dbg_up);
+  const int64_t gu_items = mch * nrt_i;
+  hipLaunchKernelGGL(gate_up_kernel, dim3((unsigned)(gu_items < resident ? gu_items : resident)),
+                     dim3(64 * kExpertWaves), 0, s, a.x, w.chunks, w.n_chunks, (int)mch, (int)a.hidden, (int)a.inter,
+                     a.w_gate, a.w_up, a.stride_gate, a.stride_up, a.scale_gate, a.scale_up, w.h, a.dbg_gate,
+                     a.dbg_up);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const int64_t grp_h = ((a.hidden + 63) / 64 + 3) / 4;
+  const int64_t dn_items = mch * grp_h;
   float* d = a.dbg_down ? a.dbg_down : w.d;
-  hipLaunchKernelGGL(down_kernel, dim3((unsigned)(mch * grp_h)), dim3(64 * kExpertWaves), 0, s, w.h, w.chunks, w.n_chunks,
-                     (int)a.hidden, (int)a.inter, a.w_down, a.stride_down, a.scale_down, d);
+  hipLaunchKernelGGL(down_kernel, dim3((unsigned)(dn_items < resident ? dn_items : resident)),
+                     dim3(64 * kExpertWaves), 0, s, w.h, w.chunks, w.n_chunks, (int)mch, (int)a.hidden,
+                     (int)a.inter, a.w_down, a.stride_down, a.scale_down, d);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const int64_t outs = a.tokens * a.hidden;
   hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, s, d, a.g, w.pos, a.tokens,
