@@ -93,6 +93,11 @@ def test_shape_and_pointer_validation(L):
     need = B.gemm_workspace_bytes(32, 5120, 17408)
     assert need > 0
     assert L.nvfp4_gemm(A, 5120, 17408, 1.0, A, 32, 17408, A, 5120, 1, A, need - 16, None) == B.NVFP4_ERR_WORKSPACE
+    # One row past the largest n a product call takes (65536 row tiles of 64).
+    big = 4194304 + 1
+    assert L.nvfp4_gemv(A, big, 1280, 1.0, A, A, A, 1 << 40, None) == B.NVFP4_ERR_SHAPE
+    assert L.nvfp4_gemm(A, big, 1280, 1.0, A, 32, 1280, A, big, 1, A, 1 << 40, None) == B.NVFP4_ERR_SHAPE
+    assert L.nvfp4_gemm(A, big, 256, 1.0, A, 64, 256, A, big, 1, A, 1 << 40, None) == B.NVFP4_ERR_SHAPE
 
 
 def moe_template(**over):
@@ -110,6 +115,8 @@ def moe_template(**over):
     (dict(top_k=513), B.NVFP4_ERR_ARG),
     (dict(top_k=65, experts=100), B.NVFP4_ERR_ARG),
     (dict(experts=4096), B.NVFP4_ERR_ARG),
+    (dict(experts=2049), B.NVFP4_ERR_ARG),       # one past the largest expert count
+    (dict(top_k=65, experts=2048), B.NVFP4_ERR_ARG),
     (dict(hidden=2040), B.NVFP4_ERR_SHAPE),
     (dict(inter=-16), B.NVFP4_ERR_SHAPE),
     (dict(tokens=-1), B.NVFP4_ERR_SHAPE),

@@ -133,6 +133,7 @@ def small_weights(seed, e, hidden, inter):
     (130, 16, 8, 128, 32),   # tokens * top_k > 1024: separate routing and grouping launches
     (4, 1100, 2, 128, 32),   # more than 1024 experts: separate launches, 32 logits per lane
     (1536, 6, 4, 1024, 384),  # more work-list items than the persistent expert-GEMM grids hold
+    (3, 2048, 64, 128, 32),   # the largest expert count and top-k the layer takes
 ])
 def test_moe_small(t, e, k, hidden, inter):
     w = small_weights(50 + e, e, hidden, inter)
