@@ -198,6 +198,7 @@ __device__ __forceinline__ void group_body(const int32_t* ids, int total, int ex
   __shared__ int s_off[kMaxExperts];
   __shared__ int s_run[kMaxExperts];
   __shared__ int s_chb[kMaxExperts];
+  __shared__ int s_last[kMaxExperts];  // token of each expert's last row
   __shared__ int s_tmp[64];
   const int tid = threadIdx.x;
   for (int e = tid; e < experts; e += 1024) { s_cnt[e] = 0; s_run[e] = 0; }
@@ -245,6 +246,7 @@ __device__ __forceinline__ void group_body(const int32_t* ids, int total, int ex
         perm[p] = f;
         pos[f] = p;
         chunks[(size_t)(s_chb[e] + r / kChunkRows) * kChunkInts + 4 + r % kChunkRows] = f / top_k;
+        if (r == s_cnt[e] - 1) s_last[e] = f / top_k;
       }
       __syncthreads();
       if (wave == w && e >= 0 && rank_w == 0) s_run[e] += cnt_w;
@@ -262,7 +264,7 @@ __device__ __forceinline__ void group_body(const int32_t* ids, int total, int ex
       r[2] = rows;
       r[3] = 0;
       if (rows < kChunkRows) {
-        const int tok = r[4 + rows - 1];  // written above by this workgroup
+        const int tok = s_last[e];
         for (int q = rows; q < kChunkRows; ++q) r[4 + q] = tok;
       }
     }
@@ -355,9 +357,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
   const int lane = threadIdx.x & 63;
   const int slot = wave % KS;
   const int nch = *n_chunks;
-  for (int item = blockIdx.x;; item += gridDim.x) {
-    const int jc = item / nrt;
-    const int rt = item % nrt;
+  for (int64_t item = blockIdx.x;; item += gridDim.x) {
+    const int64_t jq = item / nrt;
+    const int jc = jq < max_chunks ? (int)jq : max_chunks;  // max_chunks: past the list
+    const int rt = (int)(item % nrt);
     // The record's loads do not wait for the count: its index is clamped
     // into the list's allocation.
     const int32_t* rec = chunks + (size_t)(jc < max_chunks ? jc : max_chunks - 1) * kChunkInts;
@@ -416,9 +419,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void d
   const int lane = threadIdx.x & 63;
   const int slot = wave % KS;
   const int nch = *n_chunks;
-  for (int item = blockIdx.x;; item += gridDim.x) {
-    const int jc = item / ngrp;
-    const int grp = item % ngrp;
+  for (int64_t item = blockIdx.x;; item += gridDim.x) {
+    const int64_t jq = item / ngrp;
+    const int jc = jq < max_chunks ? (int)jq : max_chunks;  // max_chunks: past the list
+    const int grp = (int)(item % ngrp);
     const int32_t* rec = chunks + (size_t)(jc < max_chunks ? jc : max_chunks - 1) * kChunkInts;
     const int e = rec[0], p0 = rec[1], rows = rec[2];
     if (jc >= nch) break;
