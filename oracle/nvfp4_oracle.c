@@ -247,3 +247,100 @@ int nvo_max_threads(void) {
   return 1;
 #endif
 }
+
+/* ---- NVFP4 quantiser: weights -> codes, block scales, tensor scale ----------
+ *
+ * The step before the repack: the imp README ("How does it work?") keeps
+ * weights in NVFP4 and converts them once; the pages do not spell out the
+ * encoder.  The readings taken (each listed in the design notes):
+ *   - the per-tensor scale maps the matrix's largest magnitude amax onto the
+ *     largest value the two levels hold, 6 (E2M1) times 448 (E4M3):
+ *     s_t = amax / 2688 as an fp32 division, and 1 for an all-zero matrix;
+ *   - block b's scale byte is the E4M3FN value nearest to amax_b / (6 s_t)
+ *     (amax_b: the block's largest magnitude), ties going to the even
+ *     mantissa; above 448 the nearest value is 448;
+ *   - element w's code: the E2M1 magnitude nearest to |w| / (e4m3(scale_b) s_t),
+ *     ties to the even mantissa, values above 6 giving 6; the code's sign bit
+ *     is w's sign bit; a block whose scale byte is 0 gets code 0 throughout;
+ *   - these quotients and products are single-precision operations, in the
+ *     order written: the integer decisions are taken in fp32, the precision
+ *     the GPU encoder works in.  Inputs are finite.
+ * The rounding is written as a search for the nearest table value (plain and
+ * slow, on purpose).
+ */
+
+/* Nearest non-negative finite E4M3FN byte (0x00..0x7E) to q >= 0; ties to the
+ * even byte (the byte's low bit is the mantissa's). */
+static uint32_t e4m3_nearest(float q) {
+  uint32_t best = 0;
+  double bd = fabs((double)q);
+  for (uint32_t b = 1; b <= 0x7Eu; ++b) {
+    const double d = fabs((double)q - nvo_e4m3(b));
+    if (d < bd || (d == bd && (b & 1u) == 0u)) {
+      best = b;
+      bd = d;
+    }
+  }
+  return best;
+}
+
+/* Nearest E2M1 magnitude code (0..7) to a >= 0; ties to the even code. */
+static uint32_t e2m1_nearest(float a) {
+  uint32_t best = 0;
+  double bd = fabs((double)a);
+  for (uint32_t c = 1; c < 8u; ++c) {
+    const double d = fabs((double)a - kE2M1Magnitude[c]);
+    if (d < bd || (d == bd && (c & 1u) == 0u)) {
+      best = c;
+      bd = d;
+    }
+  }
+  return best;
+}
+
+static float input_value(const void* w, int bf16, int64_t i) {
+  if (bf16) return (float)nvo_bf16(((const uint16_t*)w)[i]);
+  return ((const float*)w)[i];
+}
+
+/* The per-tensor scale of an [n][k] matrix (row stride ldw elements);
+ * bf16 != 0: bf16 bit patterns, else fp32. */
+float nvo_tensor_scale(const void* w, int bf16, int64_t n, int64_t k, int64_t ldw) {
+  float amax = 0.0f;
+  for (int64_t r = 0; r < n; ++r)
+    for (int64_t c = 0; c < k; ++c) {
+      const float a = fabsf(input_value(w, bf16, r * ldw + c));
+      if (a > amax) amax = a;
+    }
+  return amax > 0.0f ? amax / 2688.0f : 1.0f;
+}
+
+/* Codes [n][k/2] (element 2i in the low nibble of byte i) and scales [n][k/16]
+ * of an [n][k] matrix under tensor scale st. */
+void nvo_quantize(const void* w, int bf16, int64_t n, int64_t k, int64_t ldw, float st, uint8_t* codes,
+                  uint8_t* scales) {
+  const float six_st = 6.0f * st;
+  for (int64_t r = 0; r < n; ++r)
+    for (int64_t b = 0; b < k / 16; ++b) {
+      float v[16];
+      float amax = 0.0f;
+      for (int i = 0; i < 16; ++i) {
+        v[i] = input_value(w, bf16, r * ldw + 16 * b + i);
+        if (fabsf(v[i]) > amax) amax = fabsf(v[i]);
+      }
+      const float q = amax / six_st;
+      const uint32_t sb = e4m3_nearest(q);
+      scales[r * (k / 16) + b] = (uint8_t)sb;
+      const float d = (float)nvo_e4m3(sb) * st;
+      for (int i = 0; i < 16; ++i) {
+        uint32_t c = 0;
+        if (sb != 0u) {
+          const float rq = v[i] / d;
+          c = e2m1_nearest(fabsf(rq)) | (signbit(v[i]) ? 8u : 0u);
+        }
+        uint8_t* byte = codes + r * (k / 2) + 8 * b + i / 2;
+        if (i % 2 == 0) *byte = (uint8_t)c;
+        else *byte = (uint8_t)(*byte | (c << 4));
+      }
+    }
+}

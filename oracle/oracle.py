@@ -50,6 +50,10 @@ def _load():
     lib.nvo_group.argtypes = [P, i64, i64, i64, P, P, P, P]
     lib.nvo_moe.restype = None
     lib.nvo_moe.argtypes = [P, P, P, P, P, P, P, P, P, P, P, i64, i64, i64, i64, i64, P, P, P, P, ctypes.c_int]
+    lib.nvo_tensor_scale.restype = ctypes.c_float
+    lib.nvo_tensor_scale.argtypes = [P, ctypes.c_int, i64, i64, i64]
+    lib.nvo_quantize.restype = None
+    lib.nvo_quantize.argtypes = [P, ctypes.c_int, i64, i64, i64, ctypes.c_float, P, P]
     lib.nvo_max_threads.restype = ctypes.c_int
     lib.nvo_max_threads.argtypes = []
     _lib = lib
@@ -196,3 +200,23 @@ def moe(gate, up, down, x_bits, logits, top_k, nthreads=None):
                     t, e, top_k, hidden, inter, _ptr(ids), _ptr(g), _ptr(y), _ptr(yb),
                     _threads(nthreads))
     return ids, g, y, yb
+
+
+def quantize(w, tensor_scale=None, bf16=None):
+    """NVFP4-encode an [N][K] matrix: returns (codes [N][K/2] u8, scales [N][K/16] u8, s_t float32).
+
+    w: float32 values, or uint16 bf16 bit patterns (bf16 defaults to w's dtype
+    being uint16).  tensor_scale: use this s_t instead of the matrix's own.
+    """
+    if bf16 is None:
+        bf16 = np.asarray(w).dtype == np.uint16
+    w = _c(w, np.uint16 if bf16 else np.float32)
+    n, k = w.shape
+    assert k % 16 == 0
+    lib = _load()
+    st = np.float32(lib.nvo_tensor_scale(_ptr(w), int(bf16), n, k, k)) if tensor_scale is None \
+        else np.float32(tensor_scale)
+    codes = np.zeros((n, k // 2), dtype=np.uint8)
+    scales = np.zeros((n, k // 16), dtype=np.uint8)
+    lib.nvo_quantize(_ptr(w), int(bf16), n, k, k, float(st), _ptr(codes), _ptr(scales))
+    return codes, scales, st
