@@ -27,7 +27,8 @@ EXPORTED = (
     "nvfp4_abi_version", "nvfp4_status_str", "nvfp4_last_error", "nvfp4_packed_bytes", "nvfp4_pack",
     "nvfp4_unpack", "nvfp4_gemv_workspace_bytes", "nvfp4_gemv", "nvfp4_gemm_workspace_bytes", "nvfp4_gemm",
     "nvfp4_gemv_batched_workspace_bytes", "nvfp4_gemv_batched", "nvfp4_gemm_batched_workspace_bytes",
-    "nvfp4_gemm_batched", "nvfp4_moe_workspace_bytes", "nvfp4_moe_grouped",
+    "nvfp4_gemm_batched", "nvfp4_moe_workspace_bytes", "nvfp4_moe_grouped", "nvfp4_quantize_workspace_bytes",
+    "nvfp4_quantize",
 )
 
 
@@ -93,6 +94,8 @@ def lib():
         "nvfp4_gemm_batched": (I, [ctypes.POINTER(Problem), I, i64, I, P, sz, P]),
         "nvfp4_moe_workspace_bytes": (I, [ctypes.POINTER(MoeArgs), ctypes.POINTER(sz)]),
         "nvfp4_moe_grouped": (I, [ctypes.POINTER(MoeArgs), P]),
+        "nvfp4_quantize_workspace_bytes": (I, [ctypes.POINTER(sz)]),
+        "nvfp4_quantize": (I, [P, I, i64, i64, i64, P, P, P, P, sz, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -153,6 +156,31 @@ def pack(codes, scales, stream=None):
     packed = torch.empty(packed_bytes(n, k), dtype=torch.uint8, device=codes.device)
     check(lib().nvfp4_pack(_ptr(codes), _ptr(scales), n, k, _ptr(packed), _stream(stream)))
     return packed
+
+
+def quantize_workspace_bytes():
+    out = ctypes.c_size_t()
+    check(lib().nvfp4_quantize_workspace_bytes(ctypes.byref(out)))
+    return out.value
+
+
+def quantize(w, codes=None, scales=None, tensor_scale=None, ws=None, stream=None):
+    """NVFP4-encode w (device, float32 or bfloat16, [n][k], rows may be strided):
+    returns (codes uint8 [n][k/2], scales uint8 [n][k/16], tensor_scale float32 [1])."""
+    n, k = w.shape
+    dtype = {torch.float32: NVFP4_F32, torch.bfloat16: NVFP4_BF16}[w.dtype]
+    dev = w.device
+    if codes is None:
+        codes = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((n, k // 16), dtype=torch.uint8, device=dev)
+    if tensor_scale is None:
+        tensor_scale = torch.empty(1, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(quantize_workspace_bytes(), dev, kind="quantize")
+    check(lib().nvfp4_quantize(_ptr(w), dtype, n, k, w.stride(0) if n > 0 else k, _ptr(codes), _ptr(scales),
+                               _ptr(tensor_scale), _ptr(ws), ws.numel(), _stream(stream)))
+    return codes, scales, tensor_scale
 
 
 def unpack(packed, n, k, stream=None):

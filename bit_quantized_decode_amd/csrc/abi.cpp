@@ -131,6 +131,37 @@ int nvfp4_gemv_workspace_bytes(int64_t n, int64_t k, size_t* bytes) {
   NVFP4_GUARD_END
 }
 
+int nvfp4_quantize_workspace_bytes(size_t* bytes) {
+  NVFP4_GUARD_BEGIN
+  if (!bytes) return fail(NVFP4_ERR_NULL, "bytes is NULL");
+  *bytes = nvfp4::quantize_workspace_bytes();
+  return ok();
+  NVFP4_GUARD_END
+}
+
+int nvfp4_quantize(const void* w, int w_dtype, int64_t n, int64_t k, int64_t ldw, uint8_t* codes, uint8_t* scales,
+                   float* tensor_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  NVFP4_GUARD_BEGIN
+  NVFP4_TRY(check_shape(n, k));
+  if (w_dtype != NVFP4_F32 && w_dtype != NVFP4_BF16) return fail(NVFP4_ERR_DTYPE, "w_dtype=%d unknown", w_dtype);
+  if (n == 0 || k == 0) return ok();
+  if (ldw < k || ldw % 8 != 0 || ldw > kMaxDim)
+    return fail(NVFP4_ERR_SHAPE, "ldw=%lld must be >= k=%lld, a multiple of 8 and at most 2^30", (long long)ldw,
+                (long long)k);
+  if (!w || !codes || !scales || !tensor_scale)
+    return fail(NVFP4_ERR_NULL, "w, codes, scales and tensor_scale must be non-NULL");
+  if (!aligned16(w) || !aligned16(codes) || !aligned16(scales) || !aligned4(tensor_scale))
+    return fail(NVFP4_ERR_ALIGN, "w, codes and scales must be 16-byte aligned, tensor_scale 4-byte aligned");
+  const size_t need = nvfp4::quantize_workspace_bytes();
+  if (!workspace || workspace_bytes < need)
+    return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace ? workspace_bytes : 0);
+  if (!aligned16(workspace)) return fail(NVFP4_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return hip_status(nvfp4::launch_quantize(w, w_dtype == NVFP4_BF16, n, k, ldw, codes, scales, tensor_scale,
+                                           workspace, (hipStream_t)stream),
+                    "quantize launch");
+  NVFP4_GUARD_END
+}
+
 int nvfp4_gemv(const void* packed, int64_t n, int64_t k, float tensor_scale, const uint16_t* x, float* y,
                void* workspace, size_t workspace_bytes, void* stream) {
   NVFP4_GUARD_BEGIN

@@ -69,6 +69,9 @@ hipError_t launch_pack(const uint8_t* codes, const uint8_t* scales, const Geomet
 hipError_t launch_unpack(const void* packed, const Geometry& g, uint8_t* codes, uint8_t* scales,
                          hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+size_t quantize_workspace_bytes();
+hipError_t launch_quantize(const void* w, bool bf16, int64_t n, int64_t k, int64_t ldw, uint8_t* codes,
+                           uint8_t* scales, float* tensor_scale, void* ws, hipStream_t s);
 hipError_t launch_gemv(const void* packed, const Geometry& g, float st, const uint16_t* x, float* y,
                        void* ws, hipStream_t s);
 hipError_t launch_skinny(const void* packed, const Geometry& g, float st, const uint16_t* x, int64_t m,

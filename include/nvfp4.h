@@ -109,6 +109,30 @@ int nvfp4_pack(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k
 int nvfp4_unpack(const void* packed, int64_t n, int64_t k, uint8_t* codes, uint8_t* scales,
                  void* stream);
 
+/* ---- f1: quantiser (the step before nvfp4_pack) ---------------------------------
+ * Encodes an [n][k] weight matrix, fp32 or bf16 (w_dtype), rows ldw elements
+ * apart, as canonical NVFP4: codes [n][k/2], scales [n][k/16] (the layouts
+ * nvfp4_pack() reads) and one fp32 per-tensor scale written to *tensor_scale
+ * (device memory).  The pages keep weights in NVFP4 and convert them once
+ * (imp README, "How does it work?"); they leave the encoder open.  This one:
+ *   s_t      = amax / 2688  (amax: the largest |w|; 6 * 448 = 2688 puts it on the
+ *              largest E2M1 value times the largest E4M3 value; 1 if all zero)
+ *   scale_b  = E4M3FN nearest to amax_b / (6 * s_t)   (amax_b: block b's largest |w|)
+ *   code     = E2M1 nearest to |w| / (e4m3(scale_b) * s_t), sign bit = w's sign bit
+ * Nearest means ties to an even mantissa, saturating at 448 and 6; a block
+ * whose scale is 0 gets code 0 throughout.  Every quotient and product is a
+ * single-precision operation in the order shown, so results are bit-exact and
+ * deterministic.  Inputs must be finite (NaN or infinity give unspecified
+ * bytes).  n >= 0, k % 16 == 0, ldw >= k and ldw % 8 == 0; w, codes, scales
+ * 16-byte aligned, tensor_scale 4-byte aligned; workspace: at least
+ * nvfp4_quantize_workspace_bytes() bytes, 16-byte aligned, no initial contents
+ * required.  n == 0 or k == 0 is a no-op (nothing written).
+ */
+int nvfp4_quantize_workspace_bytes(size_t* bytes /* host */);
+int nvfp4_quantize(const void* w, int w_dtype, int64_t n, int64_t k, int64_t ldw, uint8_t* codes,
+                   uint8_t* scales, float* tensor_scale, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
 /* ---- a2: GEMV, one activation vector ----------------------------------------
  * y[j] = s_t * sum_k e2m1(c[j][k]) * e4m3(sigma[j][k/16]) * x[k],   j < n.
  * x: bf16 bit patterns [k];  y: float32 [n].

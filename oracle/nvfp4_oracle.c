@@ -316,10 +316,11 @@ float nvo_tensor_scale(const void* w, int bf16, int64_t n, int64_t k, int64_t ld
 }
 
 /* Codes [n][k/2] (element 2i in the low nibble of byte i) and scales [n][k/16]
- * of an [n][k] matrix under tensor scale st. */
+ * of an [n][k] matrix under tensor scale st (OpenMP over rows). */
 void nvo_quantize(const void* w, int bf16, int64_t n, int64_t k, int64_t ldw, float st, uint8_t* codes,
                   uint8_t* scales) {
   const float six_st = 6.0f * st;
+#pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < n; ++r)
     for (int64_t b = 0; b < k / 16; ++b) {
       float v[16];

@@ -28,7 +28,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     assert set(names) == set(B.EXPORTED)
     for name in names:
         assert hasattr(L, name), name
@@ -98,6 +98,26 @@ def test_shape_and_pointer_validation(L):
     assert L.nvfp4_gemv(A, big, 1280, 1.0, A, A, A, 1 << 40, None) == B.NVFP4_ERR_SHAPE
     assert L.nvfp4_gemm(A, big, 1280, 1.0, A, 32, 1280, A, big, 1, A, 1 << 40, None) == B.NVFP4_ERR_SHAPE
     assert L.nvfp4_gemm(A, big, 256, 1.0, A, 64, 256, A, big, 1, A, 1 << 40, None) == B.NVFP4_ERR_SHAPE
+
+
+def test_quantize_validation(L):
+    A, M = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x10008)
+    T = ctypes.c_void_p(0x10004)                 # 4-byte aligned (the tensor scale's requirement)
+    need = B.quantize_workspace_bytes()
+    assert need >= 4
+    q = L.nvfp4_quantize
+    assert q(A, B.NVFP4_BF16, 0, 64, 64, None, None, None, None, 0, None) == B.NVFP4_OK        # n = 0: no-op
+    assert q(A, B.NVFP4_BF16, 4, 0, 0, None, None, None, None, 0, None) == B.NVFP4_OK          # k = 0: no-op
+    assert q(A, 7, 4, 64, 64, A, A, T, A, need, None) == B.NVFP4_ERR_DTYPE
+    assert q(A, B.NVFP4_F32, 4, 40, 40, A, A, T, A, need, None) == B.NVFP4_ERR_SHAPE           # k % 16
+    assert q(A, B.NVFP4_F32, 4, 64, 60, A, A, T, A, need, None) == B.NVFP4_ERR_SHAPE           # ldw < k
+    assert q(A, B.NVFP4_F32, 4, 64, 68, A, A, T, A, need, None) == B.NVFP4_ERR_SHAPE           # ldw % 8
+    assert q(None, B.NVFP4_F32, 4, 64, 64, A, A, T, A, need, None) == B.NVFP4_ERR_NULL
+    assert q(A, B.NVFP4_F32, 4, 64, 64, A, A, None, A, need, None) == B.NVFP4_ERR_NULL
+    assert q(M, B.NVFP4_F32, 4, 64, 64, A, A, T, A, need, None) == B.NVFP4_ERR_ALIGN
+    assert q(A, B.NVFP4_F32, 4, 64, 64, A, A, ctypes.c_void_p(0x10002), A, need, None) == B.NVFP4_ERR_ALIGN
+    assert q(A, B.NVFP4_F32, 4, 64, 64, A, A, T, None, 0, None) == B.NVFP4_ERR_WORKSPACE
+    assert q(A, B.NVFP4_F32, 4, 64, 64, A, A, T, A, need - 1, None) == B.NVFP4_ERR_WORKSPACE
 
 
 def moe_template(**over):
