@@ -88,7 +88,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target length of the oracle sample")
-    p.add_argument("--rows", default="decode_b1,decode_b32,moe,prefill")
+    p.add_argument("--rows", default="decode_b1,decode_b32,moe,prefill",
+                   help="rows to run; \"quantize\" (the NVFP4 quantiser over the layer) is optional, not a default row")
     p.add_argument("--order", default="prefill,moe,decode_b32,decode_b1",
                    help="row order within a step (the batch-1 GEMV last: see the note at the plan)")
     p.add_argument("--graphs", action="store_true", help="replay per-row HIP graphs instead of direct launches")
@@ -226,6 +227,24 @@ def main():
     def row_pre(cp):
         pre_calls[cp]()
 
+    # ---- optional: the NVFP4 quantiser over the layer's five matrices (bf16 in) ----
+    q_w, q_out, q_bytes = [], [], 0
+    if "quantize" in rows:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1234)
+        ws_q = B.workspace(B.quantize_workspace_bytes(), dev, kind="quantize")
+        for m in layer:
+            w = (torch.randn((m.n, m.k), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+            q_w.append(w)
+            q_out.append((torch.empty((m.n, m.k // 2), dtype=torch.uint8, device=dev),
+                          torch.empty((m.n, m.k // 16), dtype=torch.uint8, device=dev),
+                          torch.empty(1, dtype=torch.float32, device=dev)))
+            q_bytes += m.n * m.k * 2 + m.n * m.k * 9 // 16 + 4   # bf16 read once, codes + scales + s_t written
+
+    def row_q(cp):
+        for w, (c, sc, st) in zip(q_w, q_out):
+            B.quantize(w, c, sc, st, ws=ws_q)
+
     # Row order within a step: the compute-bound prefill first, the decode
     # rows after the memory-bound MoE.  A sustained matrix-core burst lowers
     # the clocks for tens of microseconds, and a GEMV launched straight after
@@ -236,8 +255,10 @@ def main():
         "moe": ("moe", run_moe, 2, lambda i: i % 2, None),
         "decode_b32": ("decode_b32", row_b32, dense_copies, lambda i: (2 * i + 1) % dense_copies, y32),
         "decode_b1": ("decode_b1", row_b1, dense_copies, lambda i: (2 * i) % dense_copies, y1),
+        "quantize": ("quantize", row_q, 1, lambda i: 0, [c for c, _, _ in q_out]),
     }
-    plan = [plan_all[r] for r in args.order.split(",") if r in rows]   # (row name, callable(copy), copies, copy for step i, outputs)
+    order = args.order.split(",") + [r for r in plan_all if r not in args.order.split(",")]
+    plan = [plan_all[r] for r in order if r in rows]   # (row name, callable(copy), copies, copy for step i, outputs)
     # Eager reference outputs (copy 0), then (--graphs) capture.
     eager = {}
     for name, fn, ncp, _, outs in plan:
@@ -333,6 +354,12 @@ def main():
         result_rows["prefill"] = {"TFLOP/s": pre_flops / s / 1e12, "us": s * 1e6,
                                   "frac_mfma_bf16": pre_flops / s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                                   "GB/s": pre_bytes / s / 1e9, "equiv_tok_s": pre_flops / s / (2 * 27e9)}
+
+    if "quantize" in seg:
+        s = seg["quantize"] * 1e-3
+        result_rows["quantize"] = {"GB/s": q_bytes / s / 1e9, "us": s * 1e6, "algorithmic_bytes": q_bytes,
+                                   "frac_hbm": q_bytes / s / 1e9 / HBM_PEAK_GBS,
+                                   "weights_per_s": sum(m.n * m.k for m in layer) / s}
 
     roofline = None
     if gemv_launches:

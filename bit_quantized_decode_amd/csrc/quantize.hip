@@ -14,10 +14,9 @@
 // integer decision is taken in fp32.
 //
 // Two passes over the weights, both memory-bound (2 or 4 bytes read per
-// weight, then 0.5625 written): the matrix's largest magnitude (a wavefront
-// maximum, then one integer atomic maximum per wavefront -- non-negative
-// floats order as their bit patterns, so the result does not depend on
-// order), then one thread per 16-element block.
+// weight, then 0.5625 written): workgroup maxima of the magnitudes, then one
+// thread per 16-element block, each workgroup first taking the maximum of
+// those maxima (a maximum does not depend on order: deterministic).
 #include "device_common.h"
 #include "launchers.h"
 
@@ -89,32 +88,61 @@ __device__ __forceinline__ uint32_t e2m1_nearest(float a) {
 
 __device__ __forceinline__ float tensor_scale_of(float amax) { return amax > 0.0f ? amax / 2688.0f : 1.0f; }
 
-__global__ void amax_init_kernel(unsigned* __restrict__ amax) {
-  if (threadIdx.x == 0) amax[0] = 0u;
-}
+// At most one workgroup of 1024 threads per CU, each thread four blocks per
+// round (8 loads in flight); each workgroup writes its maximum to its own
+// word, and the quantising pass takes the maximum of those (no atomics, no
+// word to clear beforehand).
+constexpr int kAmaxThreads = 1024;
+constexpr int kAmaxUnroll = 4;
 
 template <bool BF16>
-__global__ __launch_bounds__(256) void amax_kernel(const void* __restrict__ w, int64_t n, int64_t k, int64_t ldw,
-                                                   unsigned* __restrict__ amax) {
+__global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const void* __restrict__ w, int64_t n, int64_t k,
+                                                            int64_t ldw, float* __restrict__ part_max) {
+  __shared__ float s_max[kAmaxThreads / 64];
   const int64_t bpr = k / 16, total = n * bpr;
+  const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
   float m = 0.0f;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = t / bpr, b = t - r * bpr;
-    float v[16];
-    load_block<BF16>(w, r * ldw + 16 * b, v);
-    m = fmaxf(m, block_amax(v));
+  for (int64_t t0 = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x; t0 < total; t0 += kAmaxUnroll * stride) {
+    float v[kAmaxUnroll][16];
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) {
+      const int64_t t = t0 + u * stride < total ? t0 + u * stride : t0;  // past the end: re-read block t0
+      const int64_t r = t / bpr, b = t - r * bpr;
+      load_block<BF16>(w, r * ldw + 16 * b, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) m = fmaxf(m, block_amax(v[u]));
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if ((threadIdx.x & 63) == 0 && m > 0.0f) atomicMax(amax, __float_as_uint(m));
+  if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    m = threadIdx.x < kAmaxThreads / 64 ? s_max[threadIdx.x] : 0.0f;
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if (threadIdx.x == 0) part_max[blockIdx.x] = m;
+  }
+}
+
+// The matrix's largest magnitude: the maximum of the `parts` workgroup maxima.
+__device__ __forceinline__ float matrix_amax(const float* __restrict__ part_max, int parts) {
+  __shared__ float s_red[4];
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < parts; i += blockDim.x) m = fmaxf(m, part_max[i]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  return fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
 }
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ w, int64_t n, int64_t k,
-                                                       int64_t ldw, const unsigned* __restrict__ amax,
+                                                       int64_t ldw, const float* __restrict__ part_max, int parts,
                                                        uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                                        float* __restrict__ st_out) {
-  const float st = tensor_scale_of(__uint_as_float(*amax));
+  const float st = tensor_scale_of(matrix_amax(part_max, parts));
   const float six_st = 6.0f * st;
   if (blockIdx.x == 0 && threadIdx.x == 0) st_out[0] = st;
   const int64_t bpr = k / 16, total = n * bpr;
@@ -138,28 +166,28 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
   }
 }
 
-unsigned grid_for(int64_t blocks16) {
-  const int64_t wgs = (blocks16 + 255) / 256;
-  return (unsigned)(wgs < 8192 ? (wgs > 0 ? wgs : 1) : 8192);
+unsigned grid_for(int64_t blocks16, int threads, int64_t cap) {
+  const int64_t wgs = (blocks16 + threads - 1) / threads;
+  return (unsigned)(wgs < cap ? (wgs > 0 ? wgs : 1) : cap);
 }
 
 }  // namespace
 
-size_t quantize_workspace_bytes() { return 256; }
+size_t quantize_workspace_bytes() { return 256 * sizeof(float); }
 
 hipError_t launch_quantize(const void* w, bool bf16, int64_t n, int64_t k, int64_t ldw, uint8_t* codes,
                            uint8_t* scales, float* tensor_scale, void* ws, hipStream_t s) {
-  unsigned* amax = static_cast<unsigned*>(ws);
-  const unsigned grid = grid_for(n * (k / 16));
-  hipLaunchKernelGGL(amax_init_kernel, dim3(1), dim3(64), 0, s, amax);
+  float* part_max = static_cast<float*>(ws);  // one word per amax workgroup (at most 256)
+  const int64_t blocks16 = n * (k / 16);
+  const unsigned ga = grid_for(blocks16, kAmaxThreads, 256), gq = grid_for(blocks16, 256, 8192);
   if (bf16) {
-    hipLaunchKernelGGL(amax_kernel<true>, dim3(grid), dim3(256), 0, s, w, n, k, ldw, amax);
-    hipLaunchKernelGGL(quantize_kernel<true>, dim3(grid), dim3(256), 0, s, w, n, k, ldw, amax, codes, scales,
-                       tensor_scale);
+    hipLaunchKernelGGL(amax_kernel<true>, dim3(ga), dim3(kAmaxThreads), 0, s, w, n, k, ldw, part_max);
+    hipLaunchKernelGGL(quantize_kernel<true>, dim3(gq), dim3(256), 0, s, w, n, k, ldw, part_max, (int)ga, codes,
+                       scales, tensor_scale);
   } else {
-    hipLaunchKernelGGL(amax_kernel<false>, dim3(grid), dim3(256), 0, s, w, n, k, ldw, amax);
-    hipLaunchKernelGGL(quantize_kernel<false>, dim3(grid), dim3(256), 0, s, w, n, k, ldw, amax, codes, scales,
-                       tensor_scale);
+    hipLaunchKernelGGL(amax_kernel<false>, dim3(ga), dim3(kAmaxThreads), 0, s, w, n, k, ldw, part_max);
+    hipLaunchKernelGGL(quantize_kernel<false>, dim3(gq), dim3(256), 0, s, w, n, k, ldw, part_max, (int)ga, codes,
+                       scales, tensor_scale);
   }
   return hipGetLastError();
 }
