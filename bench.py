@@ -89,7 +89,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target length of the oracle sample")
     p.add_argument("--rows", default="decode_b1,decode_b32,moe,prefill",
-                   help="rows to run; \"quantize\" (the NVFP4 quantiser over the layer) is optional, not a default row")
+                   help="rows to run; optional, not default: quantize (the NVFP4 quantiser over the layer), "
+                        "decode_m2 .. decode_m8 (the layer at decode widths 2..8), head_b1 (the output head, batch 1)")
     p.add_argument("--order", default="prefill,moe,decode_b32,decode_b1",
                    help="row order within a step (the batch-1 GEMV last: see the note at the plan)")
     p.add_argument("--graphs", action="store_true", help="replay per-row HIP graphs instead of direct launches")
@@ -212,6 +213,31 @@ def main():
     def row_b32(cp):
         b32_calls[cp]()
 
+    # ---- optional rows: decode widths 2..8 (the layer's five products in one
+    # batched launch, bf16 out) and the output head at batch 1 ----------------
+    extra_rows = {}
+    for r in sorted(rows):
+        if r.startswith("decode_m") and r[len("decode_m"):].isdigit():
+            mw = int(r[len("decode_m"):])
+            if not 2 <= mw <= 8:
+                raise SystemExit(f"{r}: decode widths 2..8 only (1 is decode_b1, 32 is decode_b32)")
+            xw = [bf16(I.activations(I.DECODE_WIDTHS, m.matrix_id, mw, m.k)) for m in layer]
+            yw = [torch.empty((mw, m.n), dtype=torch.bfloat16, device=dev) for m in layer]
+            calls = [B.gemm_batched_prepared([(packed[cp][j], m.n, m.k, I.TENSOR_SCALE, xw[j], yw[j])
+                                              for j, m in enumerate(layer)], ws=ws_split)
+                     for cp in range(dense_copies)]
+            wbytes = sum(m.n * m.k * 9 // 16 + 2 * mw * m.k + 2 * mw * m.n for m in layer)
+            extra_rows[r] = (calls, dense_copies, yw, wbytes, 2.0 * mw * sum(m.n * m.k for m in layer))
+    if "head_b1" in rows:
+        hc, hs = I.nvfp4_matrix(I.OUTPUT_HEAD, I.HEAD.matrix_id, I.HEAD.n, I.HEAD.k)
+        head_packed = B.pack(u8(hc), u8(hs))
+        del hc, hs
+        xh = bf16(I.activations(I.OUTPUT_HEAD, 0, 1, I.HEAD.k)[0])
+        yh = torch.empty(I.HEAD.n, dtype=torch.float32, device=dev)
+        hbytes = I.HEAD.n * I.HEAD.k * 9 // 16 + 2 * I.HEAD.k + 4 * I.HEAD.n
+        extra_rows["head_b1"] = ([B.gemv_batched_prepared([(head_packed, I.HEAD.n, I.HEAD.k, I.TENSOR_SCALE, xh, yh)],
+                                                          ws=ws_split)], 1, [yh], hbytes, 2.0 * I.HEAD.n * I.HEAD.k)
+
     def pre_items(cp):
         return [(pre_packed[cp][j], mat.n, mat.k, I.TENSOR_SCALE, pre_x[j], pre_y[j]) for j, mat in enumerate(pre)]
 
@@ -257,8 +283,17 @@ def main():
         "decode_b1": ("decode_b1", row_b1, dense_copies, lambda i: (2 * i) % dense_copies, y1),
         "quantize": ("quantize", row_q, 1, lambda i: 0, [c for c, _, _ in q_out]),
     }
+    for r, (calls, ncp, outs, _, _) in extra_rows.items():
+        plan_all[r] = (r, (lambda cp, c=calls: c[cp]()), ncp, (lambda i, n_=ncp: (2 * i + 1) % n_), outs)
     order = args.order.split(",") + [r for r in plan_all if r not in args.order.split(",")]
     plan = [plan_all[r] for r in order if r in rows]   # (row name, callable(copy), copies, copy for step i, outputs)
+    # The rows that read the dense layer's weights take its copies in turn
+    # (j-th such row of step i: copy (i * D + j) % 4), so a copy is read again
+    # only after three others (558 MB) have passed through the 256 MB MALL.
+    dense_names = [p_[0] for p_ in plan if p_[0] in ("decode_b1", "decode_b32") or p_[0].startswith("decode_m")]
+    nd = len(dense_names)
+    plan = [(nm, fn, ncp, (lambda i, j=dense_names.index(nm): (i * nd + j) % dense_copies) if nm in dense_names
+             else pick, outs) for nm, fn, ncp, pick, outs in plan]
     # Eager reference outputs (copy 0), then (--graphs) capture.
     eager = {}
     for name, fn, ncp, _, outs in plan:
@@ -355,6 +390,10 @@ def main():
                                   "frac_mfma_bf16": pre_flops / s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                                   "GB/s": pre_bytes / s / 1e9, "equiv_tok_s": pre_flops / s / (2 * 27e9)}
 
+    for r, (_, _, _, nbytes, flops) in extra_rows.items():
+        s = seg[r] * 1e-3
+        result_rows[r] = {"GB/s": nbytes / s / 1e9, "TFLOP/s": flops / s / 1e12, "us": s * 1e6,
+                          "algorithmic_bytes": nbytes, "frac_hbm": nbytes / s / 1e9 / HBM_PEAK_GBS}
     if "quantize" in seg:
         s = seg["quantize"] * 1e-3
         result_rows["quantize"] = {"GB/s": q_bytes / s / 1e9, "us": s * 1e6, "algorithmic_bytes": q_bytes,

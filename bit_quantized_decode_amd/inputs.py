@@ -33,6 +33,8 @@ DECODE_B1 = 1      # 27B-class dense decode layer, batch 1
 DECODE_B32 = 2     # the same layer at batch 32
 MOE_32T = 3        # 512-expert MoE layer, 32 tokens, top-10
 PREFILL_512 = 4    # 512-token prefill, gate/up/down
+DECODE_WIDTHS = 5  # the dense layer at decode widths 2..8
+OUTPUT_HEAD = 6    # the output head at a 248k-token vocabulary, batch 1
 
 
 @dataclass(frozen=True)
@@ -52,6 +54,9 @@ DENSE_LAYER = (
     Matrix("o", 5120, 5120, 4),
 )
 PREFILL_MATRICES = DENSE_LAYER[:3]
+# The output head: a ~248k vocabulary (Ignis README, "Speculative decoding")
+# over the layer's hidden size; 248000 rows leave a ragged last row tile.
+HEAD = Matrix("head", 248000, 5120, 0)
 
 
 @dataclass(frozen=True)

@@ -1,0 +1,53 @@
+"""GPU parity for the decode widths 2..8 of a batch-wide round (the layer's
+five products in one batched launch, as the benchmark runs them) and for the
+output-head GEMV at a 248k-row vocabulary; sampled rows against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_quantized_decode_amd import binding as B
+from bit_quantized_decode_amd import inputs as I
+from helpers import (assert_within, bf16_to_f64, device, oracle_threads, pack_to_device, sample_rows, to_dev_bf16,
+                     ulp_bf16)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def layer():
+    dev = device()
+    mats = []
+    for mat in I.DENSE_LAYER:
+        codes, scales = I.nvfp4_matrix(I.DECODE_B1, mat.matrix_id, mat.n, mat.k)
+        mats.append((mat, codes, scales, pack_to_device(codes, scales, dev)))
+    return dev, mats
+
+
+@pytest.mark.parametrize("m", [2, 3, 4, 8])
+def test_decode_width_layer_batched(layer, m):
+    dev, mats = layer
+    xs = [I.activations(I.DECODE_WIDTHS, mat.matrix_id, m, mat.k) for mat, _, _, _ in mats]
+    ys = [torch.empty((m, mat.n), dtype=torch.bfloat16, device=dev) for mat, _, _, _ in mats]
+    items = [(p, mat.n, mat.k, I.TENSOR_SCALE, to_dev_bf16(x, dev), y) for (mat, _, _, p), x, y in zip(mats, xs, ys)]
+    B.gemm_batched(items)
+    torch.cuda.synchronize()
+    for (mat, codes, scales, _), x, y in zip(mats, xs, ys):
+        rows = sample_rows(mat.n, 200, 300 + m + mat.matrix_id)
+        y_ref, s = oracle.gemm(codes, scales, I.TENSOR_SCALE, x, rows=rows, nthreads=oracle_threads())
+        got = bf16_to_f64(y)[:, rows]
+        assert_within(got, y_ref, s, extra=ulp_bf16(y_ref), what=f"width {m} {mat.name}")
+
+
+def test_output_head_gemv():
+    """248000 x 5120 (715 MB packed), batch 1, sampled rows including the ragged last tile."""
+    dev = device()
+    mat = I.HEAD
+    codes, scales = I.nvfp4_matrix(I.OUTPUT_HEAD, mat.matrix_id, mat.n, mat.k)
+    packed = pack_to_device(codes, scales, dev)
+    x = I.activations(I.OUTPUT_HEAD, 0, 1, mat.k)[0]
+    y = B.gemv(packed, mat.n, mat.k, I.TENSOR_SCALE, to_dev_bf16(x, dev))
+    torch.cuda.synchronize()
+    rows = np.union1d(sample_rows(mat.n, 1000, 400), np.arange(mat.n - 100, mat.n))
+    y_ref, s = oracle.gemm(codes, scales, I.TENSOR_SCALE, x[None, :], rows=rows, nthreads=oracle_threads())
+    assert_within(y.cpu().numpy().astype(np.float64)[rows], y_ref[0], s[0], what="output head")
