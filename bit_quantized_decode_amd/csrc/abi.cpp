@@ -187,7 +187,12 @@ int nvfp4_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, size_t* bytes) {
   NVFP4_TRY(check_rows(n));
   if (m < 0 || m > kMaxDim) return fail(NVFP4_ERR_SHAPE, "m=%lld out of range", (long long)m);
   const nvfp4::Geometry g = nvfp4::geometry(n, k);
-  *bytes = m <= 32 ? nvfp4::skinny_workspace_bytes(g) : nvfp4::prefill_workspace_bytes(m, g);
+  if (m <= nvfp4::kGemvRowsMax) {
+    const nvfp4::Problem pr{nullptr, n, k, 1.0f, nullptr, k, nullptr, n};
+    *bytes = nvfp4::gemv_rows_batch_workspace_bytes(&pr, 1, m);
+  } else {
+    *bytes = m <= 32 ? nvfp4::skinny_workspace_bytes(g) : nvfp4::prefill_workspace_bytes(m, g);
+  }
   return ok();
   NVFP4_GUARD_END
 }
@@ -207,6 +212,15 @@ int nvfp4_gemm(const void* packed, int64_t n, int64_t k, float tensor_scale, con
   if (!aligned16(y) || (k > 0 && (!aligned16(packed) || !aligned16(x))))
     return fail(NVFP4_ERR_ALIGN, "packed, x and y must be 16-byte aligned");
   const nvfp4::Geometry g = nvfp4::geometry(n, k);
+  if (m <= nvfp4::kGemvRowsMax) {
+    const nvfp4::Problem pr{packed, n, k, tensor_scale, x, ldx, y, ldy};
+    const size_t need = nvfp4::gemv_rows_batch_workspace_bytes(&pr, 1, m);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+      return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace ? workspace_bytes : 0);
+    if (need > 0 && !aligned16(workspace)) return fail(NVFP4_ERR_ALIGN, "workspace must be 16-byte aligned");
+    return hip_status(nvfp4::launch_gemv_rows_batch(&pr, 1, m, y_dtype == NVFP4_BF16, workspace, (hipStream_t)stream),
+                      "gemv rows launch");
+  }
   const bool skinny = m <= 32;
   const size_t need = skinny ? nvfp4::skinny_workspace_bytes(g) : nvfp4::prefill_workspace_bytes(m, g);
   if (need > 0 && (!workspace || workspace_bytes < need))
@@ -323,7 +337,9 @@ int nvfp4_gemm_batched_workspace_bytes(const nvfp4_problem* problems, int count,
   std::vector<nvfp4::Problem> pr((size_t)(count > 0 ? count : 0));
   NVFP4_TRY(check_batch(problems, count, m, NVFP4_F32, false, pr.data()));
   size_t need = 0;
-  if (m <= 32) {
+  if (m <= nvfp4::kGemvRowsMax) {
+    need = nvfp4::gemv_rows_batch_workspace_bytes(pr.data(), count, m);
+  } else if (m <= 32) {
     need = nvfp4::skinny_batch_workspace_bytes(pr.data(), count);
   } else {
     need = nvfp4::prefill_batch_workspace_bytes(pr.data(), count, m);
@@ -341,6 +357,14 @@ int nvfp4_gemm_batched(const nvfp4_problem* problems, int count, int64_t m, int 
   NVFP4_TRY(check_batch(problems, count, m, y_dtype, true, pr.data()));
   if (count == 0 || m == 0) return ok();
   const bool bf16 = y_dtype == NVFP4_BF16;
+  if (m <= nvfp4::kGemvRowsMax) {
+    const size_t need = nvfp4::gemv_rows_batch_workspace_bytes(pr.data(), count, m);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+      return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace ? workspace_bytes : 0);
+    if (need > 0 && !aligned16(workspace)) return fail(NVFP4_ERR_ALIGN, "workspace must be 16-byte aligned");
+    return hip_status(nvfp4::launch_gemv_rows_batch(pr.data(), count, m, bf16, workspace, (hipStream_t)stream),
+                      "gemv rows batch launch");
+  }
   if (m <= 32) {
     const size_t need = nvfp4::skinny_batch_workspace_bytes(pr.data(), count);
     if (need > 0 && (!workspace || workspace_bytes < need))

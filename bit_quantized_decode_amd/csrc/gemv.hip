@@ -141,6 +141,141 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvBatch b, unsigned* 
   }
 }
 
+// ---- one or two activation rows (m <= kGemvRowsMax) through the GEMV --------
+// The same tile mapping and reductions as above, for M activation rows: each
+// weight pair is converted once and meets every row's activations in that
+// row's own dot2 chain, in the order the single-row kernel uses, so row i's
+// outputs are bit-identical to a GEMV of row i.  The VALU work grows by one
+// dot2 per weight pair and row: at two rows it still hides under the weight
+// stream (the 27B-class layer: 41 us, against 53 us on the matrix-core
+// path); at three it no longer does (55 us, the same as that path).
+struct GemvRowsBatch {
+  int count;
+  int y_bf16;
+  int wg_begin[kMaxBatch + 1];
+  const uint8_t* packed[kMaxBatch];
+  const uint16_t* x[kMaxBatch];
+  void* y[kMaxBatch];
+  int64_t ldx[kMaxBatch];
+  int64_t ldy[kMaxBatch];
+  int64_t n[kMaxBatch];
+  int64_t k[kMaxBatch];
+  int nkt[kMaxBatch];
+  int groups[kMaxBatch];
+  float st[kMaxBatch];
+  int counter_base[kMaxBatch];
+  int64_t partial_base[kMaxBatch];
+};
+
+template <int C, int M>
+__device__ __forceinline__ void chunk_rows(u32x4 q, const u32x4 (&xs)[M][kGemvWaves * kTileK / 8], int xi, u32x4 sa,
+                                           u32x4 sb, float (&acc_a)[M], float (&acc_b)[M]) {
+  bf16x2 w[4][4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    w[d][0] = e2m1x2_bf16<0>(q[d]);
+    w[d][1] = e2m1x2_bf16<1>(q[d]);
+    w[d][2] = e2m1x2_bf16<2>(q[d]);
+    w[d][3] = e2m1x2_bf16<3>(q[d]);
+  }
+  const float s_a0 = e4m3<(2 * C) % 4>(sa[C / 2]), s_b0 = e4m3<(2 * C) % 4>(sb[C / 2]);
+  const float s_a1 = e4m3<(2 * C + 1) % 4>(sa[C / 2]), s_b1 = e4m3<(2 * C + 1) % 4>(sb[C / 2]);
+#pragma unroll
+  for (int r = 0; r < M; ++r) {
+    const u32x4 xa = xs[r][xi + 4 * C], xb = xs[r][xi + 4 * C + 2];
+    auto d8 = [&](int d, u32x4 x) __attribute__((always_inline)) {
+      float p = dot2(w[d][0], x[0], 0.0f);
+      p = dot2(w[d][1], x[1], p);
+      p = dot2(w[d][2], x[2], p);
+      return dot2(w[d][3], x[3], p);
+    };
+    acc_a[r] = fmaf(d8(0, xa), s_a0, acc_a[r]);
+    acc_b[r] = fmaf(d8(1, xa), s_b0, acc_b[r]);
+    acc_a[r] = fmaf(d8(2, xb), s_a1, acc_a[r]);
+    acc_b[r] = fmaf(d8(3, xb), s_b1, acc_b[r]);
+  }
+}
+
+template <int M>
+__global__ __launch_bounds__(256) void gemv_rows_kernel(const GemvRowsBatch b, unsigned* __restrict__ counters,
+                                                        float* __restrict__ partial_all) {
+  __shared__ u32x4 xs[M][kGemvWaves * kTileK / 8];  // M rows' 4 k tiles of x, zero past K
+  __shared__ float red[M][kGemvWaves][64];
+  int p = 0;
+  while (p + 1 < b.count && (int)blockIdx.x >= b.wg_begin[p + 1]) ++p;
+  const uint8_t* __restrict__ packed = b.packed[p];
+  const uint16_t* __restrict__ x = b.x[p];
+  const int64_t n = b.n[p], k = b.k[p], ldx = b.ldx[p];
+  const int nkt = b.nkt[p], groups = b.groups[p];
+  const int local = (int)blockIdx.x - b.wg_begin[p];
+  const int rt = local / groups;
+  const int grp = local % groups;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int kt = grp * kGemvWaves + wave;
+  const bool has_tile = kt < nkt;
+
+  u32x4 q[8], sa = {0u, 0u, 0u, 0u}, sb = {0u, 0u, 0u, 0u};
+  if (has_tile) {
+    const uint8_t* t = packed + ((size_t)rt * nkt + kt) * kTileBytes;
+    sa = load16(t + kScaleOffset + 32 * (lane & 31));
+    sb = load16(t + kScaleOffset + 32 * (lane & 31) + 16);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) q[c] = load16(t + c * 1024 + lane * 16);
+  }
+  for (int i = threadIdx.x; i < M * (kGemvWaves * kTileK / 8); i += 256) {
+    const int r = i / (kGemvWaves * kTileK / 8), c = i % (kGemvWaves * kTileK / 8);
+    const int64_t kk = (int64_t)grp * kGemvWaves * kTileK + 8 * (int64_t)c;
+    xs[r][c] = kk < k ? *reinterpret_cast<const u32x4*>(x + r * ldx + kk) : u32x4{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+
+  float acc_a[M], acc_b[M];
+#pragma unroll
+  for (int r = 0; r < M; ++r) acc_a[r] = acc_b[r] = 0.0f;
+  if (has_tile) {
+    const int xi = wave * (kTileK / 8) + (lane >> 5);
+#define NVFP4_GEMV_ROWS_CHUNK(C) chunk_rows<C, M>(q[C], xs, xi, sa, sb, acc_a, acc_b);
+    NVFP4_GEMV_ROWS_CHUNK(0) NVFP4_GEMV_ROWS_CHUNK(1) NVFP4_GEMV_ROWS_CHUNK(2) NVFP4_GEMV_ROWS_CHUNK(3)
+    NVFP4_GEMV_ROWS_CHUNK(4) NVFP4_GEMV_ROWS_CHUNK(5) NVFP4_GEMV_ROWS_CHUNK(6) NVFP4_GEMV_ROWS_CHUNK(7)
+#undef NVFP4_GEMV_ROWS_CHUNK
+  }
+#pragma unroll
+  for (int r = 0; r < M; ++r) {
+    uint32_t ua = __float_as_uint(acc_a[r]), ub = __float_as_uint(acc_b[r]);
+    swap_halves(ua, ub);
+    red[r][wave][lane] = __uint_as_float(ua) + __uint_as_float(ub);
+  }
+  __syncthreads();
+  const int64_t row = (int64_t)rt * kTileRows + lane;
+  const float st = b.st[p];
+  void* __restrict__ y = b.y[p];
+  const int64_t ldy = b.ldy[p];
+  auto put = [&](int r, float v) __attribute__((always_inline)) {
+    if (b.y_bf16) static_cast<uint16_t*>(y)[r * ldy + row] = to_bf16(v);
+    else static_cast<float*>(y)[r * ldy + row] = v;
+  };
+  if (groups == 1) {
+    if (wave == 0 && row < n)
+#pragma unroll
+      for (int r = 0; r < M; ++r) put(r, (((red[r][0][lane] + red[r][1][lane]) + red[r][2][lane]) + red[r][3][lane]) * st);
+    return;
+  }
+  // Partials: [group][row][np], so row r's groups are M * np apart.
+  const int64_t np = (int64_t)((n + 63) / 64) * 64;
+  float* partial = partial_all + b.partial_base[p];
+  if (wave == 0)
+#pragma unroll
+    for (int r = 0; r < M; ++r)
+      store_coherent(partial + ((size_t)grp * M + r) * np + row,
+                     ((red[r][0][lane] + red[r][1][lane]) + red[r][2][lane]) + red[r][3][lane]);
+  if (arrive_last(counters + b.counter_base[p] + rt, (unsigned)groups)) {
+    if (wave == 0 && row < n)
+#pragma unroll
+      for (int r = 0; r < M; ++r) put(r, sum_coherent(partial + (size_t)r * np + row, (size_t)M * np, groups) * st);
+  }
+}
+
 __global__ void zero_f32_kernel(float* __restrict__ y, int64_t n) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) y[i] = 0.0f;
@@ -213,6 +348,60 @@ hipError_t launch_gemv_batch(const Problem* p, int count, void* ws, hipStream_t 
     unsigned* cnt = static_cast<unsigned*>(ws);
     float* partial = ws ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kCounterBytes) : nullptr;
     hipLaunchKernelGGL(gemv_kernel, dim3((unsigned)wgs), dim3(256), 0, s, b, cnt, partial);
+  }
+  return hipGetLastError();
+}
+
+size_t gemv_rows_batch_workspace_bytes(const Problem* p, int count, int64_t m) {
+  return gemv_batch_workspace_bytes(p, count) == 0 ? 0 : kCounterBytes + (gemv_batch_workspace_bytes(p, count) - kCounterBytes) * (size_t)m;
+}
+
+hipError_t launch_zero_rows(void* y, int64_t m, int64_t n, int64_t ldy, bool y_bf16, hipStream_t s);
+
+hipError_t launch_gemv_rows_batch(const Problem* p, int count, int64_t m, bool y_bf16, void* ws, hipStream_t s) {
+  for (int b0 = 0; b0 < count; b0 += kMaxBatch) {
+    GemvRowsBatch b = {};
+    b.y_bf16 = y_bf16 ? 1 : 0;
+    int wgs = 0, counters = 0;
+    int64_t pbase = 0;
+    for (int i = b0; i < count && i < b0 + kMaxBatch; ++i) {
+      const Geometry g = geometry(p[i].n, p[i].k);
+      if (g.n == 0) continue;
+      if (g.k == 0) {
+        hipError_t e = launch_zero_rows(p[i].y, m, g.n, p[i].ldy, y_bf16, s);
+        if (e != hipSuccess) return e;
+        continue;
+      }
+      const SplitPlan pl = gemv_plan(g);
+      const int j = b.count++;
+      b.wg_begin[j] = wgs;
+      b.packed[j] = static_cast<const uint8_t*>(p[i].packed);
+      b.x[j] = p[i].x;
+      b.y[j] = p[i].y;
+      b.ldx[j] = p[i].ldx;
+      b.ldy[j] = p[i].ldy;
+      b.n[j] = g.n;
+      b.k[j] = g.k;
+      b.nkt[j] = (int)g.nkt;
+      b.groups[j] = pl.groups;
+      b.st[j] = p[i].st;
+      b.counter_base[j] = counters;
+      b.partial_base[j] = pbase;
+      wgs += (int)(g.nrt * pl.groups);
+      if (pl.groups > 1) {
+        counters += (int)g.nrt;
+        pbase += (int64_t)pl.groups * g.nrt * 64 * m;
+      }
+    }
+    if (b.count == 0) continue;
+    b.wg_begin[b.count] = wgs;
+    unsigned* cnt = static_cast<unsigned*>(ws);
+    float* partial = ws ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kCounterBytes) : nullptr;
+    static_assert(kGemvRowsMax == 2, "row counts instantiated below");
+    if (m == 1)
+      hipLaunchKernelGGL(gemv_rows_kernel<1>, dim3((unsigned)wgs), dim3(256), 0, s, b, cnt, partial);
+    else
+      hipLaunchKernelGGL(gemv_rows_kernel<2>, dim3((unsigned)wgs), dim3(256), 0, s, b, cnt, partial);
   }
   return hipGetLastError();
 }

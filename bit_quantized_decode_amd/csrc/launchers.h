@@ -58,6 +58,11 @@ struct Problem {
 constexpr int kMaxBatch = 8;  // problems per kernel launch (more are split into launches)
 
 size_t gemv_batch_workspace_bytes(const Problem* p, int count);
+// Products of 1..kGemvRowsMax activation rows go to the GEMV's tile mapping
+// (all rows in one launch) instead of the matrix-core skinny path.
+constexpr int64_t kGemvRowsMax = 2;
+size_t gemv_rows_batch_workspace_bytes(const Problem* p, int count, int64_t m);
+hipError_t launch_gemv_rows_batch(const Problem* p, int count, int64_t m, bool y_bf16, void* ws, hipStream_t s);
 hipError_t launch_gemv_batch(const Problem* p, int count, void* ws, hipStream_t s);
 size_t skinny_batch_workspace_bytes(const Problem* p, int count);
 hipError_t launch_skinny_batch(const Problem* p, int count, int64_t m, bool y_bf16, void* ws, hipStream_t s);

@@ -150,10 +150,13 @@ int nvfp4_gemv(const void* packed, int64_t n, int64_t k, float tensor_scale,
  * y[i][j] = s_t * sum_k W[j][k] * x[i][k],   i < m, j < n.
  * x: bf16 bit patterns, row i at x + i*ldx (ldx >= k, ldx % 8 == 0);
  * y: y_dtype, row i at y + i*ldy elements (ldy >= n).
- * m <= 32 runs the skinny (decode-batch) kernel: the imp README's 32-users
- * table and the Ignis README's batch-wide decode round.  Larger m runs the
- * prefill kernel, which dequantises each weight x block-scale exactly to bf16
- * in LDS and runs bf16 MFMA.  m == 0 or n == 0 is a no-op.
+ * m <= 2 runs the GEMV's mapping with both rows in one launch (each row's
+ * outputs bit-identical to nvfp4_gemv of that row, fp32, before the output
+ * rounding); 2 < m <= 32 runs the skinny (decode-batch) kernel on the matrix
+ * cores: the imp README's 32-users table and the Ignis README's batch-wide
+ * decode round of widths 1..8.  Larger m runs the prefill kernel, which
+ * dequantises each weight x block-scale exactly to bf16 and runs bf16 MFMA.
+ * m == 0 or n == 0 is a no-op.
  */
 int nvfp4_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, size_t* bytes /* host */);
 int nvfp4_gemm(const void* packed, int64_t n, int64_t k, float tensor_scale,

@@ -51,3 +51,27 @@ def test_output_head_gemv():
     rows = np.union1d(sample_rows(mat.n, 1000, 400), np.arange(mat.n - 100, mat.n))
     y_ref, s = oracle.gemm(codes, scales, I.TENSOR_SCALE, x[None, :], rows=rows, nthreads=oracle_threads())
     assert_within(y.cpu().numpy().astype(np.float64)[rows], y_ref[0], s[0], what="output head")
+
+
+def test_one_and_two_rows_equal_gemv_bit_for_bit():
+    """m <= 2 runs the GEMV's mapping: each row's fp32 outputs equal a GEMV of
+    that row exactly (strided x and y, a ragged k and n)."""
+    dev = device()
+    rng = np.random.default_rng(23)
+    n, k = 1000, 5136
+    codes, scales = I.nvfp4_matrix(91, 0, n, k)
+    packed = pack_to_device(codes, scales, dev)
+    xb = I.activations(91, 1, 2, k)
+    xs = torch.zeros((2, k + 24), dtype=torch.bfloat16, device=dev)
+    xs[:, :k] = to_dev_bf16(xb, dev)
+    ys = torch.zeros((2, n + 5), dtype=torch.float32, device=dev)
+    B.gemm(packed, n, k, I.TENSOR_SCALE, xs[:, :k], y=ys[:, :n], y_dtype=torch.float32)
+    y1 = B.gemm(packed, n, k, I.TENSOR_SCALE, xs[:1, :k], y_dtype=torch.float32)
+    g0 = B.gemv(packed, n, k, I.TENSOR_SCALE, to_dev_bf16(xb[0], dev))
+    g1 = B.gemv(packed, n, k, I.TENSOR_SCALE, to_dev_bf16(xb[1], dev))
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0, :n], g0) and torch.equal(ys[1, :n], g1)
+    assert torch.equal(y1[0], g0)
+    assert not ys[:, n:].any()          # nothing written past n
+    y_ref, s = oracle.gemm(codes, scales, I.TENSOR_SCALE, xb, nthreads=oracle_threads())
+    assert_within(ys[:, :n].cpu().numpy().astype(np.float64), y_ref, s, what="two rows")
