@@ -28,7 +28,7 @@ EXPORTED = (
     "nvfp4_unpack", "nvfp4_gemv_workspace_bytes", "nvfp4_gemv", "nvfp4_gemm_workspace_bytes", "nvfp4_gemm",
     "nvfp4_gemv_batched_workspace_bytes", "nvfp4_gemv_batched", "nvfp4_gemm_batched_workspace_bytes",
     "nvfp4_gemm_batched", "nvfp4_moe_workspace_bytes", "nvfp4_moe_grouped", "nvfp4_quantize_workspace_bytes",
-    "nvfp4_quantize",
+    "nvfp4_quantize", "nvfp4_expert_cache_reset", "nvfp4_moe_streamed",
 )
 
 
@@ -65,6 +65,20 @@ class MoeArgs(ctypes.Structure):
     ]
 
 
+class ExpertCache(ctypes.Structure):
+    """Mirror of struct nvfp4_expert_cache."""
+    _fields_ = [
+        ("experts", ctypes.c_int64), ("slots", ctypes.c_int64),
+        ("host_gate", ctypes.c_void_p), ("host_up", ctypes.c_void_p), ("host_down", ctypes.c_void_p),
+        ("dev_gate", ctypes.c_void_p), ("dev_up", ctypes.c_void_p), ("dev_down", ctypes.c_void_p),
+        ("stride_gate", ctypes.c_size_t), ("stride_up", ctypes.c_size_t), ("stride_down", ctypes.c_size_t),
+        ("dev_slot_of", ctypes.c_void_p), ("host_counts", ctypes.c_void_p), ("host_slot_stage", ctypes.c_void_p),
+        ("slot_of", ctypes.c_void_p), ("expert_in", ctypes.c_void_p), ("last_use", ctypes.c_void_p),
+        ("clock", ctypes.c_uint64),
+        ("last_active", ctypes.c_int64), ("last_fetched", ctypes.c_int64), ("last_bytes", ctypes.c_size_t),
+    ]
+
+
 _lib = None
 
 
@@ -96,6 +110,8 @@ def lib():
         "nvfp4_moe_grouped": (I, [ctypes.POINTER(MoeArgs), P]),
         "nvfp4_quantize_workspace_bytes": (I, [ctypes.POINTER(sz)]),
         "nvfp4_quantize": (I, [P, I, i64, i64, i64, P, P, P, P, sz, P]),
+        "nvfp4_expert_cache_reset": (I, [ctypes.POINTER(ExpertCache)]),
+        "nvfp4_moe_streamed": (I, [ctypes.POINTER(MoeArgs), ctypes.POINTER(ExpertCache), P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -335,7 +351,12 @@ def moe_workspace_bytes(tokens, experts, top_k, hidden, inter):
 def moe_grouped(x, logits, top_k, w_gate, w_up, w_down, stride_gate, stride_up, stride_down,
                 scale_gate, scale_up, scale_down, inter, y_dtype=torch.float32, debug=False, ws=None,
                 outputs=None, stream=None):
-    """The routed expert layer.  Returns a dict of the outputs (see nvfp4_moe_grouped)."""
+    """The routed expert layer.  Returns a dict of the outputs (see nvfp4_moe_grouped).
+    w_gate may be an ExpertStream (then w_up, w_down and the strides are taken from it)."""
+    streamed = w_gate if isinstance(w_gate, ExpertStream) else None
+    if streamed is not None:
+        w_gate, w_up, w_down = streamed.dev
+        stride_gate, stride_up, stride_down = streamed.strides
     tokens, hidden = x.shape
     experts = logits.shape[1]
     dev = x.device
@@ -364,8 +385,55 @@ def moe_grouped(x, logits, top_k, w_gate, w_up, w_down, stride_gate, stride_up, 
         dbg_gate=o.get("dbg_gate"), dbg_up=o.get("dbg_up"), dbg_h=o.get("dbg_h"), dbg_down=o.get("dbg_down"),
         workspace=ws, workspace_bytes=0 if ws is None else ws.numel(),
     )
-    check(lib().nvfp4_moe_grouped(ctypes.byref(a), _stream(stream)))
+    if streamed is not None:
+        check(lib().nvfp4_moe_streamed(ctypes.byref(a), ctypes.byref(streamed.cache), _stream(stream)))
+    else:
+        check(lib().nvfp4_moe_grouped(ctypes.byref(a), _stream(stream)))
     return o
+
+
+class ExpertStream:
+    """Routed experts streamed from pinned host memory through a device cache
+    of `slots` expert slots (nvfp4_moe_streamed).  pool_*: the packed expert
+    pools (uint8 tensors, expert e at e * stride_*, any device); they are
+    copied once into pinned host memory.  Pass the object as w_gate to
+    moe_grouped (w_up / w_down / strides: None); its device slot pools then
+    stand in for the weights."""
+
+    def __init__(self, pool_gate, pool_up, pool_down, stride_gate, stride_up, stride_down, experts, slots, device):
+        import numpy as np
+        self.host = [torch.empty(p.numel(), dtype=torch.uint8, pin_memory=True) for p in (pool_gate, pool_up, pool_down)]
+        for h, p in zip(self.host, (pool_gate, pool_up, pool_down)):
+            h.copy_(p.reshape(-1))
+        strides = (stride_gate, stride_up, stride_down)
+        self.dev = [torch.empty(slots * st, dtype=torch.uint8, device=device) for st in strides]
+        self.dev_slot_of = torch.zeros(experts, dtype=torch.int32, device=device)
+        self.host_counts = torch.zeros(experts, dtype=torch.int32, pin_memory=True)
+        self.host_stage = torch.zeros(experts, dtype=torch.int32, pin_memory=True)
+        self.slot_of = np.full(experts, -1, np.int32)
+        self.expert_in = np.full(slots, -1, np.int32)
+        self.last_use = np.zeros(slots, np.uint64)
+        c = ExpertCache()
+        c.experts, c.slots = experts, slots
+        c.host_gate, c.host_up, c.host_down = (h.data_ptr() for h in self.host)
+        c.dev_gate, c.dev_up, c.dev_down = (d.data_ptr() for d in self.dev)
+        c.stride_gate, c.stride_up, c.stride_down = strides
+        c.dev_slot_of = self.dev_slot_of.data_ptr()
+        c.host_counts = self.host_counts.data_ptr()
+        c.host_slot_stage = self.host_stage.data_ptr()
+        c.slot_of = self.slot_of.ctypes.data
+        c.expert_in = self.expert_in.ctypes.data
+        c.last_use = self.last_use.ctypes.data
+        self.cache = c
+        self.strides = strides
+        self.reset()
+
+    def reset(self):
+        check(lib().nvfp4_expert_cache_reset(ctypes.byref(self.cache)))
+
+    def stats(self):
+        c = self.cache
+        return {"active": c.last_active, "fetched": c.last_fetched, "bytes": c.last_bytes}
 
 
 def moe_grouped_prepared(*args, **kw):

@@ -306,6 +306,23 @@ static int check_moe(const nvfp4_moe_args* a, bool need_buffers) {
   return NVFP4_OK;
 }
 
+static nvfp4::MoeLaunch moe_launch_of(const nvfp4_moe_args* a) {
+  nvfp4::MoeLaunch l;
+  l.tokens = a->tokens; l.experts = a->experts; l.top_k = a->top_k; l.hidden = a->hidden; l.inter = a->inter;
+  l.x = a->x; l.logits = a->router_logits;
+  l.w_gate = static_cast<const uint8_t*>(a->w_gate);
+  l.w_up = static_cast<const uint8_t*>(a->w_up);
+  l.w_down = static_cast<const uint8_t*>(a->w_down);
+  l.stride_gate = a->stride_gate; l.stride_up = a->stride_up; l.stride_down = a->stride_down;
+  l.scale_gate = a->scale_gate; l.scale_up = a->scale_up; l.scale_down = a->scale_down;
+  l.y = a->y; l.y_bf16 = a->y_dtype == NVFP4_BF16;
+  l.ids = a->topk_ids; l.g = a->topk_weights; l.counts = a->expert_counts; l.offsets = a->expert_offsets;
+  l.perm = a->perm;
+  l.dbg_gate = a->dbg_gate; l.dbg_up = a->dbg_up; l.dbg_h = a->dbg_h; l.dbg_down = a->dbg_down;
+  l.ws = a->workspace;
+  return l;
+}
+
 int nvfp4_gemv_batched_workspace_bytes(const nvfp4_problem* problems, int count, size_t* bytes) {
   NVFP4_GUARD_BEGIN
   if (!bytes) return fail(NVFP4_ERR_NULL, "bytes is NULL");
@@ -398,20 +415,108 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* a, void* stream) {
     return ok();
   }
   NVFP4_TRY(check_moe(a, true));
-  nvfp4::MoeLaunch l;
-  l.tokens = a->tokens; l.experts = a->experts; l.top_k = a->top_k; l.hidden = a->hidden; l.inter = a->inter;
-  l.x = a->x; l.logits = a->router_logits;
-  l.w_gate = static_cast<const uint8_t*>(a->w_gate);
-  l.w_up = static_cast<const uint8_t*>(a->w_up);
-  l.w_down = static_cast<const uint8_t*>(a->w_down);
-  l.stride_gate = a->stride_gate; l.stride_up = a->stride_up; l.stride_down = a->stride_down;
-  l.scale_gate = a->scale_gate; l.scale_up = a->scale_up; l.scale_down = a->scale_down;
-  l.y = a->y; l.y_bf16 = a->y_dtype == NVFP4_BF16;
-  l.ids = a->topk_ids; l.g = a->topk_weights; l.counts = a->expert_counts; l.offsets = a->expert_offsets;
-  l.perm = a->perm;
-  l.dbg_gate = a->dbg_gate; l.dbg_up = a->dbg_up; l.dbg_h = a->dbg_h; l.dbg_down = a->dbg_down;
-  l.ws = a->workspace;
-  return hip_status(nvfp4::launch_moe(l, (hipStream_t)stream), "moe launch");
+  return hip_status(nvfp4::launch_moe(moe_launch_of(a), (hipStream_t)stream), "moe launch");
+  NVFP4_GUARD_END
+}
+
+int nvfp4_expert_cache_reset(nvfp4_expert_cache* c) {
+  NVFP4_GUARD_BEGIN
+  if (!c) return fail(NVFP4_ERR_NULL, "cache is NULL");
+  if (c->experts <= 0 || c->slots <= 0) return fail(NVFP4_ERR_ARG, "experts and slots must be positive");
+  if (!c->slot_of || !c->expert_in || !c->last_use) return fail(NVFP4_ERR_NULL, "cache state arrays must be non-NULL");
+  for (int64_t e = 0; e < c->experts; ++e) c->slot_of[e] = -1;
+  for (int64_t s = 0; s < c->slots; ++s) {
+    c->expert_in[s] = -1;
+    c->last_use[s] = 0;
+  }
+  c->clock = 0;
+  c->last_active = c->last_fetched = 0;
+  c->last_bytes = 0;
+  return ok();
+  NVFP4_GUARD_END
+}
+
+int nvfp4_moe_streamed(const nvfp4_moe_args* a, nvfp4_expert_cache* c, void* stream) {
+  NVFP4_GUARD_BEGIN
+  if (!c) return fail(NVFP4_ERR_NULL, "cache is NULL");
+  if (a && a->tokens == 0) {
+    NVFP4_TRY(check_moe(a, false));
+    c->last_active = c->last_fetched = 0;
+    c->last_bytes = 0;
+    return ok();
+  }
+  NVFP4_TRY(check_moe(a, true));
+  if (c->experts != a->experts || c->slots <= 0)
+    return fail(NVFP4_ERR_ARG, "cache covers %lld experts with %lld slots; the call has %lld experts",
+                (long long)c->experts, (long long)c->slots, (long long)a->experts);
+  if (a->w_gate != c->dev_gate || a->w_up != c->dev_up || a->w_down != c->dev_down ||
+      a->stride_gate != c->stride_gate || a->stride_up != c->stride_up || a->stride_down != c->stride_down)
+    return fail(NVFP4_ERR_ARG, "args' weight pools and strides must be the cache's device slot pools");
+  if (!c->host_gate || !c->host_up || !c->host_down || !c->dev_slot_of || !c->host_counts || !c->host_slot_stage ||
+      !c->slot_of || !c->expert_in || !c->last_use)
+    return fail(NVFP4_ERR_NULL, "a cache buffer is NULL");
+  if (!aligned4(c->dev_slot_of) || !aligned4(c->host_counts) || !aligned4(c->host_slot_stage))
+    return fail(NVFP4_ERR_ALIGN, "the cache's int32 arrays must be 4-byte aligned");
+  const hipStream_t s = (hipStream_t)stream;
+  nvfp4::MoeLaunch l = moe_launch_of(a);
+  NVFP4_TRY(hip_status(nvfp4::launch_moe_routing(l, s), "moe routing launch"));
+  // Which experts this call routes to: one read-back of the counts.
+  NVFP4_TRY(hip_status(hipMemcpyAsync(c->host_counts, a->expert_counts, (size_t)a->experts * 4, hipMemcpyDeviceToHost, s),
+                       "expert counts read-back"));
+  NVFP4_TRY(hip_status(hipStreamSynchronize(s), "expert counts read-back"));
+  const uint64_t now = ++c->clock;
+  int64_t active = 0;
+  for (int64_t e = 0; e < a->experts; ++e)
+    if (c->host_counts[e] > 0) {
+      ++active;
+      if (c->slot_of[e] >= 0) c->last_use[c->slot_of[e]] = now;  // a hit: keep it this call
+    }
+  c->last_active = active;
+  c->last_fetched = 0;
+  c->last_bytes = 0;
+  if (active > c->slots)
+    return fail(NVFP4_ERR_ARG, "the call routes to %lld experts, more than the cache's %lld slots",
+                (long long)active, (long long)c->slots);
+  const size_t gu = nvfp4::packed_bytes(nvfp4::geometry(a->inter, a->hidden));
+  const size_t dn = nvfp4::packed_bytes(nvfp4::geometry(a->hidden, a->inter));
+  const uint8_t* hg = static_cast<const uint8_t*>(c->host_gate);
+  const uint8_t* hu = static_cast<const uint8_t*>(c->host_up);
+  const uint8_t* hd = static_cast<const uint8_t*>(c->host_down);
+  uint8_t* dg = static_cast<uint8_t*>(c->dev_gate);
+  uint8_t* du = static_cast<uint8_t*>(c->dev_up);
+  uint8_t* dd = static_cast<uint8_t*>(c->dev_down);
+  for (int64_t e = 0; e < a->experts; ++e) {
+    if (c->host_counts[e] <= 0 || c->slot_of[e] >= 0) continue;
+    // A miss: a free slot, else the least recently used slot not routed to in this call.
+    int64_t v = -1;
+    for (int64_t q = 0; q < c->slots; ++q)
+      if (c->expert_in[q] < 0) {
+        v = q;
+        break;
+      }
+    if (v < 0)
+      for (int64_t q = 0; q < c->slots; ++q)
+        if (c->last_use[q] < now && (v < 0 || c->last_use[q] < c->last_use[v])) v = q;
+    if (v < 0) return fail(NVFP4_ERR_ARG, "no free cache slot");  // cannot happen when active <= slots
+    if (c->expert_in[v] >= 0) c->slot_of[c->expert_in[v]] = -1;
+    c->expert_in[v] = (int32_t)e;
+    c->slot_of[e] = (int32_t)v;
+    c->last_use[v] = now;
+    NVFP4_TRY(hip_status(hipMemcpyAsync(dg + v * c->stride_gate, hg + e * c->stride_gate, gu, hipMemcpyHostToDevice, s),
+                         "expert copy"));
+    NVFP4_TRY(hip_status(hipMemcpyAsync(du + v * c->stride_up, hu + e * c->stride_up, gu, hipMemcpyHostToDevice, s),
+                         "expert copy"));
+    NVFP4_TRY(hip_status(hipMemcpyAsync(dd + v * c->stride_down, hd + e * c->stride_down, dn, hipMemcpyHostToDevice, s),
+                         "expert copy"));
+    ++c->last_fetched;
+    c->last_bytes += 2 * gu + dn;
+  }
+  // The slot table (entries of experts not routed to are never read).
+  for (int64_t e = 0; e < a->experts; ++e) c->host_slot_stage[e] = c->slot_of[e] < 0 ? 0 : c->slot_of[e];
+  NVFP4_TRY(hip_status(hipMemcpyAsync(c->dev_slot_of, c->host_slot_stage, (size_t)a->experts * 4, hipMemcpyHostToDevice, s),
+                       "slot table copy"));
+  l.slot_table = c->dev_slot_of;
+  return hip_status(nvfp4::launch_moe_experts(l, s), "moe expert launch");
   NVFP4_GUARD_END
 }
 

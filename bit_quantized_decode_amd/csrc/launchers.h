@@ -107,9 +107,13 @@ struct MoeLaunch {
   uint16_t* dbg_h;
   float* dbg_down;
   void* ws;
+  const int32_t* slot_table = nullptr;  // device [experts]: pool slot of each expert (nullptr: slot e)
 };
 size_t moe_workspace_bytes(int64_t tokens, int64_t experts, int64_t top_k, int64_t hidden, int64_t inter);
 int64_t moe_max_experts();
 hipError_t launch_moe(const MoeLaunch& a, hipStream_t s);
+// The two halves of launch_moe: routing and grouping, then the expert GEMMs and the scatter.
+hipError_t launch_moe_routing(const MoeLaunch& a, hipStream_t s);
+hipError_t launch_moe_experts(const MoeLaunch& a, hipStream_t s);
 
 }  // namespace nvfp4

@@ -347,8 +347,9 @@ __device__ __forceinline__ void store_partials(float* red, int wave, int lane, c
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void gate_up_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ chunks, const int32_t* __restrict__ n_chunks,
     int max_chunks, int hidden, int inter, const uint8_t* __restrict__ w_gate, const uint8_t* __restrict__ w_up,
-    size_t stride_gate, size_t stride_up, const float* __restrict__ scale_gate, const float* __restrict__ scale_up,
-    uint16_t* __restrict__ h, float* __restrict__ dbg_gate, float* __restrict__ dbg_up) {
+    size_t stride_gate, size_t stride_up, const int32_t* __restrict__ slot_table,
+    const float* __restrict__ scale_gate, const float* __restrict__ scale_up, uint16_t* __restrict__ h,
+    float* __restrict__ dbg_gate, float* __restrict__ dbg_up) {
   constexpr int KS = 4;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kExpertLds];
   const int nrt = (inter + 63) / 64;
@@ -366,8 +367,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
     const int32_t* rec = chunks + (size_t)(jc < max_chunks ? jc : max_chunks - 1) * kChunkInts;
     const int e = rec[0], p0 = rec[1], rows = rec[2];
     if (jc >= nch) break;
+    const int es = slot_table ? slot_table[e] : e;  // where expert e's matrices sit in the pools
     const uint8_t* wrow =
-        (wave >= KS ? w_up + e * stride_up : w_gate + e * stride_gate) + (size_t)rt * nkt * kTileBytes;
+        (wave >= KS ? w_up + es * stride_up : w_gate + es * stride_gate) + (size_t)rt * nkt * kTileBytes;
     const uint16_t* xrow[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) xrow[j] = x + (int64_t)rec[4 + 4 * wave + 2 * j + (lane >> 5)] * hidden;
@@ -409,7 +411,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void down_kernel(
     const uint16_t* __restrict__ hin, const int32_t* __restrict__ chunks, const int32_t* __restrict__ n_chunks,
     int max_chunks, int hidden, int inter, const uint8_t* __restrict__ w_down, size_t stride_down,
-    const float* __restrict__ scale_down, float* __restrict__ d) {
+    const int32_t* __restrict__ slot_table, const float* __restrict__ scale_down, float* __restrict__ d) {
   constexpr int KS = 2;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kExpertLds];
   const int nrt = (hidden + 63) / 64;
@@ -428,7 +430,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void d
     if (jc >= nch) break;
     const int rt = 4 * grp + wave / KS;
     const bool has_rows = rt < nrt;
-    const uint8_t* wrow = has_rows ? w_down + e * stride_down + (size_t)rt * nkt * kTileBytes : nullptr;
+    const int es = slot_table ? slot_table[e] : e;
+    const uint8_t* wrow = has_rows ? w_down + es * stride_down + (size_t)rt * nkt * kTileBytes : nullptr;
     // The chunk's rows of h are contiguous (the last repeated past the end).
     const uint16_t* xrow[2];
 #pragma unroll
@@ -543,7 +546,7 @@ size_t moe_workspace_bytes(int64_t tokens, int64_t experts, int64_t top_k, int64
   return total;
 }
 
-hipError_t launch_moe(const MoeLaunch& a, hipStream_t s) {
+hipError_t launch_moe_routing(const MoeLaunch& a, hipStream_t s) {
   if (a.tokens == 0) return hipSuccess;
   MoeWs w = carve(a.ws, a.tokens, a.experts, a.top_k, a.hidden, a.inter, nullptr);
   const int64_t flat = a.tokens * a.top_k;
@@ -558,7 +561,14 @@ hipError_t launch_moe(const MoeLaunch& a, hipStream_t s) {
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(group_kernel, dim3(1), dim3(1024), 0, s, a.ids, (int)flat, (int)a.experts, (int)a.top_k,
                      a.counts, a.offsets, a.perm, w.pos, w.chunks, w.n_chunks);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_experts(const MoeLaunch& a, hipStream_t s) {
+  if (a.tokens == 0) return hipSuccess;
+  MoeWs w = carve(a.ws, a.tokens, a.experts, a.top_k, a.hidden, a.inter, nullptr);
+  const int64_t flat = a.tokens * a.top_k;
+  hipError_t err = hipSuccess;
   // The expert GEMMs run on persistent grids of at most two workgroups per
   // CU (what fits at once), which walk the work list's items (chunk, output
   // rows) with a stride; the list's actual length is read on the device.
@@ -568,15 +578,15 @@ hipError_t launch_moe(const MoeLaunch& a, hipStream_t s) {
   const int64_t gu_items = mch * nrt_i;
   hipLaunchKernelGGL(gate_up_kernel, dim3((unsigned)(gu_items < resident ? gu_items : resident)),
                      dim3(64 * kExpertWaves), 0, s, a.x, w.chunks, w.n_chunks, (int)mch, (int)a.hidden, (int)a.inter,
-                     a.w_gate, a.w_up, a.stride_gate, a.stride_up, a.scale_gate, a.scale_up, w.h, a.dbg_gate,
-                     a.dbg_up);
+                     a.w_gate, a.w_up, a.stride_gate, a.stride_up, a.slot_table, a.scale_gate, a.scale_up, w.h,
+                     a.dbg_gate, a.dbg_up);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const int64_t grp_h = ((a.hidden + 63) / 64 + 3) / 4;
   const int64_t dn_items = mch * grp_h;
   float* d = a.dbg_down ? a.dbg_down : w.d;
   hipLaunchKernelGGL(down_kernel, dim3((unsigned)(dn_items < resident ? dn_items : resident)),
                      dim3(64 * kExpertWaves), 0, s, w.h, w.chunks, w.n_chunks, (int)mch, (int)a.hidden,
-                     (int)a.inter, a.w_down, a.stride_down, a.scale_down, d);
+                     (int)a.inter, a.w_down, a.stride_down, a.slot_table, a.scale_down, d);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const int64_t outs = a.tokens * a.hidden;
   hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, s, d, a.g, w.pos, a.tokens,
@@ -586,6 +596,11 @@ hipError_t launch_moe(const MoeLaunch& a, hipStream_t s) {
     err = hipMemcpyAsync(a.dbg_h, w.h, (size_t)flat * a.inter * 2, hipMemcpyDeviceToDevice, s);
   }
   return err;
+}
+
+hipError_t launch_moe(const MoeLaunch& a, hipStream_t s) {
+  const hipError_t err = launch_moe_routing(a, s);
+  return err != hipSuccess ? err : launch_moe_experts(a, s);
 }
 
 }  // namespace nvfp4

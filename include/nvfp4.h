@@ -249,6 +249,59 @@ typedef struct nvfp4_moe_args {
 int nvfp4_moe_workspace_bytes(const nvfp4_moe_args* args /* host */, size_t* bytes /* host */);
 int nvfp4_moe_grouped(const nvfp4_moe_args* args /* host */, void* stream);
 
+/* ---- f3: routed experts streamed from host memory --------------------------
+ * The imp README runs mixture-of-experts models larger than the card with the
+ * experts in host RAM ("Will it fit?"); only the routed experts' weights are
+ * needed per token (CHImp-Alpha-v1.0 model card, "How it fits on one GPU").
+ * Here every expert's packed gate, up and down matrices stay in pinned host
+ * pools; a device cache of `slots` expert slots keeps recently used experts.
+ * nvfp4_moe_streamed() routes and groups on the GPU, reads the expert counts
+ * back (it synchronises `stream` once), copies each routed expert that is not
+ * cached into a free slot or, failing that, the least recently used slot no
+ * routed expert of this call occupies (host to device, on `stream`), and then
+ * runs the expert GEMMs on the slots.  Outputs are bit-identical to
+ * nvfp4_moe_grouped() with the same weights device-resident.
+ *
+ * The caller owns every buffer.  Device: dev_gate/dev_up/dev_down (slot s at
+ * s * stride_*, 16-byte aligned strides of at least the packed matrix size),
+ * dev_slot_of [experts] int32.  Pinned host (hipHostMalloc): host_gate/host_up/
+ * host_down (expert e at e * stride_*, same strides), host_counts [experts]
+ * and host_slot_stage [experts] int32.  Host (any): slot_of [experts] int32,
+ * expert_in [slots] int32, last_use [slots] uint64 -- the cache state, set up
+ * by nvfp4_expert_cache_reset() and kept across calls.  Calls sharing a cache
+ * must be issued in order on one stream.
+ * In nvfp4_moe_streamed(), args->w_gate/w_up/w_down and the strides must be
+ * the cache's device slot pools and strides; every other argument is as for
+ * nvfp4_moe_grouped().  If a call routes to more experts than there are
+ * slots it returns NVFP4_ERR_ARG after routing (topk_ids, topk_weights,
+ * expert_counts, expert_offsets and perm are then valid, y is not).
+ * last_active / last_fetched / last_bytes: the routed experts, the experts
+ * copied and the bytes copied by the last call.
+ */
+typedef struct nvfp4_expert_cache {
+  int64_t experts, slots;
+  const void* host_gate;
+  const void* host_up;
+  const void* host_down;
+  void* dev_gate;
+  void* dev_up;
+  void* dev_down;
+  size_t stride_gate, stride_up, stride_down;
+  int32_t* dev_slot_of;
+  int32_t* host_counts;
+  int32_t* host_slot_stage;
+  int32_t* slot_of;
+  int32_t* expert_in;
+  uint64_t* last_use;
+  uint64_t clock;
+  int64_t last_active, last_fetched;
+  size_t last_bytes;
+} nvfp4_expert_cache;
+
+/* Empty the cache: every slot free, every expert uncached, statistics zero. */
+int nvfp4_expert_cache_reset(nvfp4_expert_cache* cache /* host */);
+int nvfp4_moe_streamed(const nvfp4_moe_args* args /* host */, nvfp4_expert_cache* cache /* host */, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     assert set(names) == set(B.EXPORTED)
     for name in names:
         assert hasattr(L, name), name
@@ -197,3 +197,27 @@ def test_batched_validation(L):
     big[0].ldx, big[0].ldy = 17408, 5120
     assert L.nvfp4_gemm_batched_workspace_bytes(big, 1, 32, ctypes.byref(sz)) == B.NVFP4_OK and sz.value > 0
     assert L.nvfp4_gemm_batched(big, 1, 32, 1, None, 0, None) == B.NVFP4_ERR_WORKSPACE
+
+
+def test_expert_cache_validation(L):
+    import numpy as np
+    c = B.ExpertCache()
+    assert L.nvfp4_expert_cache_reset(None) == B.NVFP4_ERR_NULL
+    c.experts, c.slots = 8, 0
+    assert L.nvfp4_expert_cache_reset(ctypes.byref(c)) == B.NVFP4_ERR_ARG
+    c.slots = 4
+    assert L.nvfp4_expert_cache_reset(ctypes.byref(c)) == B.NVFP4_ERR_NULL      # no state arrays
+    slot_of = np.zeros(8, np.int32)
+    expert_in = np.zeros(4, np.int32)
+    last_use = np.ones(4, np.uint64)
+    c.slot_of, c.expert_in, c.last_use = slot_of.ctypes.data, expert_in.ctypes.data, last_use.ctypes.data
+    c.clock = 99
+    assert L.nvfp4_expert_cache_reset(ctypes.byref(c)) == B.NVFP4_OK
+    assert (slot_of == -1).all() and (expert_in == -1).all() and (last_use == 0).all() and c.clock == 0
+    # nvfp4_moe_streamed refuses before any launch: no cache, or pools that are not the cache's.
+    a = moe_template()
+    assert L.nvfp4_moe_streamed(ctypes.byref(a), None, None) == B.NVFP4_ERR_NULL
+    c.experts = 512
+    c.dev_gate = c.dev_up = c.dev_down = 0x20000
+    c.stride_gate = c.stride_up = c.stride_down = 589_824
+    assert L.nvfp4_moe_streamed(ctypes.byref(a), ctypes.byref(c), None) == B.NVFP4_ERR_ARG
