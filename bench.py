@@ -90,7 +90,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target length of the oracle sample")
     p.add_argument("--rows", default="decode_b1,decode_b32,moe,prefill",
                    help="rows to run; optional, not default: quantize (the NVFP4 quantiser over the layer), "
-                        "decode_m2 .. decode_m8 (the layer at decode widths 2..8), head_b1 (the output head, batch 1)")
+                        "decode_m2 .. decode_m8 (the layer at decode widths 2..8), head_b1 (the output head, batch 1), "
+                        "moe_stream (the MoE layer with experts streamed from host memory)")
     p.add_argument("--order", default="prefill,moe,decode_b32,decode_b1",
                    help="row order within a step (the batch-1 GEMV last: see the note at the plan)")
     p.add_argument("--graphs", action="store_true", help="replay per-row HIP graphs instead of direct launches")
@@ -142,7 +143,7 @@ def main():
     # ---- MoE --------------------------------------------------------------
     shape = I.MoeShape()
     moe_pools = []
-    if "moe" in rows:
+    if "moe" in rows or "moe_stream" in rows:
         w = I.moe_weights(I.MOE_32T, shape)
         stride_gu = B.packed_bytes(shape.inter, shape.hidden)
         stride_d = B.packed_bytes(shape.hidden, shape.inter)
@@ -174,6 +175,26 @@ def main():
 
     def run_moe(cp):
         moe_calls[cp]()
+
+    # ---- optional: the same layer with the experts streamed from pinned host
+    # memory through a device cache of 64 expert slots (1/8 of the experts);
+    # each step routes a new batch of 32 tokens (other tokens, the same expert
+    # popularity), 64 batches in turn -------------------------------------
+    stream_state = {}
+    if "moe_stream" in rows:
+        es = B.ExpertStream(*moe_pools[0], stride_gu, stride_gu, stride_d, shape.experts, 64, dev)
+        batches = 64
+        sx = [bf16(I.activations(I.MOE_32T, 100 + r, shape.tokens, shape.hidden)) for r in range(batches)]
+        slg = [torch.from_numpy(I.router_logits(I.MOE_32T, shape.tokens, shape.experts, shape.zipf_s, batch=r)).to(dev)
+               for r in range(batches)]
+        s_out = {}
+        stream_state.update(es=es, stats=[], out=s_out)
+
+    def run_moe_stream(cp):
+        es = stream_state["es"]
+        B.moe_grouped(sx[cp], slg[cp], shape.top_k, es, None, None, None, None, None, sts[0], sts[1], sts[2],
+                      shape.inter, y_dtype=torch.float32, ws=moe_ws, outputs=stream_state["out"])
+        stream_state["stats"].append(es.stats())
 
     # ---- prefill ----------------------------------------------------------
     pre = I.PREFILL_MATRICES
@@ -282,6 +303,7 @@ def main():
         "decode_b32": ("decode_b32", row_b32, dense_copies, lambda i: (2 * i + 1) % dense_copies, y32),
         "decode_b1": ("decode_b1", row_b1, dense_copies, lambda i: (2 * i) % dense_copies, y1),
         "quantize": ("quantize", row_q, 1, lambda i: 0, [c for c, _, _ in q_out]),
+        "moe_stream": ("moe_stream", run_moe_stream, 64, lambda i: i % 64, None),
     }
     for r, (calls, ncp, outs, _, _) in extra_rows.items():
         plan_all[r] = (r, (lambda cp, c=calls: c[cp]()), ncp, (lambda i, n_=ncp: (2 * i + 1) % n_), outs)
@@ -299,8 +321,12 @@ def main():
     for name, fn, ncp, _, outs in plan:
         fn(0)
         torch.cuda.synchronize()
-        eager[name] = [o.clone() for o in outs] if outs is not None else [moe_out["y"].clone()]
+        if outs is None:
+            outs = [moe_out["y"]] if name == "moe" else [stream_state["out"]["y"]]
+        eager[name] = [o.clone() for o in outs]
     graphs = {}
+    if args.graphs and "moe_stream" in rows:
+        raise SystemExit("--graphs: the moe_stream row synchronises with the host inside each call; run it without --graphs")
     if args.graphs:
         for name, fn, ncp, _, _ in plan:
             for cp in range(ncp):
@@ -390,6 +416,16 @@ def main():
                                   "frac_mfma_bf16": pre_flops / s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                                   "GB/s": pre_bytes / s / 1e9, "equiv_tok_s": pre_flops / s / (2 * 27e9)}
 
+    if "moe_stream" in seg:
+        s = seg["moe_stream"] * 1e-3
+        st_timed = stream_state["stats"][-args.steps:]
+        fetched = sum(x["fetched"] for x in st_timed) / len(st_timed)
+        active = sum(x["active"] for x in st_timed) / len(st_timed)
+        pcie = sum(x["bytes"] for x in st_timed) / len(st_timed)
+        result_rows["moe_stream"] = {"us": s * 1e6, "cache_slots": 64, "active_experts": active,
+                                     "fetched_experts": fetched, "hit_rate": 1.0 - fetched / active,
+                                     "copied_bytes": pcie, "copied_GB/s": pcie / s / 1e9,
+                                     "layer_tok_s": shape.tokens / s}
     for r, (_, _, _, nbytes, flops) in extra_rows.items():
         s = seg[r] * 1e-3
         result_rows[r] = {"GB/s": nbytes / s / 1e9, "TFLOP/s": flops / s / 1e12, "us": s * 1e6,

@@ -479,9 +479,18 @@ int nvfp4_moe_streamed(const nvfp4_moe_args* a, nvfp4_expert_cache* c, void* str
                 (long long)active, (long long)c->slots);
   const size_t gu = nvfp4::packed_bytes(nvfp4::geometry(a->inter, a->hidden));
   const size_t dn = nvfp4::packed_bytes(nvfp4::geometry(a->hidden, a->inter));
-  const uint8_t* hg = static_cast<const uint8_t*>(c->host_gate);
-  const uint8_t* hu = static_cast<const uint8_t*>(c->host_up);
-  const uint8_t* hd = static_cast<const uint8_t*>(c->host_down);
+  // The GPU reads the pinned pools directly (their device-side addresses).
+  void* mapped[3] = {nullptr, nullptr, nullptr};
+  const void* hosts[3] = {c->host_gate, c->host_up, c->host_down};
+  for (int i = 0; i < 3; ++i)
+    if (hipHostGetDevicePointer(&mapped[i], const_cast<void*>(hosts[i]), 0) != hipSuccess || !mapped[i])
+      return fail(NVFP4_ERR_ARG, "host pools must be pinned host memory mapped for the GPU (hipHostMalloc)");
+  const uint8_t* hg = static_cast<const uint8_t*>(mapped[0]);
+  const uint8_t* hu = static_cast<const uint8_t*>(mapped[1]);
+  const uint8_t* hd = static_cast<const uint8_t*>(mapped[2]);
+  std::vector<const void*> csrc;
+  std::vector<void*> cdst;
+  std::vector<size_t> cbytes;
   uint8_t* dg = static_cast<uint8_t*>(c->dev_gate);
   uint8_t* du = static_cast<uint8_t*>(c->dev_up);
   uint8_t* dd = static_cast<uint8_t*>(c->dev_down);
@@ -502,15 +511,21 @@ int nvfp4_moe_streamed(const nvfp4_moe_args* a, nvfp4_expert_cache* c, void* str
     c->expert_in[v] = (int32_t)e;
     c->slot_of[e] = (int32_t)v;
     c->last_use[v] = now;
-    NVFP4_TRY(hip_status(hipMemcpyAsync(dg + v * c->stride_gate, hg + e * c->stride_gate, gu, hipMemcpyHostToDevice, s),
-                         "expert copy"));
-    NVFP4_TRY(hip_status(hipMemcpyAsync(du + v * c->stride_up, hu + e * c->stride_up, gu, hipMemcpyHostToDevice, s),
-                         "expert copy"));
-    NVFP4_TRY(hip_status(hipMemcpyAsync(dd + v * c->stride_down, hd + e * c->stride_down, dn, hipMemcpyHostToDevice, s),
-                         "expert copy"));
+    csrc.push_back(hg + e * c->stride_gate);
+    cdst.push_back(dg + v * c->stride_gate);
+    cbytes.push_back(gu);
+    csrc.push_back(hu + e * c->stride_up);
+    cdst.push_back(du + v * c->stride_up);
+    cbytes.push_back(gu);
+    csrc.push_back(hd + e * c->stride_down);
+    cdst.push_back(dd + v * c->stride_down);
+    cbytes.push_back(dn);
     ++c->last_fetched;
     c->last_bytes += 2 * gu + dn;
   }
+  if (!csrc.empty())
+    NVFP4_TRY(hip_status(nvfp4::launch_expert_copies(csrc.data(), cdst.data(), cbytes.data(), (int)csrc.size(), s),
+                         "expert copy launch"));
   // The slot table (entries of experts not routed to are never read).
   for (int64_t e = 0; e < a->experts; ++e) c->host_slot_stage[e] = c->slot_of[e] < 0 ? 0 : c->slot_of[e];
   NVFP4_TRY(hip_status(hipMemcpyAsync(c->dev_slot_of, c->host_slot_stage, (size_t)a->experts * 4, hipMemcpyHostToDevice, s),

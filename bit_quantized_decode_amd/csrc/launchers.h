@@ -115,5 +115,9 @@ hipError_t launch_moe(const MoeLaunch& a, hipStream_t s);
 // The two halves of launch_moe: routing and grouping, then the expert GEMMs and the scatter.
 hipError_t launch_moe_routing(const MoeLaunch& a, hipStream_t s);
 hipError_t launch_moe_experts(const MoeLaunch& a, hipStream_t s);
+// Copies of `count` byte ranges (multiples of 16 bytes, 16-byte aligned) from
+// GPU-mapped pinned host memory into device memory, in one launch per 96.
+hipError_t launch_expert_copies(const void* const* src, void* const* dst, const size_t* bytes, int count,
+                                hipStream_t s);
 
 }  // namespace nvfp4

@@ -492,6 +492,50 @@ __global__ __launch_bounds__(256) void scatter_kernel(const float* __restrict__ 
   else static_cast<float*>(y)[i] = acc;
 }
 
+// Copies of whole expert matrices from pinned host memory into device cache
+// slots, read by the GPU over PCIe: one launch for all of a call's copies, so
+// that many 16-byte reads are in flight at once (a DMA transfer per matrix
+// pays a set-up cost per copy).  Entry j copies words16[j] 16-byte words.
+constexpr int kCopiesPerLaunch = 96;
+constexpr int kCopyWordsPerBlock = 256 * 8;  // 32 KB per workgroup
+struct CopyList {
+  int count;
+  int blocks_per_entry;
+  const u32x4* src[kCopiesPerLaunch];
+  u32x4* dst[kCopiesPerLaunch];
+  int64_t words16[kCopiesPerLaunch];
+};
+
+__global__ __launch_bounds__(256) void expert_copy_kernel(const CopyList l) {
+  const int entry = blockIdx.x / l.blocks_per_entry;
+  const int64_t w0 = (int64_t)(blockIdx.x % l.blocks_per_entry) * kCopyWordsPerBlock;
+  int j = 0;
+#pragma unroll
+  for (int i = 1; i < kCopiesPerLaunch; ++i)
+    if (i == entry) j = i;  // static indices into the argument arrays
+  const u32x4* src = nullptr;
+  u32x4* dst = nullptr;
+  int64_t n = 0;
+#pragma unroll
+  for (int i = 0; i < kCopiesPerLaunch; ++i)
+    if (i == j) {
+      src = l.src[i];
+      dst = l.dst[i];
+      n = l.words16[i];
+    }
+  u32x4 v[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int64_t w = w0 + u * 256 + threadIdx.x;
+    if (w < n) v[u] = src[w];
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int64_t w = w0 + u * 256 + threadIdx.x;
+    if (w < n) dst[w] = v[u];
+  }
+}
+
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // Compute units of the current device (queried once per device).
@@ -539,6 +583,27 @@ MoeWs carve(void* ws, int64_t tokens, int64_t experts, int64_t top_k, int64_t hi
 }  // namespace
 
 int64_t moe_max_experts() { return kMaxExperts; }
+
+hipError_t launch_expert_copies(const void* const* src, void* const* dst, const size_t* bytes, int count,
+                                hipStream_t s) {
+  for (int c0 = 0; c0 < count; c0 += kCopiesPerLaunch) {
+    CopyList l = {};
+    l.count = count - c0 < kCopiesPerLaunch ? count - c0 : kCopiesPerLaunch;
+    int64_t most = 0;
+    for (int i = 0; i < l.count; ++i) {
+      l.src[i] = static_cast<const u32x4*>(src[c0 + i]);
+      l.dst[i] = static_cast<u32x4*>(dst[c0 + i]);
+      l.words16[i] = (int64_t)(bytes[c0 + i] / 16);
+      if (l.words16[i] > most) most = l.words16[i];
+    }
+    l.blocks_per_entry = (int)((most + kCopyWordsPerBlock - 1) / kCopyWordsPerBlock);
+    if (l.blocks_per_entry == 0) continue;
+    hipLaunchKernelGGL(expert_copy_kernel, dim3((unsigned)(l.count * l.blocks_per_entry)), dim3(256), 0, s, l);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
 
 size_t moe_workspace_bytes(int64_t tokens, int64_t experts, int64_t top_k, int64_t hidden, int64_t inter) {
   size_t total = 0;

@@ -108,9 +108,10 @@ def nvfp4_matrix(workload_id, matrix_id, n, k):
     return nvfp4_codes(workload_id, matrix_id, n, k), nvfp4_scales(workload_id, matrix_id, n, k)
 
 
-def router_logits(workload_id, tokens, experts, zipf_s=1.1):
-    """fp32 [tokens][experts] = N(0,1) + (-zipf_s * ln r_e)."""
-    z = generator(workload_id, 0, 3).standard_normal(size=(tokens, experts), dtype=np.float32)
+def router_logits(workload_id, tokens, experts, zipf_s=1.1, batch=0):
+    """fp32 [tokens][experts] = N(0,1) + (-zipf_s * ln r_e).  `batch` draws other
+    tokens' noise over the same expert popularity r."""
+    z = generator(workload_id, batch, 3).standard_normal(size=(tokens, experts), dtype=np.float32)
     r = generator(workload_id, 0, 4).permutation(experts) + 1
     bias = (-zipf_s * np.log(r.astype(np.float64))).astype(np.float32)
     return (z + bias[None, :]).astype(np.float32)

@@ -258,13 +258,15 @@ int nvfp4_moe_grouped(const nvfp4_moe_args* args /* host */, void* stream);
  * nvfp4_moe_streamed() routes and groups on the GPU, reads the expert counts
  * back (it synchronises `stream` once), copies each routed expert that is not
  * cached into a free slot or, failing that, the least recently used slot no
- * routed expert of this call occupies (host to device, on `stream`), and then
+ * routed expert of this call occupies -- one kernel on `stream` reads all of
+ * the call's missing matrices from the pinned pools over PCIe -- and then
  * runs the expert GEMMs on the slots.  Outputs are bit-identical to
  * nvfp4_moe_grouped() with the same weights device-resident.
  *
  * The caller owns every buffer.  Device: dev_gate/dev_up/dev_down (slot s at
  * s * stride_*, 16-byte aligned strides of at least the packed matrix size),
- * dev_slot_of [experts] int32.  Pinned host (hipHostMalloc): host_gate/host_up/
+ * dev_slot_of [experts] int32.  Pinned host memory mapped for the GPU
+ * (hipHostMalloc; NVFP4_ERR_ARG otherwise): host_gate/host_up/
  * host_down (expert e at e * stride_*, same strides), host_counts [experts]
  * and host_slot_stage [experts] int32.  Host (any): slot_of [experts] int32,
  * expert_in [slots] int32, last_use [slots] uint64 -- the cache state, set up
