@@ -5,5 +5,5 @@ this package.  The GPU library never imports it and it never imports the GPU
 library.
 """
 from .oracle import (  # noqa: F401
-    build, e2m1, e4m3, bf16_to_f64, dequant, gemm, route, group, silu, moe, max_threads, quantize,
+    build, e2m1, e4m3, bf16_to_f64, dequant, gemm, route, group, silu, moe, max_threads, quantize, mx_from_nvfp4, mx_from_bf16, mx_gemm,
 )

@@ -345,3 +345,107 @@ void nvo_quantize(const void* w, int bf16, int64_t n, int64_t k, int64_t ldw, fl
       }
     }
 }
+
+/* ---- W4A4: both operands in the OCP MX FP4 block format ---------------------
+ *
+ * The pages' prefill runs native FP4 on both operands (imp README, "How does
+ * it work?"); on this hardware the FP4 matrix instructions take the OCP MX
+ * format: 32 consecutive k elements share one E8M0 (power-of-two) scale.
+ * Readings (each listed in the design notes):
+ *   - a 32-element block v with largest magnitude amax gets the scale
+ *     X = 2^(floor(log2 amax) - 2) (2 is the exponent of E2M1's largest
+ *     power of two, 4), the exponent clamped to [-127, 127]; an all-zero
+ *     block gets the smallest scale (byte 0) and zero codes;
+ *   - each element's code is the E2M1 value nearest v / X (ties to the even
+ *     mantissa, +-6 beyond 6; v / X is exact, X being a power of two); the
+ *     sign bit is v's;
+ *   - weights: an NVFP4 matrix's values e2m1(c) * e4m3(sigma) (exact, s_t left
+ *     out) are requantised this way along k; activations: the bf16 values;
+ *   - y = s_t * sum_k w'[n][k] * x'[m][k] over the requantised values, in
+ *     fp64 here (every product is exact).
+ * The block is 32 k elements along each row; K is a multiple of 32.
+ */
+
+/* E8M0 byte and the 32 codes (low nibble first) of one block of doubles. */
+static void mx_block(const double* v, uint8_t* codes16, uint8_t* scale) {
+  double amax = 0.0;
+  for (int i = 0; i < 32; ++i)
+    if (fabs(v[i]) > amax) amax = fabs(v[i]);
+  memset(codes16, 0, 16);
+  if (amax == 0.0) {
+    *scale = 0;
+    return;
+  }
+  int e2 = 0;
+  frexp(amax, &e2);              /* amax = f * 2^e2, f in [0.5, 1): floor(log2 amax) = e2 - 1 */
+  int ex = (e2 - 1) - 2;
+  if (ex < -127) ex = -127;
+  if (ex > 127) ex = 127;
+  *scale = (uint8_t)(ex + 127);
+  for (int i = 0; i < 32; ++i) {
+    const double q = ldexp(fabs(v[i]), -ex);
+    uint32_t best = 0;
+    double bd = q;
+    for (uint32_t c = 1; c < 8u; ++c) {
+      const double d = fabs(q - kE2M1Magnitude[c]);
+      if (d < bd || (d == bd && (c & 1u) == 0u)) {
+        best = c;
+        bd = d;
+      }
+    }
+    const uint32_t code = best | (signbit(v[i]) ? 8u : 0u);
+    codes16[i / 2] |= (uint8_t)((i & 1) ? (code << 4) : code);
+  }
+}
+
+static double mx_value(const uint8_t* codes16, uint8_t scale, int i) {
+  const uint32_t c = (i & 1) ? (codes16[i / 2] >> 4) : (codes16[i / 2] & 15u);
+  return nvo_e2m1(c) * ldexp(1.0, (int)scale - 127);
+}
+
+/* MX-requantise an [n][k] NVFP4 matrix (s_t left out): codes [n][k/2], E8M0
+ * scales [n][k/32]. */
+void nvo_mx_from_nvfp4(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k, uint8_t* mx_codes,
+                       uint8_t* mx_scales) {
+  for (int64_t r = 0; r < n; ++r)
+    for (int64_t b = 0; b < k / 32; ++b) {
+      double v[32];
+      for (int i = 0; i < 32; ++i) v[i] = weight(codes, scales, k, 1.0, r, 32 * b + i);
+      mx_block(v, mx_codes + r * (k / 2) + 16 * b, mx_scales + r * (k / 32) + b);
+    }
+}
+
+/* MX-quantise bf16 activations [m][ldx] (k used): codes [m][k/2], scales [m][k/32]. */
+void nvo_mx_from_bf16(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, uint8_t* mx_codes, uint8_t* mx_scales) {
+  for (int64_t r = 0; r < m; ++r)
+    for (int64_t b = 0; b < k / 32; ++b) {
+      double v[32];
+      for (int i = 0; i < 32; ++i) v[i] = nvo_bf16(x[r * ldx + 32 * b + i]);
+      mx_block(v, mx_codes + r * (k / 2) + 16 * b, mx_scales + r * (k / 32) + b);
+    }
+}
+
+/* y[m][j] = st * sum_k w'[rows[j]][k] x'[m][k] and s[m][j] = st * sum_k |w' x'|
+ * from MX operands (both [..][k/2] codes, [..][k/32] scales). */
+void nvo_mx_gemm(const uint8_t* wc, const uint8_t* ws, int64_t n, int64_t k, float st, const uint8_t* xc,
+                 const uint8_t* xs, int64_t m, const int64_t* rows, int64_t nrows, double* y, double* s,
+                 int nthreads) {
+  if (rows == NULL) nrows = n;
+  if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+  for (int64_t j = 0; j < nrows; ++j) {
+    const int64_t r = rows ? rows[j] : j;
+    for (int64_t t = 0; t < m; ++t) {
+      double acc = 0.0, mag = 0.0;
+      for (int64_t b = 0; b < k / 32; ++b)
+        for (int i = 0; i < 32; ++i) {
+          const double p = mx_value(wc + r * (k / 2) + 16 * b, ws[r * (k / 32) + b], i) *
+                           mx_value(xc + t * (k / 2) + 16 * b, xs[t * (k / 32) + b], i);
+          acc += p;
+          mag += fabs(p);
+        }
+      y[t * nrows + j] = (double)st * acc;
+      if (s) s[t * nrows + j] = (double)st * mag;
+    }
+  }
+}

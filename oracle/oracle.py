@@ -54,6 +54,12 @@ def _load():
     lib.nvo_tensor_scale.argtypes = [P, ctypes.c_int, i64, i64, i64]
     lib.nvo_quantize.restype = None
     lib.nvo_quantize.argtypes = [P, ctypes.c_int, i64, i64, i64, ctypes.c_float, P, P]
+    lib.nvo_mx_from_nvfp4.restype = None
+    lib.nvo_mx_from_nvfp4.argtypes = [P, P, i64, i64, P, P]
+    lib.nvo_mx_from_bf16.restype = None
+    lib.nvo_mx_from_bf16.argtypes = [P, i64, i64, i64, P, P]
+    lib.nvo_mx_gemm.restype = None
+    lib.nvo_mx_gemm.argtypes = [P, P, i64, i64, ctypes.c_float, P, P, i64, P, i64, P, P, ctypes.c_int]
     lib.nvo_max_threads.restype = ctypes.c_int
     lib.nvo_max_threads.argtypes = []
     _lib = lib
@@ -220,3 +226,42 @@ def quantize(w, tensor_scale=None, bf16=None):
     scales = np.zeros((n, k // 16), dtype=np.uint8)
     lib.nvo_quantize(_ptr(w), int(bf16), n, k, k, float(st), _ptr(codes), _ptr(scales))
     return codes, scales, st
+
+
+def mx_from_nvfp4(codes, scales):
+    """MX FP4 requantisation of an NVFP4 matrix (s_t left out): (codes [N][K/2], E8M0 scales [N][K/32])."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    n, kh = codes.shape
+    k = 2 * kh
+    assert k % 32 == 0 and scales.shape == (n, k // 16)
+    mc = np.zeros((n, k // 2), np.uint8)
+    ms = np.zeros((n, k // 32), np.uint8)
+    _load().nvo_mx_from_nvfp4(_ptr(codes), _ptr(scales), n, k, _ptr(mc), _ptr(ms))
+    return mc, ms
+
+
+def mx_from_bf16(x_bits):
+    """MX FP4 quantisation of bf16 activations [M][K]: (codes [M][K/2], E8M0 scales [M][K/32])."""
+    x = _c(x_bits, np.uint16)
+    m, k = x.shape
+    assert k % 32 == 0
+    mc = np.zeros((m, k // 2), np.uint8)
+    ms = np.zeros((m, k // 32), np.uint8)
+    _load().nvo_mx_from_bf16(_ptr(x), m, k, k, _ptr(mc), _ptr(ms))
+    return mc, ms
+
+
+def mx_gemm(wc, ws, tensor_scale, xc, xs, rows=None, nthreads=None):
+    """y[m][j] = s_t * sum_k w'[rows[j]][k] x'[m][k] and s = s_t * sum |w' x'| (fp64) over MX operands."""
+    wc, ws, xc, xs = _c(wc, np.uint8), _c(ws, np.uint8), _c(xc, np.uint8), _c(xs, np.uint8)
+    n, kh = wc.shape
+    m = xc.shape[0]
+    k = 2 * kh
+    r = None if rows is None else _c(rows, np.int64)
+    nr = n if r is None else r.size
+    y = np.empty((m, nr), np.float64)
+    s = np.empty((m, nr), np.float64)
+    _load().nvo_mx_gemm(_ptr(wc), _ptr(ws), n, k, float(tensor_scale), _ptr(xc), _ptr(xs), m,
+                        None if r is None else _ptr(r), nr, _ptr(y), _ptr(s), _threads(nthreads))
+    return y, s
