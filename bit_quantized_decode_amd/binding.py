@@ -28,7 +28,8 @@ EXPORTED = (
     "nvfp4_unpack", "nvfp4_gemv_workspace_bytes", "nvfp4_gemv", "nvfp4_gemm_workspace_bytes", "nvfp4_gemm",
     "nvfp4_gemv_batched_workspace_bytes", "nvfp4_gemv_batched", "nvfp4_gemm_batched_workspace_bytes",
     "nvfp4_gemm_batched", "nvfp4_moe_workspace_bytes", "nvfp4_moe_grouped", "nvfp4_quantize_workspace_bytes",
-    "nvfp4_quantize", "nvfp4_expert_cache_reset", "nvfp4_moe_streamed",
+    "nvfp4_quantize", "nvfp4_expert_cache_reset", "nvfp4_moe_streamed", "nvfp4_mx_packed_bytes", "nvfp4_mx_pack",
+    "nvfp4_mx_unpack", "nvfp4_w4a4_workspace_bytes", "nvfp4_w4a4_gemm",
 )
 
 
@@ -112,6 +113,11 @@ def lib():
         "nvfp4_quantize": (I, [P, I, i64, i64, i64, P, P, P, P, sz, P]),
         "nvfp4_expert_cache_reset": (I, [ctypes.POINTER(ExpertCache)]),
         "nvfp4_moe_streamed": (I, [ctypes.POINTER(MoeArgs), ctypes.POINTER(ExpertCache), P]),
+        "nvfp4_mx_packed_bytes": (I, [i64, i64, ctypes.POINTER(sz)]),
+        "nvfp4_mx_pack": (I, [P, P, i64, i64, P, P]),
+        "nvfp4_mx_unpack": (I, [P, i64, i64, P, P, P]),
+        "nvfp4_w4a4_workspace_bytes": (I, [i64, i64, ctypes.POINTER(sz)]),
+        "nvfp4_w4a4_gemm": (I, [P, i64, i64, ctypes.c_float, P, i64, i64, P, i64, I, P, sz, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -172,6 +178,43 @@ def pack(codes, scales, stream=None):
     packed = torch.empty(packed_bytes(n, k), dtype=torch.uint8, device=codes.device)
     check(lib().nvfp4_pack(_ptr(codes), _ptr(scales), n, k, _ptr(packed), _stream(stream)))
     return packed
+
+
+def mx_packed_bytes(rows, k):
+    out = ctypes.c_size_t()
+    check(lib().nvfp4_mx_packed_bytes(rows, k, ctypes.byref(out)))
+    return out.value
+
+
+def mx_pack(codes, scales, stream=None):
+    """Canonical NVFP4 codes [n][k/2], scales [n][k/16] (device) -> MX tiles for nvfp4_w4a4_gemm."""
+    n, kh = codes.shape
+    k = 2 * kh
+    out = torch.empty(mx_packed_bytes(n, k), dtype=torch.uint8, device=codes.device)
+    check(lib().nvfp4_mx_pack(_ptr(codes), _ptr(scales), n, k, _ptr(out), _stream(stream)))
+    return out
+
+
+def mx_unpack(mx, rows, k, stream=None):
+    codes = torch.empty((rows, k // 2), dtype=torch.uint8, device=mx.device)
+    scales = torch.empty((rows, k // 32), dtype=torch.uint8, device=mx.device)
+    check(lib().nvfp4_mx_unpack(_ptr(mx), rows, k, _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def w4a4_gemm(mx, n, k, tensor_scale, x, y=None, y_dtype=torch.bfloat16, ws=None, stream=None):
+    """y[m][n] = s_t * x' W'^T over MX FP4 operands (see nvfp4_w4a4_gemm); ws receives x's MX tiles."""
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=y_dtype, device=x.device)
+    out = ctypes.c_size_t()
+    check(lib().nvfp4_w4a4_workspace_bytes(m, k, ctypes.byref(out)))
+    if ws is None:
+        ws = workspace(out.value, x.device, kind="w4a4")
+    dt = NVFP4_BF16 if y.dtype == torch.bfloat16 else NVFP4_F32
+    check(lib().nvfp4_w4a4_gemm(_ptr(mx), n, k, float(tensor_scale), _ptr(x), m, x.stride(0), _ptr(y), y.stride(0),
+                                dt, _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    return y
 
 
 def quantize_workspace_bytes():

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libnvfp4.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["pack.hip", "quantize.hip", "gemv.hip", "skinny.hip", "prefill.hip", "moe.hip", "abi.cpp"]
+SOURCES = ["pack.hip", "quantize.hip", "gemv.hip", "skinny.hip", "prefill.hip", "moe.hip", "w4a4.hip", "abi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

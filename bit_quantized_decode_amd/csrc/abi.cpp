@@ -131,6 +131,74 @@ int nvfp4_gemv_workspace_bytes(int64_t n, int64_t k, size_t* bytes) {
   NVFP4_GUARD_END
 }
 
+static int check_mx_shape(int64_t rows, int64_t k) {
+  NVFP4_TRY(check_shape(rows, k));
+  if (k % 32 != 0) return fail(NVFP4_ERR_SHAPE, "k=%lld is not a multiple of 32 (one MX scale per 32 k)", (long long)k);
+  return NVFP4_OK;
+}
+
+int nvfp4_mx_packed_bytes(int64_t rows, int64_t k, size_t* bytes) {
+  NVFP4_GUARD_BEGIN
+  if (!bytes) return fail(NVFP4_ERR_NULL, "bytes is NULL");
+  NVFP4_TRY(check_mx_shape(rows, k));
+  *bytes = nvfp4::mx_packed_bytes(rows, k);
+  return ok();
+  NVFP4_GUARD_END
+}
+
+int nvfp4_mx_pack(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k, void* mx_packed, void* stream) {
+  NVFP4_GUARD_BEGIN
+  NVFP4_TRY(check_mx_shape(n, k));
+  if (n == 0 || k == 0) return ok();
+  if (!codes || !scales || !mx_packed) return fail(NVFP4_ERR_NULL, "codes, scales and mx_packed must be non-NULL");
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(mx_packed))
+    return fail(NVFP4_ERR_ALIGN, "codes, scales and mx_packed must be 16-byte aligned");
+  return hip_status(nvfp4::launch_mx_pack(codes, scales, n, k, mx_packed, (hipStream_t)stream), "mx pack launch");
+  NVFP4_GUARD_END
+}
+
+int nvfp4_mx_unpack(const void* mx_packed, int64_t rows, int64_t k, uint8_t* codes, uint8_t* scales, void* stream) {
+  NVFP4_GUARD_BEGIN
+  NVFP4_TRY(check_mx_shape(rows, k));
+  if (rows == 0 || k == 0) return ok();
+  if (!codes || !scales || !mx_packed) return fail(NVFP4_ERR_NULL, "codes, scales and mx_packed must be non-NULL");
+  if (!aligned16(codes) || !aligned16(mx_packed)) return fail(NVFP4_ERR_ALIGN, "codes and mx_packed must be 16-byte aligned");
+  return hip_status(nvfp4::launch_mx_unpack(mx_packed, rows, k, codes, scales, (hipStream_t)stream), "mx unpack launch");
+  NVFP4_GUARD_END
+}
+
+int nvfp4_w4a4_workspace_bytes(int64_t m, int64_t k, size_t* bytes) {
+  NVFP4_GUARD_BEGIN
+  if (!bytes) return fail(NVFP4_ERR_NULL, "bytes is NULL");
+  NVFP4_TRY(check_mx_shape(m, k));
+  *bytes = nvfp4::mx_packed_bytes(m, k);
+  return ok();
+  NVFP4_GUARD_END
+}
+
+int nvfp4_w4a4_gemm(const void* mx_packed, int64_t n, int64_t k, float tensor_scale, const uint16_t* x, int64_t m,
+                    int64_t ldx, void* y, int64_t ldy, int y_dtype, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  NVFP4_GUARD_BEGIN
+  NVFP4_TRY(check_mx_shape(n, k));
+  if (m < 0 || m > (int64_t(1) << 24)) return fail(NVFP4_ERR_SHAPE, "m=%lld out of range", (long long)m);
+  if (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16) return fail(NVFP4_ERR_DTYPE, "unknown y_dtype %d", y_dtype);
+  if (m == 0 || n == 0) return ok();
+  if (k == 0) return hip_status(nvfp4::launch_zero_rows(y, m, n, ldy, y_dtype == NVFP4_BF16, (hipStream_t)stream), "zero fill");
+  if (ldx < k || ldx % 8 != 0) return fail(NVFP4_ERR_SHAPE, "ldx=%lld must be >= k=%lld and a multiple of 8", (long long)ldx, (long long)k);
+  if (ldy < n) return fail(NVFP4_ERR_SHAPE, "ldy=%lld must be >= n=%lld", (long long)ldy, (long long)n);
+  if (!mx_packed || !x || !y) return fail(NVFP4_ERR_NULL, "mx_packed, x and y must be non-NULL");
+  if (!aligned16(mx_packed) || !aligned16(x) || !aligned16(y)) return fail(NVFP4_ERR_ALIGN, "mx_packed, x and y must be 16-byte aligned");
+  const size_t need = nvfp4::mx_packed_bytes(m, k);
+  if (!workspace || workspace_bytes < need)
+    return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace ? workspace_bytes : 0);
+  if (!aligned16(workspace)) return fail(NVFP4_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return hip_status(nvfp4::launch_w4a4_gemm(mx_packed, n, k, tensor_scale, x, m, ldx, y, ldy, y_dtype == NVFP4_BF16,
+                                            workspace, (hipStream_t)stream),
+                    "w4a4 gemm launch");
+  NVFP4_GUARD_END
+}
+
 int nvfp4_quantize_workspace_bytes(size_t* bytes) {
   NVFP4_GUARD_BEGIN
   if (!bytes) return fail(NVFP4_ERR_NULL, "bytes is NULL");

@@ -356,8 +356,6 @@ size_t gemv_rows_batch_workspace_bytes(const Problem* p, int count, int64_t m) {
   return gemv_batch_workspace_bytes(p, count) == 0 ? 0 : kCounterBytes + (gemv_batch_workspace_bytes(p, count) - kCounterBytes) * (size_t)m;
 }
 
-hipError_t launch_zero_rows(void* y, int64_t m, int64_t n, int64_t ldy, bool y_bf16, hipStream_t s);
-
 hipError_t launch_gemv_rows_batch(const Problem* p, int count, int64_t m, bool y_bf16, void* ws, hipStream_t s) {
   for (int b0 = 0; b0 < count; b0 += kMaxBatch) {
     GemvRowsBatch b = {};

@@ -74,6 +74,13 @@ hipError_t launch_pack(const uint8_t* codes, const uint8_t* scales, const Geomet
 hipError_t launch_unpack(const void* packed, const Geometry& g, uint8_t* codes, uint8_t* scales,
                          hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+// Zero-fill y [m][ldy] (n columns used), fp32 or bf16.
+hipError_t launch_zero_rows(void* y, int64_t m, int64_t n, int64_t ldy, bool y_bf16, hipStream_t s);
+size_t mx_packed_bytes(int64_t rows, int64_t k);
+hipError_t launch_mx_pack(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k, void* dst, hipStream_t s);
+hipError_t launch_mx_unpack(const void* src, int64_t rows, int64_t k, uint8_t* codes, uint8_t* scales, hipStream_t s);
+hipError_t launch_w4a4_gemm(const void* mx_w, int64_t n, int64_t k, float st, const uint16_t* x, int64_t m,
+                            int64_t ldx, void* y, int64_t ldy, bool y_bf16, void* ws, hipStream_t s);
 size_t quantize_workspace_bytes();
 hipError_t launch_quantize(const void* w, bool bf16, int64_t n, int64_t k, int64_t ldw, uint8_t* codes,
                            uint8_t* scales, float* tensor_scale, void* ws, hipStream_t s);

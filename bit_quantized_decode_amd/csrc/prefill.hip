@@ -631,8 +631,6 @@ size_t prefill_workspace_bytes(int64_t m, const Geometry& g) {
   return prefill_batch_workspace_bytes(&pr, 1, m);
 }
 
-hipError_t launch_zero_rows(void* y, int64_t m, int64_t n, int64_t ldy, bool y_bf16, hipStream_t s);
-
 hipError_t launch_prefill_batch(const Problem* p, int count, int64_t m, bool y_bf16, void* ws, hipStream_t s) {
   if (m <= 0) return hipSuccess;
   const size_t esize = y_bf16 ? 2 : 4;

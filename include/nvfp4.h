@@ -164,6 +164,34 @@ int nvfp4_gemm(const void* packed, int64_t n, int64_t k, float tensor_scale,
                void* y, int64_t ldy, int y_dtype,
                void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- f4: W4A4 prefill on the FP4 matrix cores (an approximation) -------------
+ * The pages' prefill runs native FP4 on weights and activations (imp README,
+ * "How does it work?").  gfx950's FP4 matrix instruction takes the OCP MX
+ * format: E2M1 values with one power-of-two (E8M0) scale per 32 k.  Both
+ * operands are requantised to it -- so this product approximates the NVFP4 one
+ * (typically ~2 % of sum|w x| for N(0,1) activations) and is defined by its
+ * own rule:
+ *   block of 32: X = 2^(floor(log2 amax) - 2), exponent clamped to [-127, 127];
+ *   code = E2M1 nearest v / X (ties to even, +-6 beyond 6, sign of v); an
+ *   all-zero block has X = 2^-127 and zero codes;
+ *   weights: the NVFP4 values e2m1 * e4m3 (s_t left out) in blocks along k;
+ *   activations: the bf16 values in blocks along k;
+ *   y[i][j] = s_t * sum_k w'[j][k] x'[i][k]  (fp32 accumulation).
+ * k % 32 == 0.  nvfp4_mx_pack() converts a canonical NVFP4 matrix (once, like
+ * nvfp4_pack) into "MX tiles" of nvfp4_mx_packed_bytes() bytes;
+ * nvfp4_w4a4_gemm() quantises x into the workspace (at least
+ * nvfp4_w4a4_workspace_bytes(m, k), 16-byte aligned; it holds x's MX tiles
+ * after the call) and runs the product.  m <= 2^24.  nvfp4_mx_unpack() (a test
+ * hook) turns MX tiles back into codes [rows][k/2] and E8M0 scales [rows][k/32].
+ */
+int nvfp4_mx_packed_bytes(int64_t rows, int64_t k, size_t* bytes /* host */);
+int nvfp4_mx_pack(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k, void* mx_packed, void* stream);
+int nvfp4_mx_unpack(const void* mx_packed, int64_t rows, int64_t k, uint8_t* codes, uint8_t* scales, void* stream);
+int nvfp4_w4a4_workspace_bytes(int64_t m, int64_t k, size_t* bytes /* host */);
+int nvfp4_w4a4_gemm(const void* mx_packed, int64_t n, int64_t k, float tensor_scale, const uint16_t* x, int64_t m,
+                    int64_t ldx, void* y, int64_t ldy, int y_dtype, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
 /* ---- Batched products: several independent matrices in one launch ----------
  * A decode step multiplies several weight matrices of a layer by their own
  * activations (gate, up, down, QKV, O); the Ignis README's decode round runs

@@ -28,7 +28,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 25, names
     assert set(names) == set(B.EXPORTED)
     for name in names:
         assert hasattr(L, name), name

@@ -1,0 +1,84 @@
+"""GPU parity for the W4A4 product (f4): both operands in the OCP MX FP4 format
+on the FP4 matrix instruction, against the oracle's MX product.  The MX
+operands themselves (weights requantised from NVFP4, activations quantised per
+call) must match the oracle bit for bit; the products within 1e-5 of
+sum |w' x'| (fp32 accumulation)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_quantized_decode_amd import binding as B
+from bit_quantized_decode_amd import inputs as I
+from helpers import (assert_within, bf16_to_f64, device, oracle_threads, random_matrix, sample_rows, to_dev_bf16,
+                     to_dev_u8, ulp_bf16)
+
+pytestmark = pytest.mark.gpu
+
+
+def wide_x(rng, m, k):
+    """N(0,1) activations with row scales 2^-20..2^20, some zeros, negative zeros and bf16 subnormals."""
+    x = rng.standard_normal((m, k)) * np.exp2(rng.uniform(-20, 20, size=(m, 1)))
+    x[rng.random((m, k)) < 0.03] = 0.0
+    x[rng.random((m, k)) < 0.03] = -0.0
+    x = x.astype(np.float32)
+    x[0, :5] = np.float32(1e-39)                     # subnormal
+    u = x.view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("n,k", [(1, 32), (37, 96), (130, 320), (257, 1056)])
+def test_mx_pack_matches_oracle(n, k):
+    dev = device()
+    rng = np.random.default_rng(n + 7 * k)
+    codes, scales = random_matrix(rng, n, k)
+    scales[0, :2] = [0x00, 0x01]                     # a zero and a subnormal block scale
+    mx = B.mx_pack(to_dev_u8(codes, dev), to_dev_u8(scales, dev))
+    c, s = B.mx_unpack(mx, n, k)
+    torch.cuda.synchronize()
+    rc, rs = oracle.mx_from_nvfp4(codes, scales)
+    assert np.array_equal(s.cpu().numpy(), rs)
+    assert np.array_equal(c.cpu().numpy(), rc)
+
+
+@pytest.mark.parametrize("y_dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("m,n,k", [(1, 1, 32), (5, 37, 96), (64, 130, 320), (300, 257, 1056), (513, 200, 2048)])
+def test_w4a4_matches_oracle(m, n, k, y_dtype):
+    dev = device()
+    rng = np.random.default_rng(m * 101 + n * 7 + k)
+    codes, scales = random_matrix(rng, n, k)
+    xb = wide_x(rng, m, k)
+    mx = B.mx_pack(to_dev_u8(codes, dev), to_dev_u8(scales, dev))
+    ws = torch.zeros(B.mx_packed_bytes(m, k), dtype=torch.uint8, device=dev)
+    y = B.w4a4_gemm(mx, n, k, I.TENSOR_SCALE, to_dev_bf16(xb, dev), y_dtype=y_dtype, ws=ws)
+    xc, xs = B.mx_unpack(ws, m, k)                   # the activations as the kernel quantised them
+    torch.cuda.synchronize()
+    rxc, rxs = oracle.mx_from_bf16(xb)
+    assert np.array_equal(xs.cpu().numpy(), rxs) and np.array_equal(xc.cpu().numpy(), rxc)
+    wc, wsc = oracle.mx_from_nvfp4(codes, scales)
+    y_ref, s = oracle.mx_gemm(wc, wsc, I.TENSOR_SCALE, rxc, rxs, nthreads=oracle_threads())
+    got = y.cpu().numpy().astype(np.float64) if y_dtype == torch.float32 else bf16_to_f64(y)
+    extra = 0.0 if y_dtype == torch.float32 else ulp_bf16(y_ref)
+    assert_within(got, y_ref, s, extra=extra, what=f"w4a4 {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("mat", I.PREFILL_MATRICES, ids=lambda m: m.name)
+def test_w4a4_prefill_full_size(mat):
+    """The 512-token prefill's matrices, sampled weight rows x all tokens; also
+    reports how far W4A4 lands from the exact NVFP4 product."""
+    dev = device()
+    codes, scales = I.nvfp4_matrix(I.PREFILL_512, mat.matrix_id, mat.n, mat.k)
+    x = I.activations(I.PREFILL_512, mat.matrix_id, 512, mat.k)
+    mx = B.mx_pack(to_dev_u8(codes, dev), to_dev_u8(scales, dev))
+    y = B.w4a4_gemm(mx, mat.n, mat.k, I.TENSOR_SCALE, to_dev_bf16(x, dev), y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = sample_rows(mat.n, 48, 500 + mat.matrix_id)
+    wc, wsc = oracle.mx_from_nvfp4(codes, scales)
+    xc, xs = oracle.mx_from_bf16(x)
+    y_ref, s = oracle.mx_gemm(wc, wsc, I.TENSOR_SCALE, xc, xs, rows=rows, nthreads=oracle_threads())
+    got = y.cpu().numpy().astype(np.float64)[:, rows]
+    assert_within(got, y_ref, s, what=f"w4a4 {mat.name}")
+    ye, se = oracle.gemm(codes, scales, I.TENSOR_SCALE, x, rows=rows, nthreads=oracle_threads())
+    rel = np.abs(got - ye) / se
+    print(f"W4A4 vs exact NVFP4 ({mat.name}): median {np.median(rel):.3g}, max {rel.max():.3g} of sum|w x|")
+    assert np.median(rel) < 0.05
