@@ -91,7 +91,8 @@ def parse():
     p.add_argument("--rows", default="decode_b1,decode_b32,moe,prefill",
                    help="rows to run; optional, not default: quantize (the NVFP4 quantiser over the layer), "
                         "decode_m2 .. decode_m8 (the layer at decode widths 2..8), head_b1 (the output head, batch 1), "
-                        "moe_stream (the MoE layer with experts streamed from host memory)")
+                        "moe_stream (the MoE layer with experts streamed from host memory), prefill_w4a4 (the prefill "
+                        "products as W4A4 on the FP4 matrix cores)")
     p.add_argument("--order", default="prefill,moe,decode_b32,decode_b1",
                    help="row order within a step (the batch-1 GEMV last: see the note at the plan)")
     p.add_argument("--graphs", action="store_true", help="replay per-row HIP graphs instead of direct launches")
@@ -274,6 +275,22 @@ def main():
     def row_pre(cp):
         pre_calls[cp]()
 
+    # ---- optional: the same three prefill products as W4A4 (both operands in
+    # MX FP4 on the FP4 matrix cores; an approximation of the NVFP4 product) ---
+    w4_mx, w4_x, w4_y = [[None] * len(pre) for _ in range(2)], [], []
+    if "prefill_w4a4" in rows:
+        for j, mat in enumerate(pre):
+            c, s_ = I.nvfp4_matrix(I.PREFILL_512, mat.matrix_id, mat.n, mat.k)
+            m0 = B.mx_pack(u8(c), u8(s_))
+            w4_mx[0][j], w4_mx[1][j] = m0, m0.clone()
+            w4_x.append(bf16(I.activations(I.PREFILL_512, mat.matrix_id, 512, mat.k)))
+            w4_y.append(torch.empty((512, mat.n), dtype=torch.bfloat16, device=dev))
+        ws_w4 = B.workspace(max(B.mx_packed_bytes(512, m.k) for m in pre), dev, kind="w4a4")
+
+    def row_w4(cp):
+        for j, mat in enumerate(pre):
+            B.w4a4_gemm(w4_mx[cp][j], mat.n, mat.k, I.TENSOR_SCALE, w4_x[j], y=w4_y[j], ws=ws_w4)
+
     # ---- optional: the NVFP4 quantiser over the layer's five matrices (bf16 in) ----
     q_w, q_out, q_bytes = [], [], 0
     if "quantize" in rows:
@@ -304,6 +321,7 @@ def main():
         "decode_b1": ("decode_b1", row_b1, dense_copies, lambda i: (2 * i) % dense_copies, y1),
         "quantize": ("quantize", row_q, 1, lambda i: 0, [c for c, _, _ in q_out]),
         "moe_stream": ("moe_stream", run_moe_stream, 64, lambda i: i % 64, None),
+        "prefill_w4a4": ("prefill_w4a4", row_w4, 2, lambda i: i % 2, w4_y),
     }
     for r, (calls, ncp, outs, _, _) in extra_rows.items():
         plan_all[r] = (r, (lambda cp, c=calls: c[cp]()), ncp, (lambda i, n_=ncp: (2 * i + 1) % n_), outs)
@@ -416,6 +434,11 @@ def main():
                                   "frac_mfma_bf16": pre_flops / s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                                   "GB/s": pre_bytes / s / 1e9, "equiv_tok_s": pre_flops / s / (2 * 27e9)}
 
+    if "prefill_w4a4" in seg:
+        s = seg["prefill_w4a4"] * 1e-3
+        result_rows["prefill_w4a4"] = {"TFLOP/s": pre_flops / s / 1e12, "us": s * 1e6,
+                                       "frac_mfma_fp4": pre_flops / s / 1e12 / 10100.0,
+                                       "frac_mfma_bf16": pre_flops / s / 1e12 / MFMA_BF16_PEAK_TFLOPS}
     if "moe_stream" in seg:
         s = seg["moe_stream"] * 1e-3
         st_timed = stream_state["stats"][-args.steps:]

@@ -152,30 +152,14 @@ __global__ __launch_bounds__(256) void mx_unpack_kernel(const uint8_t* __restric
   }
 }
 
-// The product: a workgroup of four wavefronts computes 128 weight rows x 256
-// activation rows; wavefront w owns weight rows 32 w .. 32 w + 31 (one A
-// operand per 64-k step) against the 8 activation blocks (eight B operands),
-// eight MFMAs per step; the next step's operands load while this step's
-// MFMAs run.
-constexpr int kWJT = 8;
-
-struct MxOps {
-  u32x4 a;
-  uint32_t sa;
-  u32x4 b[kWJT];
-  uint32_t sb[kWJT];
-};
-
-__device__ __forceinline__ void load_ops(const uint8_t* wa, const uint8_t* wsc, const uint8_t* xa, const uint8_t* xsc,
-                                         int64_t a_blk, const int64_t (&b_blk)[kWJT], int lane, MxOps& o) {
-  o.a = *reinterpret_cast<const u32x4*>(wa + a_blk * 1024 + lane * 16);
-  o.sa = wsc[a_blk * 64 + lane];
-#pragma unroll
-  for (int j = 0; j < kWJT; ++j) {
-    o.b[j] = *reinterpret_cast<const u32x4*>(xa + b_blk[j] * 1024 + lane * 16);
-    o.sb[j] = xsc[b_blk[j] * 64 + lane];
-  }
-}
+// The product: a workgroup of four wavefronts computes 256 weight rows x 128
+// activation rows.  Wavefront w owns weight blocks 2w and 2w + 1 (two A
+// operands per 64-k step, loaded one step ahead into registers); the four
+// activation blocks of a step (four B operands) are staged once per workgroup
+// in LDS, double-buffered, one 16-byte load per thread; each wavefront then
+// runs 2 x 4 MFMAs per step.
+constexpr int kWJT = 4;        // activation blocks of 32 rows per workgroup
+constexpr int kBStage = kWJT * 1024 + kWJT * 64;  // LDS bytes of one step's B operands
 
 __device__ __forceinline__ v8i widen(u32x4 q) {
   return v8i{(int)q[0], (int)q[1], (int)q[2], (int)q[3], 0, 0, 0, 0};
@@ -184,53 +168,102 @@ __device__ __forceinline__ v8i widen(u32x4 q) {
 __global__ __launch_bounds__(256, 2) void w4a4_gemm_kernel(const uint8_t* __restrict__ w, MxGeom gw,
                                                            const uint8_t* __restrict__ xm, MxGeom gx, float st,
                                                            void* __restrict__ y, int64_t ldy, int y_bf16) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int64_t wrb = (int64_t)blockIdx.x * 4 + wave;           // this wavefront's 32-row weight block
-  const int64_t xrb0 = (int64_t)blockIdx.y * kWJT;              // first activation block
+  __shared__ __attribute__((aligned(16))) uint8_t sb0[kBStage];
+  __shared__ __attribute__((aligned(16))) uint8_t sb1[kBStage];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int64_t nks = gw.nks;
-  const int64_t wrb_c = wrb < gw.nrb ? wrb : gw.nrb - 1;        // past the end: re-read the last block (not stored)
-  int64_t xrb[kWJT];
+  // This wavefront's two weight blocks (past the end: the last block, not stored).
+  int64_t wrb[2];
 #pragma unroll
-  for (int j = 0; j < kWJT; ++j) xrb[j] = xrb0 + j < gx.nrb ? xrb0 + j : gx.nrb - 1;
+  for (int i = 0; i < 2; ++i) {
+    const int64_t r = (int64_t)blockIdx.x * 8 + 2 * wave + i;
+    wrb[i] = r < gw.nrb ? r : gw.nrb - 1;
+  }
   const uint8_t* wsc = w + gw.scale_offset;
+  // The B block this thread stages: codes of block tid / 64 (16 bytes at lane), and
+  // for threads 0..15 a 16-byte run of the blocks' scales.
+  const int sblk = tid >> 6;
+  int64_t xrb = (int64_t)blockIdx.y * kWJT + sblk;
+  xrb = xrb < gx.nrb ? xrb : gx.nrb - 1;
+  const int64_t scb = (int64_t)blockIdx.y * kWJT + (tid >> 2);  // threads 0..15: block tid / 4, 16 scale bytes
+  const int64_t scb_c = scb < gx.nrb ? scb : gx.nrb - 1;
   const uint8_t* xsc = xm + gx.scale_offset;
-  f32x16 acc[kWJT];
+  auto load_b = [&](int64_t ks, u32x4& codes, u32x4& scales) __attribute__((always_inline)) {
+    codes = *reinterpret_cast<const u32x4*>(xm + (xrb * nks + ks) * 1024 + lane * 16);
+    if (tid < 16) scales = *reinterpret_cast<const u32x4*>(xsc + (scb_c * nks + ks) * 64 + (tid & 3) * 16);
+  };
+  auto store_b = [&](uint8_t* buf, u32x4 codes, u32x4 scales) __attribute__((always_inline)) {
+    *reinterpret_cast<u32x4*>(buf + sblk * 1024 + lane * 16) = codes;
+    if (tid < 16) *reinterpret_cast<u32x4*>(buf + kWJT * 1024 + (tid >> 2) * 64 + (tid & 3) * 16) = scales;
+  };
+  auto load_a = [&](int64_t ks, u32x4 (&a)[2], uint32_t (&sa)[2]) __attribute__((always_inline)) {
 #pragma unroll
-  for (int j = 0; j < kWJT; ++j) acc[j] = f32x16{};
-  int64_t bb[kWJT];
-  MxOps cur, nxt;
+    for (int i = 0; i < 2; ++i) {
+      a[i] = *reinterpret_cast<const u32x4*>(w + (wrb[i] * nks + ks) * 1024 + lane * 16);
+      sa[i] = wsc[(wrb[i] * nks + ks) * 64 + lane];
+    }
+  };
+  f32x16 acc[2][kWJT];
 #pragma unroll
-  for (int j = 0; j < kWJT; ++j) bb[j] = xrb[j] * nks;
-  load_ops(w, wsc, xm, xsc, wrb_c * nks, bb, lane, cur);
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < kWJT; ++j) acc[i][j] = f32x16{};
+  u32x4 a[2], an[2], bc, bs = u32x4{0u, 0u, 0u, 0u};
+  uint32_t sa[2], san[2];
+  load_a(0, a, sa);
+  load_b(0, bc, bs);
+  store_b(sb0, bc, bs);
+  __syncthreads();
   for (int64_t ks = 0; ks < nks; ++ks) {
     const int64_t kn = ks + 1 < nks ? ks + 1 : ks;
-    int64_t bn[kWJT];
+    load_a(kn, an, san);
+    load_b(kn, bc, bs);
+    const uint8_t* cur = (ks & 1) ? sb1 : sb0;
+    u32x4 b[kWJT];
+    uint32_t sbv[kWJT];
 #pragma unroll
-    for (int j = 0; j < kWJT; ++j) bn[j] = xrb[j] * nks + kn;
-    load_ops(w, wsc, xm, xsc, wrb_c * nks + kn, bn, lane, nxt);
-    const v8i a = widen(cur.a);
+    for (int j = 0; j < kWJT; ++j) {
+      b[j] = *reinterpret_cast<const u32x4*>(cur + j * 1024 + lane * 16);
+      sbv[j] = cur[kWJT * 1024 + j * 64 + lane];
+    }
 #pragma unroll
-    for (int j = 0; j < kWJT; ++j)
-      acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, widen(cur.b[j]), acc[j], 4, 4, 0, (int)cur.sa, 0,
-                                                               (int)cur.sb[j]);
-    cur = nxt;
+    for (int i = 0; i < 2; ++i) {
+      const v8i av = widen(a[i]);
+#pragma unroll
+      for (int j = 0; j < kWJT; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, widen(b[j]), acc[i][j], 4, 4, 0, (int)sa[i], 0,
+                                                                    (int)sbv[j]);
+    }
+    store_b((ks & 1) ? sb0 : sb1, bc, bs);  // the other buffer: read by no wavefront this step
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      a[i] = an[i];
+      sa[i] = san[i];
+    }
   }
-  if (wrb >= gw.nrb) return;
-  // acc[j] element e: weight row 32 wrb + 8 (e / 4) + 4 (lane / 32) + e % 4, activation row 32 (xrb0 + j) + lane % 32.
+  // acc[i][j] element e: weight row 32 wrb_i + 8 (e / 4) + 4 (lane / 32) + e % 4,
+  // activation row 32 (4 blockIdx.y + j) + lane % 32.
 #pragma unroll
-  for (int j = 0; j < kWJT; ++j) {
-    const int64_t arow = 32 * (xrb0 + j) + (lane & 31);
-    if (xrb0 + j >= gx.nrb || arow >= gx.rows) continue;
+  for (int i = 0; i < 2; ++i) {
+    const int64_t rb = (int64_t)blockIdx.x * 8 + 2 * wave + i;
+    if (rb >= gw.nrb) continue;
 #pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      const int64_t col = 32 * wrb + 8 * e4 + 4 * (lane >> 5);
+    for (int j = 0; j < kWJT; ++j) {
+      const int64_t arow = 32 * ((int64_t)blockIdx.y * kWJT + j) + (lane & 31);
+      if (arow >= gx.rows) continue;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (col + c >= gw.rows) continue;
-        const float v = acc[j][4 * e4 + c] * st;
-        if (y_bf16) static_cast<uint16_t*>(y)[arow * ldy + col + c] = to_bf16(v);
-        else static_cast<float*>(y)[arow * ldy + col + c] = v;
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int64_t col = 32 * rb + 8 * e4 + 4 * (lane >> 5);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (col + c >= gw.rows) continue;
+          const float v = acc[i][j][4 * e4 + c] * st;
+          if (y_bf16) static_cast<uint16_t*>(y)[arow * ldy + col + c] = to_bf16(v);
+          else static_cast<float*>(y)[arow * ldy + col + c] = v;
+        }
       }
     }
   }
@@ -274,7 +307,7 @@ hipError_t launch_w4a4_gemm(const void* mx_w, int64_t n, int64_t k, float st, co
   const hipError_t e = launch_mx_quant_act(x, m, k, ldx, ws, s);
   if (e != hipSuccess) return e;
   const MxGeom gw = mx_geom(n, k), gx = mx_geom(m, k);
-  const dim3 grid((unsigned)((gw.nrb + 3) / 4), (unsigned)((gx.nrb + kWJT - 1) / kWJT));
+  const dim3 grid((unsigned)((gw.nrb + 7) / 8), (unsigned)((gx.nrb + kWJT - 1) / kWJT));
   hipLaunchKernelGGL(w4a4_gemm_kernel, grid, dim3(256), 0, s, static_cast<const uint8_t*>(mx_w), gw,
                      static_cast<const uint8_t*>(ws), gx, st, y, ldy, y_bf16 ? 1 : 0);
   return hipGetLastError();
