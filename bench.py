@@ -285,11 +285,13 @@ def main():
             w4_mx[0][j], w4_mx[1][j] = m0, m0.clone()
             w4_x.append(bf16(I.activations(I.PREFILL_512, mat.matrix_id, 512, mat.k)))
             w4_y.append(torch.empty((512, mat.n), dtype=torch.bfloat16, device=dev))
-        ws_w4 = B.workspace(max(B.mx_packed_bytes(512, m.k) for m in pre), dev, kind="w4a4")
+        w4_items = [[(w4_mx[cp][j], mat.n, mat.k, I.TENSOR_SCALE, w4_x[j], w4_y[j]) for j, mat in enumerate(pre)]
+                    for cp in range(2)]
+        ws_w4 = B.workspace(B.w4a4_batched_workspace_bytes(w4_items[0], 512), dev, kind="w4a4")
+        w4_calls = [B.w4a4_batched_prepared(w4_items[cp], ws=ws_w4) for cp in range(2)]
 
     def row_w4(cp):
-        for j, mat in enumerate(pre):
-            B.w4a4_gemm(w4_mx[cp][j], mat.n, mat.k, I.TENSOR_SCALE, w4_x[j], y=w4_y[j], ws=ws_w4)
+        w4_calls[cp]()
 
     # ---- optional: the NVFP4 quantiser over the layer's five matrices (bf16 in) ----
     q_w, q_out, q_bytes = [], [], 0

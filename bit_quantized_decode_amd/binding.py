@@ -29,7 +29,8 @@ EXPORTED = (
     "nvfp4_gemv_batched_workspace_bytes", "nvfp4_gemv_batched", "nvfp4_gemm_batched_workspace_bytes",
     "nvfp4_gemm_batched", "nvfp4_moe_workspace_bytes", "nvfp4_moe_grouped", "nvfp4_quantize_workspace_bytes",
     "nvfp4_quantize", "nvfp4_expert_cache_reset", "nvfp4_moe_streamed", "nvfp4_mx_packed_bytes", "nvfp4_mx_pack",
-    "nvfp4_mx_unpack", "nvfp4_w4a4_workspace_bytes", "nvfp4_w4a4_gemm",
+    "nvfp4_mx_unpack", "nvfp4_w4a4_workspace_bytes", "nvfp4_w4a4_gemm", "nvfp4_w4a4_batched_workspace_bytes",
+    "nvfp4_w4a4_batched",
 )
 
 
@@ -118,6 +119,8 @@ def lib():
         "nvfp4_mx_unpack": (I, [P, i64, i64, P, P, P]),
         "nvfp4_w4a4_workspace_bytes": (I, [i64, i64, ctypes.POINTER(sz)]),
         "nvfp4_w4a4_gemm": (I, [P, i64, i64, ctypes.c_float, P, i64, i64, P, i64, I, P, sz, P]),
+        "nvfp4_w4a4_batched_workspace_bytes": (I, [ctypes.POINTER(Problem), I, i64, ctypes.POINTER(sz)]),
+        "nvfp4_w4a4_batched": (I, [ctypes.POINTER(Problem), I, i64, I, P, sz, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -202,19 +205,66 @@ def mx_unpack(mx, rows, k, stream=None):
     return codes, scales
 
 
+def w4a4_workspace_bytes(m, k):
+    out = ctypes.c_size_t()
+    check(lib().nvfp4_w4a4_workspace_bytes(m, k, ctypes.byref(out)))
+    return out.value
+
+
+def w4a4_x_tiles(ws, m, k):
+    """The MX tiles of x that the last nvfp4_w4a4_gemm left in workspace ws."""
+    off = w4a4_workspace_bytes(m, k) - mx_packed_bytes(m, k)
+    return ws[off:off + mx_packed_bytes(m, k)]
+
+
 def w4a4_gemm(mx, n, k, tensor_scale, x, y=None, y_dtype=torch.bfloat16, ws=None, stream=None):
-    """y[m][n] = s_t * x' W'^T over MX FP4 operands (see nvfp4_w4a4_gemm); ws receives x's MX tiles."""
+    """y[m][n] = s_t * x' W'^T over MX FP4 operands (see nvfp4_w4a4_gemm); ws (zeroed
+    before its first use) receives the schedule's counters and x's MX tiles."""
     m = x.shape[0]
     if y is None:
         y = torch.empty((m, n), dtype=y_dtype, device=x.device)
-    out = ctypes.c_size_t()
-    check(lib().nvfp4_w4a4_workspace_bytes(m, k, ctypes.byref(out)))
     if ws is None:
-        ws = workspace(out.value, x.device, kind="w4a4")
+        ws = workspace(w4a4_workspace_bytes(m, k), x.device, kind="w4a4")
     dt = NVFP4_BF16 if y.dtype == torch.bfloat16 else NVFP4_F32
     check(lib().nvfp4_w4a4_gemm(_ptr(mx), n, k, float(tensor_scale), _ptr(x), m, x.stride(0), _ptr(y), y.stride(0),
                                 dt, _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
     return y
+
+
+def w4a4_batched_workspace_bytes(items, m):
+    """Workspace bytes nvfp4_w4a4_batched needs for these problems at m activation rows."""
+    need = ctypes.c_size_t()
+    check(lib().nvfp4_w4a4_batched_workspace_bytes(problems(items), len(items), m, ctypes.byref(need)))
+    return need.value
+
+
+def w4a4_batched(items, ws=None, stream=None):
+    """Several W4A4 products sharing m and the output dtype:
+    items = [(mx_tiles, n, k, tensor_scale, x [m][ldx], y [m][ldy])]."""
+    arr = problems(items)
+    m = items[0][4].shape[0] if items else 0
+    dt = NVFP4_BF16 if items and items[0][5].dtype == torch.bfloat16 else NVFP4_F32
+    if ws is None and items:
+        ws = workspace(w4a4_batched_workspace_bytes(items, m), items[0][4].device, kind="w4a4")
+    check(lib().nvfp4_w4a4_batched(arr, len(items), m, dt, _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def w4a4_batched_prepared(items, ws=None, stream=None):
+    """nvfp4_w4a4_batched with its arguments marshalled once: returns a
+    zero-argument callable that only makes the library call."""
+    arr = problems(items)
+    m = items[0][4].shape[0] if items else 0
+    dt = NVFP4_BF16 if items and items[0][5].dtype == torch.bfloat16 else NVFP4_F32
+    if ws is None and items:
+        ws = workspace(w4a4_batched_workspace_bytes(items, m), items[0][4].device, kind="w4a4")
+    fn, n, wsp, wsb = lib().nvfp4_w4a4_batched, len(items), _ptr(ws), 0 if ws is None else ws.numel()
+    keep = (items, ws)
+
+    def call():
+        check(fn(arr, n, m, dt, wsp, wsb, _stream(stream)))
+        return keep
+
+    return call
 
 
 def quantize_workspace_bytes():

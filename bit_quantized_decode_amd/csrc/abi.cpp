@@ -171,7 +171,7 @@ int nvfp4_w4a4_workspace_bytes(int64_t m, int64_t k, size_t* bytes) {
   NVFP4_GUARD_BEGIN
   if (!bytes) return fail(NVFP4_ERR_NULL, "bytes is NULL");
   NVFP4_TRY(check_mx_shape(m, k));
-  *bytes = nvfp4::mx_packed_bytes(m, k);
+  *bytes = nvfp4::w4a4_workspace_bytes(m, k);
   return ok();
   NVFP4_GUARD_END
 }
@@ -181,6 +181,7 @@ int nvfp4_w4a4_gemm(const void* mx_packed, int64_t n, int64_t k, float tensor_sc
                     void* stream) {
   NVFP4_GUARD_BEGIN
   NVFP4_TRY(check_mx_shape(n, k));
+  NVFP4_TRY(check_rows(n));
   if (m < 0 || m > (int64_t(1) << 24)) return fail(NVFP4_ERR_SHAPE, "m=%lld out of range", (long long)m);
   if (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16) return fail(NVFP4_ERR_DTYPE, "unknown y_dtype %d", y_dtype);
   if (m == 0 || n == 0) return ok();
@@ -189,7 +190,7 @@ int nvfp4_w4a4_gemm(const void* mx_packed, int64_t n, int64_t k, float tensor_sc
   if (ldy < n) return fail(NVFP4_ERR_SHAPE, "ldy=%lld must be >= n=%lld", (long long)ldy, (long long)n);
   if (!mx_packed || !x || !y) return fail(NVFP4_ERR_NULL, "mx_packed, x and y must be non-NULL");
   if (!aligned16(mx_packed) || !aligned16(x) || !aligned16(y)) return fail(NVFP4_ERR_ALIGN, "mx_packed, x and y must be 16-byte aligned");
-  const size_t need = nvfp4::mx_packed_bytes(m, k);
+  const size_t need = nvfp4::w4a4_workspace_bytes(m, k);
   if (!workspace || workspace_bytes < need)
     return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace ? workspace_bytes : 0);
   if (!aligned16(workspace)) return fail(NVFP4_ERR_ALIGN, "workspace must be 16-byte aligned");
@@ -412,6 +413,44 @@ int nvfp4_gemv_batched(const nvfp4_problem* problems, int count, void* workspace
     return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace ? workspace_bytes : 0);
   if (need > 0 && !aligned16(workspace)) return fail(NVFP4_ERR_ALIGN, "workspace must be 16-byte aligned");
   return hip_status(nvfp4::launch_gemv_batch(pr.data(), count, workspace, (hipStream_t)stream), "gemv batch launch");
+  NVFP4_GUARD_END
+}
+
+// W4A4 batches: the gemm batch's checks, and k % 32 == 0 for the MX scales.
+static int check_w4a4_batch(const nvfp4_problem* pr, int count, int64_t m, int y_dtype, bool need_buffers,
+                            nvfp4::Problem* out) {
+  if (m < 0 || m > (int64_t(1) << 24)) return fail(NVFP4_ERR_SHAPE, "m=%lld out of range", (long long)m);
+  NVFP4_TRY(check_batch(pr, count, m, y_dtype, need_buffers, out));
+  for (int i = 0; i < count; ++i)
+    if (pr[i].k % 32 != 0)
+      return fail(NVFP4_ERR_SHAPE, "problem %d: k=%lld is not a multiple of 32 (one MX scale per 32 k)", i,
+                  (long long)pr[i].k);
+  return NVFP4_OK;
+}
+
+int nvfp4_w4a4_batched_workspace_bytes(const nvfp4_problem* problems, int count, int64_t m, size_t* bytes) {
+  NVFP4_GUARD_BEGIN
+  if (!bytes) return fail(NVFP4_ERR_NULL, "bytes is NULL");
+  std::vector<nvfp4::Problem> pr((size_t)(count > 0 ? count : 0));
+  NVFP4_TRY(check_w4a4_batch(problems, count, m, NVFP4_F32, false, pr.data()));
+  *bytes = nvfp4::w4a4_batch_workspace_bytes(pr.data(), count, m);
+  return ok();
+  NVFP4_GUARD_END
+}
+
+int nvfp4_w4a4_batched(const nvfp4_problem* problems, int count, int64_t m, int y_dtype, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  NVFP4_GUARD_BEGIN
+  std::vector<nvfp4::Problem> pr((size_t)(count > 0 ? count : 0));
+  NVFP4_TRY(check_w4a4_batch(problems, count, m, y_dtype, true, pr.data()));
+  if (count == 0 || m == 0) return ok();
+  const size_t need = nvfp4::w4a4_batch_workspace_bytes(pr.data(), count, m);
+  if (!workspace || workspace_bytes < need)
+    return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace ? workspace_bytes : 0);
+  if (!aligned16(workspace)) return fail(NVFP4_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return hip_status(nvfp4::launch_w4a4_gemm_batch(pr.data(), count, m, y_dtype == NVFP4_BF16, workspace,
+                                                  (hipStream_t)stream),
+                    "w4a4 batch launch");
   NVFP4_GUARD_END
 }
 

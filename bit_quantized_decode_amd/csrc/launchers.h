@@ -79,6 +79,24 @@ hipError_t launch_zero_rows(void* y, int64_t m, int64_t n, int64_t ldy, bool y_b
 size_t mx_packed_bytes(int64_t rows, int64_t k);
 hipError_t launch_mx_pack(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k, void* dst, hipStream_t s);
 hipError_t launch_mx_unpack(const void* src, int64_t rows, int64_t k, uint8_t* codes, uint8_t* scales, hipStream_t s);
+// W4A4 product: x quantised to MX tiles in the workspace, then the stream-K
+// prefill schedule with MX operands (workspace: its counters and partial sums
+// first, w4a4_streamk_bytes(), then x's MX tiles).
+struct MxProblem {
+  const uint8_t* w;  // weight MX tiles
+  int64_t n, k;
+  float st;
+  const uint8_t* x;  // activation MX tiles (m rows)
+  void* y;
+  int64_t ldy;
+};
+size_t w4a4_streamk_bytes();
+hipError_t launch_w4a4_batch(const MxProblem* p, int count, int64_t m, bool y_bf16, void* ws, hipStream_t s);
+// Batches: Problem::packed holds the weights' MX tiles; x is quantised into
+// the workspace after the stream-K area, problem after problem.
+size_t w4a4_batch_workspace_bytes(const Problem* p, int count, int64_t m);
+hipError_t launch_w4a4_gemm_batch(const Problem* p, int count, int64_t m, bool y_bf16, void* ws, hipStream_t s);
+size_t w4a4_workspace_bytes(int64_t m, int64_t k);
 hipError_t launch_w4a4_gemm(const void* mx_w, int64_t n, int64_t k, float st, const uint16_t* x, int64_t m,
                             int64_t ldx, void* y, int64_t ldy, bool y_bf16, void* ws, hipStream_t s);
 size_t quantize_workspace_bytes();

@@ -56,6 +56,12 @@ struct PrefillBatch {
   void* y[kMaxPre];
   int64_t n[kMaxPre], k[kMaxPre], ldx[kMaxPre], ldy[kMaxPre];
   float st[kMaxPre];
+  // MX operands (W4A4): `packed` holds the weights' MX codes, these the rest.
+  const uint8_t* wsc[kMaxPre];  // weight scale bytes
+  const uint8_t* xm[kMaxPre];   // activation codes, first row block of the launch
+  const uint8_t* xsc[kMaxPre];  // activation scale bytes, same block
+  int64_t nrb[kMaxPre];         // weight row blocks of 32
+  int64_t xnrb;                 // activation row blocks of 32 in the launch
 };
 
 // One problem's fields, as the kernel uses them.
@@ -67,6 +73,8 @@ struct ProbView {
   int64_t n, k, ldx, ldy;
   float st;
   int tile_base, iters, nkt, nrt, ntn;
+  const uint8_t *wsc, *xm, *xsc;
+  int64_t nrb;
 };
 
 // Share w covers global iterations [share_begin(w), share_begin(w + 1)).
@@ -210,7 +218,7 @@ __device__ __forceinline__ void stage_half(const f32x16 (&acc)[2][JT], uint8_t* 
 }
 
 
-template <int JT, bool KFULL>
+template <int JT, bool KFULL, bool MX>
 __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillBatch b, unsigned* __restrict__ counters,
                                                          float* __restrict__ partials) {
   constexpr int kBM = 32 * JT;
@@ -254,7 +262,8 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillBatch b, u
 #pragma unroll
     for (int i = 0; i < kMaxPre; ++i)
       if (i == p) pv = ProbView{b.iter_begin[i], b.packed[i], b.x[i], b.y[i], b.n[i], b.k[i], b.ldx[i], b.ldy[i],
-                                b.st[i], b.tile_base[i], b.iters[i], b.nkt[i], b.nrt[i], b.ntn[i]};
+                                b.st[i], b.tile_base[i], b.iters[i], b.nkt[i], b.nrt[i], b.ntn[i],
+                                b.wsc[i], b.xm[i], b.xsc[i], b.nrb[i]};
     const int iters = pv.iters;
     const int64_t gl = g - pv.iter_begin;
     const int tile = (int)(gl / iters);
@@ -267,142 +276,254 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillBatch b, u
     const int64_t kdim = pv.k;
     const int nkt = pv.nkt;
 
-    // Activations go from memory straight into LDS: load j of this wavefront
-    // fills the 1 KB block q = wave * JT + j of a buffer, lane l landing at
-    // byte 16 l -- row 8 q + l / 8, physical chunk l % 8 -- so lane l fetches
-    // the logical chunk that the swizzle puts there.  Rows past m re-read row
-    // m - 1 (their outputs are not written).
-    const uint16_t* xrow[JT];
-    int c8[JT];  // k offset (elements) of this lane's chunk within an iteration
-#pragma unroll
-    for (int j = 0; j < JT; ++j) {
-      const int row = 8 * (wave * JT + j) + (lane >> 3);
-      c8[j] = 8 * ((lane & 7) ^ swz_key(row));
-      int64_t r = m0 + row;
-      r = r < b_m ? r : b_m - 1;
-      xrow[j] = pv.x + r * pv.ldx;
-    }
-    auto dma_x = [&](int it, uint8_t* xbuf) __attribute__((always_inline)) {
-      uint8_t* dst = xbuf + wave * JT * 1024;
-#pragma unroll
-      for (int j = 0; j < JT; ++j) {
-        int64_t kk = (int64_t)it * kBK + c8[j];
-        if (!KFULL) kk = kk < kdim ? kk : kdim - 8;  // in bounds; zeroed once landed
-        load_lds16(xrow[j] + kk, dst + j * 1024);
-      }
-    };
-    // Iteration it's chunks at k >= K must read as zeros (K % 64 != 0 only):
-    // each lane clears the chunks it loaded, after they have landed.
-    auto zero_tail = [&](int it, uint8_t* xbuf) __attribute__((always_inline)) {
-      if (KFULL || it != iters - 1) return;
-#pragma unroll
-      for (int j = 0; j < JT; ++j)
-        if ((int64_t)it * kBK + c8[j] >= kdim)
-          *reinterpret_cast<u32x4*>(xbuf + (wave * JT + j) * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
-    };
-
-    // Weight source: this wavefront's packed row tile (clamped; rows past n are not written).
-    int rt = nt * 4 + wave;
-    rt = rt < pv.nrt ? rt : pv.nrt - 1;
-    // Addresses: a wavefront-uniform base (scalar registers) plus a fixed
-    // 32-bit per-lane offset, so no per-step vector address arithmetic.
-    const uint8_t* wt = pv.packed + (size_t)rt * nkt * kTileBytes;
-    const uint32_t lane_code = lane * 16;
-    const uint32_t lane_scale = kScaleOffset + 32 * (lane & 31);
-    auto load_w = [&](int it, WStage& s) __attribute__((always_inline)) {
-      const uint8_t* tb = wt + (size_t)(it >> 2) * kTileBytes;
-      const uint8_t* cb = tb + (it & 3) * 2048;
-      const uint8_t* sb = tb + 4 * (it & 3);
-      s.q0 = load16(cb + lane_code);
-      s.q1 = load16(cb + 1024 + lane_code);
-      s.sa = *reinterpret_cast<const uint32_t*>(sb + lane_scale);
-      s.sb = *reinterpret_cast<const uint32_t*>(sb + 16 + lane_scale);
-    };
-
     f32x16 acc[2][JT];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < JT; ++j) acc[i][j] = f32x16{};
-
-    // ---- pipeline.  Four LDS activation buffers: iteration it lives in
-    // buffer (it - ib) % 4, loaded three iterations ahead; weights are loaded
-    // four iterations ahead; each k step's operands are read from LDS and
-    // dequantised during the previous k step's MFMAs.  Loads past the segment
-    // re-read its last iteration, so every step issues the same memory
-    // instructions in the same order -- per step JT activation loads (k step
-    // 0) and four weight loads (k step 2) -- and the main loop has no branches.
-    // Before k step 3 of step it the activations of it + 1 (loaded at k step
-    // 0 of step it - 2) must have landed; after them 4 + JT + 4 + JT + 4
-    // memory instructions have been issued.
-    constexpr int kVmAfterX = 12 + 2 * JT;
-    const int last = ie - 1;
-    auto clampi = [&](int it) __attribute__((always_inline)) { return it < last ? it : last; };
-    WStage w0, w1, w2, w3;
-    load_w(ib, w0);
-    load_w(clampi(ib + 1), w1);
-    load_w(clampi(ib + 2), w2);
-    load_w(clampi(ib + 3), w3);
-    dma_x(ib, NVFP4_XBUF(0));
-    dma_x(clampi(ib + 1), NVFP4_XBUF(1));
-    dma_x(clampi(ib + 2), NVFP4_XBUF(2));
-    wait_vmcnt<0>();
-    zero_tail(ib, NVFP4_XBUF(0));
-    zero_tail(clampi(ib + 1), NVFP4_XBUF(1));
-    zero_tail(clampi(ib + 2), NVFP4_XBUF(2));
-    barrier_only();
-    AOps ac, an;
-    bf16x8 bc[JT], bn[JT];
-    load_b<0, JT>(NVFP4_XBUF(0), lane, bc);
-    dequant_ks<0>(w0, ac);
-    // Step S of a group of four: iteration it = i + S in buffer S.  On entry
-    // ac / bc hold k step 0's operands; on exit, iteration it + 1's.  Before
-    // k step 3 every wavefront waits for its loads of it + 1's activations
-    // (which also covers the weights of it + 1) and for its own LDS reads,
-    // then the workgroup barrier publishes buffer it + 1, so that k step 3
-    // can read it + 1's first B operands while its MFMAs run.
-#define NVFP4_PREFILL_STEP(S, WC, WN)                                   \
-  {                                                                     \
-    const int it = i + (S);                                             \
-    const uint8_t* xcur = NVFP4_XBUF(S);                                \
-    load_b<1, JT>(xcur, lane, bn);                                      \
-    dma_x(clampi(it + 3), NVFP4_XBUF(((S) + 3) & 3));                   \
-    dequant_ks<1>(WC, an);                                              \
-    mfma_ks<JT>(ac, bc, acc);                                           \
-    interleave_ks<JT>();                                                \
-    __builtin_amdgcn_sched_barrier(0);                                  \
-    load_b<2, JT>(xcur, lane, bc);                                      \
-    dequant_ks<2>(WC, ac);                                              \
-    mfma_ks<JT>(an, bn, acc);                                           \
-    interleave_ks<JT>();                                                \
-    __builtin_amdgcn_sched_barrier(0);                                  \
-    load_b<3, JT>(xcur, lane, bn);                                      \
-    dequant_ks<3>(WC, an);                                              \
-    load_w(clampi(it + 4), WC);                                         \
-    mfma_ks<JT>(ac, bc, acc);                                           \
-    interleave_ks<JT>();                                                \
-    __builtin_amdgcn_sched_barrier(0);                                  \
-    wait_vmcnt_lgkm0<kVmAfterX>();                                      \
-    zero_tail(it + 1, NVFP4_XBUF(((S) + 1) & 3));                       \
-    barrier_only();                                                     \
-    __builtin_amdgcn_sched_barrier(0);                                  \
-    load_b<0, JT>(NVFP4_XBUF(((S) + 1) & 3), lane, bc);                 \
-    dequant_ks<0>(WN, ac);                                              \
-    mfma_ks<JT>(an, bn, acc);                                           \
-    interleave_ks<JT>();                                                \
-    __builtin_amdgcn_sched_barrier(0);                                  \
+    if constexpr (MX) {
+      // W4A4: both operands are MX tiles (1 KB of codes per 32 rows x 64 k, in
+      // the scaled FP4 MFMA's operand order, and 64 E8M0 scale bytes), so an
+      // iteration is one MFMA k step and nothing is converted.  Activation
+      // blocks go straight into LDS, loaded three iterations ahead: block q's
+      // codes at 1024 q; its scales, 16-byte pieces p = 4 q .. 4 q + 3, piece p
+      // at 1024 (JT + p / JT) + 16 (p % JT) (wavefront v loads pieces JT v ..
+      // JT v + JT - 1 with lanes 0 .. JT - 1; its other lanes repeat them into
+      // the rest of its 1 KB, so that no lane is masked off).  Each
+      // wavefront's two weight blocks (rows 64 rt .. 64 rt + 63) load four
+      // iterations ahead into registers.  Blocks past the end re-read the last
+      // one (their outputs are not written).
+      static_assert(JT == 4 || JT == 8, "MX tiles: 4 or 8 activation blocks");
+      constexpr int kXq = JT / 4;  // activation code blocks a wavefront loads
+      const int64_t nks = pv.nkt;
+      const int64_t xlast = b.xnrb - 1;
+      const uint8_t* xcode[kXq];
+#pragma unroll
+      for (int j = 0; j < kXq; ++j) {
+        int64_t xb = (int64_t)mt * JT + wave * kXq + j;
+        xb = xb < xlast ? xb : xlast;
+        xcode[j] = pv.xm + xb * nks * 1024 + lane * 16;
+      }
+      // Lanes 0 .. JT-1 of wavefront v load 16-byte piece p = JT v + lane of the JT * 64 scale bytes.
+      const int piece = wave * JT + (lane & (JT - 1));
+      int64_t xbs = (int64_t)mt * JT + piece / 4;
+      xbs = xbs < xlast ? xbs : xlast;
+      const uint8_t* xscale = pv.xsc + xbs * nks * 64 + 16 * (piece & 3);
+      auto dma_mx = [&](int it, uint8_t* xbuf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < kXq; ++j) load_lds16(xcode[j] + (size_t)it * 1024, xbuf + (wave * kXq + j) * 1024);
+        load_lds16(xscale + (size_t)it * 64, xbuf + (JT + wave) * 1024);
+      };
+      int rt = nt * 4 + wave;
+      rt = rt < pv.nrt ? rt : pv.nrt - 1;
+      const uint8_t* wcode[2];
+      const uint8_t* wscale[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        int64_t rb = 2 * (int64_t)rt + h;
+        rb = rb < pv.nrb ? rb : pv.nrb - 1;
+        wcode[h] = pv.packed + rb * nks * 1024 + lane * 16;
+        wscale[h] = pv.wsc + rb * nks * 64 + lane;
+      }
+      // Scale bytes stay 8-bit in the ring: widened where an MFMA takes them
+      // (after that iteration's wait), not where the loop carries them.
+      struct MxA {
+        u32x4 a0, a1;
+        uint8_t s0, s1;
+      };
+      auto load_a = [&](int it, MxA& o) __attribute__((always_inline)) {
+        o.a0 = load16(wcode[0] + (size_t)it * 1024);
+        o.a1 = load16(wcode[1] + (size_t)it * 1024);
+        o.s0 = wscale[0][(size_t)it * 64];
+        o.s1 = wscale[1][(size_t)it * 64];
+      };
+      // Before the barrier that ends iteration it, the activations of it + 1
+      // (loaded during it - 2) must have landed; after them 4 + D + 4 + D + 4
+      // memory instructions have been issued (D = kXq + 1 a load of activations).
+      constexpr int kVmAfter = 12 + 2 * (kXq + 1);
+      const int last = ie - 1;
+      auto clampi = [&](int it) __attribute__((always_inline)) { return it < last ? it : last; };
+      MxA w0, w1, w2, w3;
+      load_a(ib, w0);
+      load_a(clampi(ib + 1), w1);
+      load_a(clampi(ib + 2), w2);
+      load_a(clampi(ib + 3), w3);
+      dma_mx(ib, NVFP4_XBUF(0));
+      dma_mx(clampi(ib + 1), NVFP4_XBUF(1));
+      dma_mx(clampi(ib + 2), NVFP4_XBUF(2));
+      wait_vmcnt<0>();
+      barrier_only();
+#define NVFP4_MX_STEP(S, WC)                                                                                  \
+  {                                                                                                           \
+    const int it = i + (S);                                                                                   \
+    const uint8_t* xcur = NVFP4_XBUF(S);                                                                      \
+    u32x4 bq[JT];                                                                                             \
+    uint32_t bs[JT];                                                                                          \
+    _Pragma("unroll") for (int q = 0; q < JT; ++q) {                                                          \
+      bq[q] = *reinterpret_cast<const u32x4*>(xcur + q * 1024 + lane * 16);                                   \
+      bs[q] = xcur[(JT + 4 * q / JT) * 1024 + (4 * q % JT) * 16 + lane];                                      \
+    }                                                                                                         \
+    dma_mx(clampi(it + 3), NVFP4_XBUF(((S) + 3) & 3));                                                        \
+    const v8i a0 = v8i{(int)WC.a0[0], (int)WC.a0[1], (int)WC.a0[2], (int)WC.a0[3], 0, 0, 0, 0};               \
+    const v8i a1 = v8i{(int)WC.a1[0], (int)WC.a1[1], (int)WC.a1[2], (int)WC.a1[3], 0, 0, 0, 0};               \
+    _Pragma("unroll") for (int q = 0; q < JT; ++q) {                                                          \
+      const v8i bv = v8i{(int)bq[q][0], (int)bq[q][1], (int)bq[q][2], (int)bq[q][3], 0, 0, 0, 0};             \
+      acc[0][q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, bv, acc[0][q], 4, 4, 0, (int)WC.s0, 0,  \
+                                                                  (int)bs[q]);                                \
+      acc[1][q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, bv, acc[1][q], 4, 4, 0, (int)WC.s1, 0,  \
+                                                                  (int)bs[q]);                                \
+    }                                                                                                         \
+    /* the products stay ahead of the barrier: nothing may sink them past it */                             \
+    _Pragma("unroll") for (int q = 0; q < JT; ++q) asm volatile("" ::"a"(acc[0][q]), "a"(acc[1][q]));         \
+    load_a(clampi(it + 4), WC);                                                                               \
+    wait_vmcnt_lgkm0<kVmAfter>();                                                                             \
+    barrier_only();                                                                                           \
+    __builtin_amdgcn_sched_barrier(0);                                                                        \
   }
-    int i = ib;
-    for (; i + 4 <= ie; i += 4) {
-      NVFP4_PREFILL_STEP(0, w0, w1)
-      NVFP4_PREFILL_STEP(1, w1, w2)
-      NVFP4_PREFILL_STEP(2, w2, w3)
-      NVFP4_PREFILL_STEP(3, w3, w0)
+      int i = ib;
+      for (; i + 4 <= ie; i += 4) {
+        NVFP4_MX_STEP(0, w0)
+        NVFP4_MX_STEP(1, w1)
+        NVFP4_MX_STEP(2, w2)
+        NVFP4_MX_STEP(3, w3)
+      }
+      if (i < ie) NVFP4_MX_STEP(0, w0)
+      if (i + 1 < ie) NVFP4_MX_STEP(1, w1)
+      if (i + 2 < ie) NVFP4_MX_STEP(2, w2)
+#undef NVFP4_MX_STEP
+    } else {
+      // Activations go from memory straight into LDS: load j of this wavefront
+      // fills the 1 KB block q = wave * JT + j of a buffer, lane l landing at
+      // byte 16 l -- row 8 q + l / 8, physical chunk l % 8 -- so lane l fetches
+      // the logical chunk that the swizzle puts there.  Rows past m re-read row
+      // m - 1 (their outputs are not written).
+      const uint16_t* xrow[JT];
+      int c8[JT];  // k offset (elements) of this lane's chunk within an iteration
+#pragma unroll
+      for (int j = 0; j < JT; ++j) {
+        const int row = 8 * (wave * JT + j) + (lane >> 3);
+        c8[j] = 8 * ((lane & 7) ^ swz_key(row));
+        int64_t r = m0 + row;
+        r = r < b_m ? r : b_m - 1;
+        xrow[j] = pv.x + r * pv.ldx;
+      }
+      auto dma_x = [&](int it, uint8_t* xbuf) __attribute__((always_inline)) {
+        uint8_t* dst = xbuf + wave * JT * 1024;
+#pragma unroll
+        for (int j = 0; j < JT; ++j) {
+          int64_t kk = (int64_t)it * kBK + c8[j];
+          if (!KFULL) kk = kk < kdim ? kk : kdim - 8;  // in bounds; zeroed once landed
+          load_lds16(xrow[j] + kk, dst + j * 1024);
+        }
+      };
+      // Iteration it's chunks at k >= K must read as zeros (K % 64 != 0 only):
+      // each lane clears the chunks it loaded, after they have landed.
+      auto zero_tail = [&](int it, uint8_t* xbuf) __attribute__((always_inline)) {
+        if (KFULL || it != iters - 1) return;
+#pragma unroll
+        for (int j = 0; j < JT; ++j)
+          if ((int64_t)it * kBK + c8[j] >= kdim)
+            *reinterpret_cast<u32x4*>(xbuf + (wave * JT + j) * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+      };
+
+      // Weight source: this wavefront's packed row tile (clamped; rows past n are not written).
+      int rt = nt * 4 + wave;
+      rt = rt < pv.nrt ? rt : pv.nrt - 1;
+      // Addresses: a wavefront-uniform base (scalar registers) plus a fixed
+      // 32-bit per-lane offset, so no per-step vector address arithmetic.
+      const uint8_t* wt = pv.packed + (size_t)rt * nkt * kTileBytes;
+      const uint32_t lane_code = lane * 16;
+      const uint32_t lane_scale = kScaleOffset + 32 * (lane & 31);
+      auto load_w = [&](int it, WStage& s) __attribute__((always_inline)) {
+        const uint8_t* tb = wt + (size_t)(it >> 2) * kTileBytes;
+        const uint8_t* cb = tb + (it & 3) * 2048;
+        const uint8_t* sb = tb + 4 * (it & 3);
+        s.q0 = load16(cb + lane_code);
+        s.q1 = load16(cb + 1024 + lane_code);
+        s.sa = *reinterpret_cast<const uint32_t*>(sb + lane_scale);
+        s.sb = *reinterpret_cast<const uint32_t*>(sb + 16 + lane_scale);
+      };
+
+
+      // ---- pipeline.  Four LDS activation buffers: iteration it lives in
+      // buffer (it - ib) % 4, loaded three iterations ahead; weights are loaded
+      // four iterations ahead; each k step's operands are read from LDS and
+      // dequantised during the previous k step's MFMAs.  Loads past the segment
+      // re-read its last iteration, so every step issues the same memory
+      // instructions in the same order -- per step JT activation loads (k step
+      // 0) and four weight loads (k step 2) -- and the main loop has no branches.
+      // Before k step 3 of step it the activations of it + 1 (loaded at k step
+      // 0 of step it - 2) must have landed; after them 4 + JT + 4 + JT + 4
+      // memory instructions have been issued.
+      constexpr int kVmAfterX = 12 + 2 * JT;
+      const int last = ie - 1;
+      auto clampi = [&](int it) __attribute__((always_inline)) { return it < last ? it : last; };
+      WStage w0, w1, w2, w3;
+      load_w(ib, w0);
+      load_w(clampi(ib + 1), w1);
+      load_w(clampi(ib + 2), w2);
+      load_w(clampi(ib + 3), w3);
+      dma_x(ib, NVFP4_XBUF(0));
+      dma_x(clampi(ib + 1), NVFP4_XBUF(1));
+      dma_x(clampi(ib + 2), NVFP4_XBUF(2));
+      wait_vmcnt<0>();
+      zero_tail(ib, NVFP4_XBUF(0));
+      zero_tail(clampi(ib + 1), NVFP4_XBUF(1));
+      zero_tail(clampi(ib + 2), NVFP4_XBUF(2));
+      barrier_only();
+      AOps ac, an;
+      bf16x8 bc[JT], bn[JT];
+      load_b<0, JT>(NVFP4_XBUF(0), lane, bc);
+      dequant_ks<0>(w0, ac);
+      // Step S of a group of four: iteration it = i + S in buffer S.  On entry
+      // ac / bc hold k step 0's operands; on exit, iteration it + 1's.  Before
+      // k step 3 every wavefront waits for its loads of it + 1's activations
+      // (which also covers the weights of it + 1) and for its own LDS reads,
+      // then the workgroup barrier publishes buffer it + 1, so that k step 3
+      // can read it + 1's first B operands while its MFMAs run.
+#define NVFP4_PREFILL_STEP(S, WC, WN)                                   \
+    {                                                                     \
+      const int it = i + (S);                                             \
+      const uint8_t* xcur = NVFP4_XBUF(S);                                \
+      load_b<1, JT>(xcur, lane, bn);                                      \
+      dma_x(clampi(it + 3), NVFP4_XBUF(((S) + 3) & 3));                   \
+      dequant_ks<1>(WC, an);                                              \
+      mfma_ks<JT>(ac, bc, acc);                                           \
+      interleave_ks<JT>();                                                \
+      __builtin_amdgcn_sched_barrier(0);                                  \
+      load_b<2, JT>(xcur, lane, bc);                                      \
+      dequant_ks<2>(WC, ac);                                              \
+      mfma_ks<JT>(an, bn, acc);                                           \
+      interleave_ks<JT>();                                                \
+      __builtin_amdgcn_sched_barrier(0);                                  \
+      load_b<3, JT>(xcur, lane, bn);                                      \
+      dequant_ks<3>(WC, an);                                              \
+      load_w(clampi(it + 4), WC);                                         \
+      mfma_ks<JT>(ac, bc, acc);                                           \
+      interleave_ks<JT>();                                                \
+      __builtin_amdgcn_sched_barrier(0);                                  \
+      wait_vmcnt_lgkm0<kVmAfterX>();                                      \
+      zero_tail(it + 1, NVFP4_XBUF(((S) + 1) & 3));                       \
+      barrier_only();                                                     \
+      __builtin_amdgcn_sched_barrier(0);                                  \
+      load_b<0, JT>(NVFP4_XBUF(((S) + 1) & 3), lane, bc);                 \
+      dequant_ks<0>(WN, ac);                                              \
+      mfma_ks<JT>(an, bn, acc);                                           \
+      interleave_ks<JT>();                                                \
+      __builtin_amdgcn_sched_barrier(0);                                  \
     }
-    if (i < ie) NVFP4_PREFILL_STEP(0, w0, w1)
-    if (i + 1 < ie) NVFP4_PREFILL_STEP(1, w1, w2)
-    if (i + 2 < ie) NVFP4_PREFILL_STEP(2, w2, w3)
+      int i = ib;
+      for (; i + 4 <= ie; i += 4) {
+        NVFP4_PREFILL_STEP(0, w0, w1)
+        NVFP4_PREFILL_STEP(1, w1, w2)
+        NVFP4_PREFILL_STEP(2, w2, w3)
+        NVFP4_PREFILL_STEP(3, w3, w0)
+      }
+      if (i < ie) NVFP4_PREFILL_STEP(0, w0, w1)
+      if (i + 1 < ie) NVFP4_PREFILL_STEP(1, w1, w2)
+      if (i + 2 < ie) NVFP4_PREFILL_STEP(2, w2, w3)
 #undef NVFP4_PREFILL_STEP
+    }
 
     // ---- output ------------------------------------------------------------
     // Accumulator element e of tile (i, jt) of this lane: weight row
@@ -582,9 +703,9 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillBatch b, u
 #undef NVFP4_XBUF
 }
 
-template <int JT, bool KFULL>
+template <int JT, bool KFULL, bool MX = false>
 void launch_one(const PrefillBatch& b, unsigned wgs, unsigned* counters, float* partials, hipStream_t s) {
-  prefill_kernel<JT, KFULL><<<dim3(wgs), dim3(256), 0, s>>>(b, counters, partials);
+  prefill_kernel<JT, KFULL, MX><<<dim3(wgs), dim3(256), 0, s>>>(b, counters, partials);
 }
 
 struct Plan {
@@ -700,6 +821,77 @@ hipError_t launch_prefill_batch(const Problem* p, int count, int64_t m, bool y_b
         else launch_one<2, false>(b, nwg, counters, partials, s);
       }
       hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+size_t w4a4_streamk_bytes() { return kCounterBytes + (size_t)2 * kPreWgs * part_bytes(8); }
+
+hipError_t launch_w4a4_batch(const MxProblem* p, int count, int64_t m, bool y_bf16, void* ws, hipStream_t s) {
+  if (m <= 0) return hipSuccess;
+  const size_t esize = y_bf16 ? 2 : 4;
+  const int jt = m > 128 ? 8 : 4;
+  const int64_t bm = 32 * jt, xnrb_all = (m + 31) / 32;
+  unsigned* counters = static_cast<unsigned*>(ws);
+  float* partials = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kCounterBytes);
+  for (int c0 = 0; c0 < count; c0 += kMaxPre) {
+    const int cn = count - c0 < kMaxPre ? count - c0 : kMaxPre;
+    MxProblem q[kMaxPre];
+    int nq = 0;
+    for (int i = c0; i < c0 + cn; ++i)
+      if (p[i].n > 0 && p[i].k > 0) q[nq++] = p[i];
+    if (nq == 0) continue;
+    // One counter and one XCD mask per output tile of a launch: cut m so that
+    // a launch's tiles fit (a launch holds at most kCounterSlots row tiles of
+    // 64, so at most kCounterSlots / 4 weight-row tiles and max_mt >= 2).
+    int64_t ntiles = 0;
+    for (int j = 0; j < nq; ++j) ntiles += ((q[j].n + 63) / 64 + 3) / 4;
+    int64_t max_mt = (kCounterSlots / 2) / ntiles;
+    if (max_mt < 1) max_mt = 1;
+    const int64_t mt_all = (m + bm - 1) / bm;
+    const int64_t mrows = (mt_all <= max_mt ? mt_all : max_mt) * bm;
+    for (int64_t r0 = 0; r0 < m; r0 += mrows) {
+      const int64_t mr = m - r0 < mrows ? m - r0 : mrows;
+      PrefillBatch b{};
+      b.count = nq;
+      b.mtiles = (int)((mr + bm - 1) / bm);
+      b.y_bf16 = y_bf16 ? 1 : 0;
+      b.m = mr;
+      b.xnrb = (mr + 31) / 32;
+      int64_t it = 0;
+      int tiles = 0;
+      for (int j = 0; j < nq; ++j) {
+        const int64_t nrb = (q[j].n + 31) / 32, nks = (q[j].k + 63) / 64;
+        const int nrt = (int)((nrb + 1) / 2), ntn = (nrt + 3) / 4;
+        b.iter_begin[j] = it;
+        b.tile_base[j] = tiles;
+        b.iters[j] = (int)nks;
+        b.nkt[j] = (int)nks;
+        b.nrt[j] = nrt;
+        b.ntn[j] = ntn;
+        b.packed[j] = q[j].w;
+        b.wsc[j] = q[j].w + (size_t)nrb * nks * 1024;
+        b.xm[j] = q[j].x + (size_t)(r0 / 32) * nks * 1024;
+        b.xsc[j] = q[j].x + (size_t)xnrb_all * nks * 1024 + (size_t)(r0 / 32) * nks * 64;
+        b.nrb[j] = nrb;
+        b.y[j] = static_cast<uint8_t*>(q[j].y) + (size_t)r0 * q[j].ldy * esize;
+        b.n[j] = q[j].n;
+        b.k[j] = q[j].k;
+        b.ldy[j] = q[j].ldy;
+        b.st[j] = q[j].st;
+        tiles += ntn * b.mtiles;
+        it += (int64_t)ntn * b.mtiles * nks;
+      }
+      b.iter_begin[nq] = it;
+      b.total = it;
+      int64_t wgs = it / kMinShare;
+      wgs = wgs < 1 ? 1 : (wgs > kPreWgs ? kPreWgs : wgs);
+      b.wgs = (int)wgs;
+      if (jt == 8) launch_one<8, true, true>(b, (unsigned)wgs, counters, partials, s);
+      else launch_one<4, true, true>(b, (unsigned)wgs, counters, partials, s);
+      const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
   }

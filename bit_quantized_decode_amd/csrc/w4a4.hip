@@ -16,13 +16,14 @@
 // (j = 0..31, low nibble first) -- exactly the instruction's A / B operand for
 // one lane -- and 64 scale bytes, after all codes, at (rb * nks + ks) * 64 + l.
 // Rows past the matrix and k past K are zero.
+#include <vector>
+
 #include "device_common.h"
 #include "launchers.h"
 
 namespace nvfp4 {
 namespace {
 
-typedef int v8i __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ uint32_t e2m1_code(float a) {
   return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
@@ -152,123 +153,6 @@ __global__ __launch_bounds__(256) void mx_unpack_kernel(const uint8_t* __restric
   }
 }
 
-// The product: a workgroup of four wavefronts computes 256 weight rows x 128
-// activation rows.  Wavefront w owns weight blocks 2w and 2w + 1 (two A
-// operands per 64-k step, loaded one step ahead into registers); the four
-// activation blocks of a step (four B operands) are staged once per workgroup
-// in LDS, double-buffered, one 16-byte load per thread; each wavefront then
-// runs 2 x 4 MFMAs per step.
-constexpr int kWJT = 4;        // activation blocks of 32 rows per workgroup
-constexpr int kBStage = kWJT * 1024 + kWJT * 64;  // LDS bytes of one step's B operands
-
-__device__ __forceinline__ v8i widen(u32x4 q) {
-  return v8i{(int)q[0], (int)q[1], (int)q[2], (int)q[3], 0, 0, 0, 0};
-}
-
-__global__ __launch_bounds__(256, 2) void w4a4_gemm_kernel(const uint8_t* __restrict__ w, MxGeom gw,
-                                                           const uint8_t* __restrict__ xm, MxGeom gx, float st,
-                                                           void* __restrict__ y, int64_t ldy, int y_bf16) {
-  __shared__ __attribute__((aligned(16))) uint8_t sb0[kBStage];
-  __shared__ __attribute__((aligned(16))) uint8_t sb1[kBStage];
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int64_t nks = gw.nks;
-  // This wavefront's two weight blocks (past the end: the last block, not stored).
-  int64_t wrb[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int64_t r = (int64_t)blockIdx.x * 8 + 2 * wave + i;
-    wrb[i] = r < gw.nrb ? r : gw.nrb - 1;
-  }
-  const uint8_t* wsc = w + gw.scale_offset;
-  // The B block this thread stages: codes of block tid / 64 (16 bytes at lane), and
-  // for threads 0..15 a 16-byte run of the blocks' scales.
-  const int sblk = tid >> 6;
-  int64_t xrb = (int64_t)blockIdx.y * kWJT + sblk;
-  xrb = xrb < gx.nrb ? xrb : gx.nrb - 1;
-  const int64_t scb = (int64_t)blockIdx.y * kWJT + (tid >> 2);  // threads 0..15: block tid / 4, 16 scale bytes
-  const int64_t scb_c = scb < gx.nrb ? scb : gx.nrb - 1;
-  const uint8_t* xsc = xm + gx.scale_offset;
-  auto load_b = [&](int64_t ks, u32x4& codes, u32x4& scales) __attribute__((always_inline)) {
-    codes = *reinterpret_cast<const u32x4*>(xm + (xrb * nks + ks) * 1024 + lane * 16);
-    if (tid < 16) scales = *reinterpret_cast<const u32x4*>(xsc + (scb_c * nks + ks) * 64 + (tid & 3) * 16);
-  };
-  auto store_b = [&](uint8_t* buf, u32x4 codes, u32x4 scales) __attribute__((always_inline)) {
-    *reinterpret_cast<u32x4*>(buf + sblk * 1024 + lane * 16) = codes;
-    if (tid < 16) *reinterpret_cast<u32x4*>(buf + kWJT * 1024 + (tid >> 2) * 64 + (tid & 3) * 16) = scales;
-  };
-  auto load_a = [&](int64_t ks, u32x4 (&a)[2], uint32_t (&sa)[2]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      a[i] = *reinterpret_cast<const u32x4*>(w + (wrb[i] * nks + ks) * 1024 + lane * 16);
-      sa[i] = wsc[(wrb[i] * nks + ks) * 64 + lane];
-    }
-  };
-  f32x16 acc[2][kWJT];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < kWJT; ++j) acc[i][j] = f32x16{};
-  u32x4 a[2], an[2], bc, bs = u32x4{0u, 0u, 0u, 0u};
-  uint32_t sa[2], san[2];
-  load_a(0, a, sa);
-  load_b(0, bc, bs);
-  store_b(sb0, bc, bs);
-  __syncthreads();
-  for (int64_t ks = 0; ks < nks; ++ks) {
-    const int64_t kn = ks + 1 < nks ? ks + 1 : ks;
-    load_a(kn, an, san);
-    load_b(kn, bc, bs);
-    const uint8_t* cur = (ks & 1) ? sb1 : sb0;
-    u32x4 b[kWJT];
-    uint32_t sbv[kWJT];
-#pragma unroll
-    for (int j = 0; j < kWJT; ++j) {
-      b[j] = *reinterpret_cast<const u32x4*>(cur + j * 1024 + lane * 16);
-      sbv[j] = cur[kWJT * 1024 + j * 64 + lane];
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const v8i av = widen(a[i]);
-#pragma unroll
-      for (int j = 0; j < kWJT; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, widen(b[j]), acc[i][j], 4, 4, 0, (int)sa[i], 0,
-                                                                    (int)sbv[j]);
-    }
-    store_b((ks & 1) ? sb0 : sb1, bc, bs);  // the other buffer: read by no wavefront this step
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      a[i] = an[i];
-      sa[i] = san[i];
-    }
-  }
-  // acc[i][j] element e: weight row 32 wrb_i + 8 (e / 4) + 4 (lane / 32) + e % 4,
-  // activation row 32 (4 blockIdx.y + j) + lane % 32.
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int64_t rb = (int64_t)blockIdx.x * 8 + 2 * wave + i;
-    if (rb >= gw.nrb) continue;
-#pragma unroll
-    for (int j = 0; j < kWJT; ++j) {
-      const int64_t arow = 32 * ((int64_t)blockIdx.y * kWJT + j) + (lane & 31);
-      if (arow >= gx.rows) continue;
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int64_t col = 32 * rb + 8 * e4 + 4 * (lane >> 5);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          if (col + c >= gw.rows) continue;
-          const float v = acc[i][j][4 * e4 + c] * st;
-          if (y_bf16) static_cast<uint16_t*>(y)[arow * ldy + col + c] = to_bf16(v);
-          else static_cast<float*>(y)[arow * ldy + col + c] = v;
-        }
-      }
-    }
-  }
-}
-
 unsigned grid_of(int64_t items) {
   const int64_t wgs = (items + 255) / 256;
   return (unsigned)(wgs < 16384 ? (wgs > 0 ? wgs : 1) : 16384);
@@ -302,15 +186,40 @@ hipError_t launch_mx_quant_act(const uint16_t* x, int64_t m, int64_t k, int64_t 
   return hipGetLastError();
 }
 
+size_t w4a4_batch_workspace_bytes(const Problem* p, int count, int64_t m) {
+  size_t need = w4a4_streamk_bytes();
+  for (int i = 0; i < count; ++i)
+    if (p[i].n > 0 && p[i].k > 0) need += mx_packed_bytes(m, p[i].k);
+  return need;
+}
+
+size_t w4a4_workspace_bytes(int64_t m, int64_t k) { return w4a4_streamk_bytes() + mx_packed_bytes(m, k); }
+
+hipError_t launch_w4a4_gemm_batch(const Problem* p, int count, int64_t m, bool y_bf16, void* ws, hipStream_t s) {
+  if (m <= 0 || count <= 0) return hipSuccess;
+  std::vector<MxProblem> q;
+  q.reserve((size_t)count);
+  // Workspace: the stream-K counters and partial sums, then each problem's x as MX tiles.
+  uint8_t* xmx = static_cast<uint8_t*>(ws) + w4a4_streamk_bytes();
+  for (int i = 0; i < count; ++i) {
+    if (p[i].n <= 0) continue;
+    if (p[i].k <= 0) {
+      const hipError_t e = launch_zero_rows(p[i].y, m, p[i].n, p[i].ldy, y_bf16, s);
+      if (e != hipSuccess) return e;
+      continue;
+    }
+    const hipError_t e = launch_mx_quant_act(p[i].x, m, p[i].k, p[i].ldx, xmx, s);
+    if (e != hipSuccess) return e;
+    q.push_back(MxProblem{static_cast<const uint8_t*>(p[i].packed), p[i].n, p[i].k, p[i].st, xmx, p[i].y, p[i].ldy});
+    xmx += mx_packed_bytes(m, p[i].k);
+  }
+  return launch_w4a4_batch(q.data(), (int)q.size(), m, y_bf16, ws, s);
+}
+
 hipError_t launch_w4a4_gemm(const void* mx_w, int64_t n, int64_t k, float st, const uint16_t* x, int64_t m,
                             int64_t ldx, void* y, int64_t ldy, bool y_bf16, void* ws, hipStream_t s) {
-  const hipError_t e = launch_mx_quant_act(x, m, k, ldx, ws, s);
-  if (e != hipSuccess) return e;
-  const MxGeom gw = mx_geom(n, k), gx = mx_geom(m, k);
-  const dim3 grid((unsigned)((gw.nrb + 7) / 8), (unsigned)((gx.nrb + kWJT - 1) / kWJT));
-  hipLaunchKernelGGL(w4a4_gemm_kernel, grid, dim3(256), 0, s, static_cast<const uint8_t*>(mx_w), gw,
-                     static_cast<const uint8_t*>(ws), gx, st, y, ldy, y_bf16 ? 1 : 0);
-  return hipGetLastError();
+  const Problem p{mx_w, n, k, st, x, ldx, y, ldy};
+  return launch_w4a4_gemm_batch(&p, 1, m, y_bf16, ws, s);
 }
 
 }  // namespace nvfp4

@@ -177,12 +177,17 @@ int nvfp4_gemm(const void* packed, int64_t n, int64_t k, float tensor_scale,
  *   weights: the NVFP4 values e2m1 * e4m3 (s_t left out) in blocks along k;
  *   activations: the bf16 values in blocks along k;
  *   y[i][j] = s_t * sum_k w'[j][k] x'[i][k]  (fp32 accumulation).
- * k % 32 == 0.  nvfp4_mx_pack() converts a canonical NVFP4 matrix (once, like
- * nvfp4_pack) into "MX tiles" of nvfp4_mx_packed_bytes() bytes;
- * nvfp4_w4a4_gemm() quantises x into the workspace (at least
- * nvfp4_w4a4_workspace_bytes(m, k), 16-byte aligned; it holds x's MX tiles
- * after the call) and runs the product.  m <= 2^24.  nvfp4_mx_unpack() (a test
- * hook) turns MX tiles back into codes [rows][k/2] and E8M0 scales [rows][k/32].
+ * k % 32 == 0, n within the product calls' row limit.  nvfp4_mx_pack()
+ * converts a canonical NVFP4 matrix (once, like nvfp4_pack) into "MX tiles" of
+ * nvfp4_mx_packed_bytes() bytes; nvfp4_w4a4_gemm() quantises x into the
+ * workspace and runs the product on the prefill's stream-K schedule.  The
+ * workspace (at least nvfp4_w4a4_workspace_bytes(m, k), 16-byte aligned) holds
+ * the schedule's counters and partial sums first -- like the gemm workspace,
+ * all zero before the first use and left so by every call -- and then x's MX
+ * tiles, at byte offset nvfp4_w4a4_workspace_bytes(m, k) -
+ * nvfp4_mx_packed_bytes(m, k) (the same for every m and k), which stay there
+ * after the call.  m <= 2^24.  nvfp4_mx_unpack() (a test hook) turns MX tiles
+ * back into codes [rows][k/2] and E8M0 scales [rows][k/32].
  */
 int nvfp4_mx_packed_bytes(int64_t rows, int64_t k, size_t* bytes /* host */);
 int nvfp4_mx_pack(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k, void* mx_packed, void* stream);
@@ -222,6 +227,16 @@ int nvfp4_gemv_batched(const nvfp4_problem* problems /* host */, int count, void
 int nvfp4_gemm_batched_workspace_bytes(const nvfp4_problem* problems /* host */, int count, int64_t m,
                                        size_t* bytes /* host */);
 int nvfp4_gemm_batched(const nvfp4_problem* problems /* host */, int count, int64_t m, int y_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+/* W4A4 batch (the f4 rule above for each problem; `packed` holds the MX
+ * tiles of nvfp4_mx_pack): one stream-K launch per eight problems, so that
+ * the split tiles' fix-up is shared like the gemm batch's.  The workspace holds
+ * the schedule's counters and partial sums (zero before the first use, left
+ * so) and then each problem's x as MX tiles, in problem order.  k % 32 == 0,
+ * m <= 2^24. */
+int nvfp4_w4a4_batched_workspace_bytes(const nvfp4_problem* problems /* host */, int count, int64_t m,
+                                       size_t* bytes /* host */);
+int nvfp4_w4a4_batched(const nvfp4_problem* problems /* host */, int count, int64_t m, int y_dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- a4-a8: top-k routed mixture-of-experts layer ----------------------------

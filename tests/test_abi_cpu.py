@@ -28,7 +28,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 25, names
+    assert len(names) == 27, names
     assert set(names) == set(B.EXPORTED)
     for name in names:
         assert hasattr(L, name), name
@@ -197,6 +197,36 @@ def test_batched_validation(L):
     big[0].ldx, big[0].ldy = 17408, 5120
     assert L.nvfp4_gemm_batched_workspace_bytes(big, 1, 32, ctypes.byref(sz)) == B.NVFP4_OK and sz.value > 0
     assert L.nvfp4_gemm_batched(big, 1, 32, 1, None, 0, None) == B.NVFP4_ERR_WORKSPACE
+
+
+def test_w4a4_validation(L):
+    A = 0x10000
+    sz, one = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.nvfp4_w4a4_workspace_bytes(512, 5120, ctypes.byref(one)) == B.NVFP4_OK
+    assert L.nvfp4_mx_packed_bytes(512, 5120, ctypes.byref(sz)) == B.NVFP4_OK
+    stream_k = one.value - sz.value                   # counters and partial sums ahead of x's MX tiles
+    assert stream_k > 0
+    assert L.nvfp4_w4a4_workspace_bytes(64, 96, ctypes.byref(one)) == B.NVFP4_OK
+    assert L.nvfp4_mx_packed_bytes(64, 96, ctypes.byref(sz)) == B.NVFP4_OK
+    assert one.value - sz.value == stream_k           # the same offset for every shape
+    assert L.nvfp4_w4a4_workspace_bytes(64, 48, ctypes.byref(one)) == B.NVFP4_ERR_SHAPE   # k % 32
+    arr = (B.Problem * 2)()
+    for i in range(2):
+        arr[i].packed, arr[i].n, arr[i].k, arr[i].tensor_scale = A, 64, 256, 1.0
+        arr[i].x, arr[i].ldx, arr[i].y, arr[i].ldy = A, 256, A + 0x1000 * (i + 1), 64
+    assert L.nvfp4_w4a4_batched_workspace_bytes(arr, 2, 300, ctypes.byref(sz)) == B.NVFP4_OK
+    assert L.nvfp4_mx_packed_bytes(300, 256, ctypes.byref(one)) == B.NVFP4_OK
+    assert sz.value == stream_k + 2 * one.value       # each problem's x tiles after the stream-K area
+    arr[1].k = 48
+    assert L.nvfp4_w4a4_batched_workspace_bytes(arr, 2, 300, ctypes.byref(sz)) == B.NVFP4_ERR_SHAPE
+    arr[1].k = 256
+    assert L.nvfp4_w4a4_batched(arr, 2, -1, 1, None, 0, None) == B.NVFP4_ERR_SHAPE
+    assert L.nvfp4_w4a4_batched(arr, 2, 1 << 25, 1, None, 0, None) == B.NVFP4_ERR_SHAPE
+    assert L.nvfp4_w4a4_batched(arr, 2, 300, 9, None, 0, None) == B.NVFP4_ERR_DTYPE
+    assert L.nvfp4_w4a4_batched(arr, 2, 300, 1, None, 0, None) == B.NVFP4_ERR_WORKSPACE
+    assert L.nvfp4_w4a4_batched(arr, 2, 0, 1, None, 0, None) == B.NVFP4_OK      # m = 0
+    arr[1].y = arr[0].y
+    assert L.nvfp4_w4a4_batched(arr, 2, 300, 1, None, 0, None) == B.NVFP4_ERR_ARG   # shared output
 
 
 def test_expert_cache_validation(L):

@@ -49,9 +49,9 @@ def test_w4a4_matches_oracle(m, n, k, y_dtype):
     codes, scales = random_matrix(rng, n, k)
     xb = wide_x(rng, m, k)
     mx = B.mx_pack(to_dev_u8(codes, dev), to_dev_u8(scales, dev))
-    ws = torch.zeros(B.mx_packed_bytes(m, k), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(B.w4a4_workspace_bytes(m, k), dtype=torch.uint8, device=dev)
     y = B.w4a4_gemm(mx, n, k, I.TENSOR_SCALE, to_dev_bf16(xb, dev), y_dtype=y_dtype, ws=ws)
-    xc, xs = B.mx_unpack(ws, m, k)                   # the activations as the kernel quantised them
+    xc, xs = B.mx_unpack(B.w4a4_x_tiles(ws, m, k), m, k)  # the activations as the kernel quantised them
     torch.cuda.synchronize()
     rxc, rxs = oracle.mx_from_bf16(xb)
     assert np.array_equal(xs.cpu().numpy(), rxs) and np.array_equal(xc.cpu().numpy(), rxc)
@@ -60,6 +60,55 @@ def test_w4a4_matches_oracle(m, n, k, y_dtype):
     got = y.cpu().numpy().astype(np.float64) if y_dtype == torch.float32 else bf16_to_f64(y)
     extra = 0.0 if y_dtype == torch.float32 else ulp_bf16(y_ref)
     assert_within(got, y_ref, s, extra=extra, what=f"w4a4 {m}x{n}x{k}")
+
+
+def test_w4a4_workspace_reuse():
+    """One workspace through calls of different shapes, each with tiles cut
+    between workgroups: every call leaves the counters as it found them."""
+    dev = device()
+    shapes = [(300, 257, 1056), (40, 700, 4096), (513, 64, 8192), (300, 257, 1056)]
+    ws = torch.zeros(max(B.w4a4_workspace_bytes(m, k) for m, _, k in shapes), dtype=torch.uint8, device=dev)
+    for m, n, k in shapes:
+        rng = np.random.default_rng(m + n + k)
+        codes, scales = random_matrix(rng, n, k)
+        xb = wide_x(rng, m, k)
+        mx = B.mx_pack(to_dev_u8(codes, dev), to_dev_u8(scales, dev))
+        y = B.w4a4_gemm(mx, n, k, I.TENSOR_SCALE, to_dev_bf16(xb, dev), y_dtype=torch.float32, ws=ws)
+        torch.cuda.synchronize()
+        rxc, rxs = oracle.mx_from_bf16(xb)
+        wc, wsc = oracle.mx_from_nvfp4(codes, scales)
+        y_ref, s = oracle.mx_gemm(wc, wsc, I.TENSOR_SCALE, rxc, rxs, nthreads=oracle_threads())
+        assert_within(y.cpu().numpy().astype(np.float64), y_ref, s, what=f"w4a4 {m}x{n}x{k} (shared workspace)")
+
+
+@pytest.mark.parametrize("m", [1, 100, 300])
+def test_w4a4_batched_matches_oracle(m):
+    """Several products in one launch (an empty one and a k = 0 one among them)."""
+    dev = device()
+    shapes = [(257, 1056), (0, 64), (64, 2048), (130, 320), (70, 0)]
+    items, refs = [], []
+    for i, (n, k) in enumerate(shapes):
+        rng = np.random.default_rng(1000 * m + i)
+        codes, scales = random_matrix(rng, n, k)
+        xb = wide_x(rng, m, k)
+        mx = B.mx_pack(to_dev_u8(codes, dev), to_dev_u8(scales, dev)) if n * k else torch.zeros(16, dtype=torch.uint8, device=dev)
+        y = torch.full((m, n), float("nan"), dtype=torch.float32, device=dev)
+        items.append((mx, n, k, I.TENSOR_SCALE, to_dev_bf16(xb, dev), y))
+        refs.append((codes, scales, xb))
+    ws = torch.zeros(B.w4a4_batched_workspace_bytes(items, m), dtype=torch.uint8, device=dev)
+    B.w4a4_batched(items, ws=ws)
+    torch.cuda.synchronize()
+    for (mx, n, k, st, xd, y), (codes, scales, xb) in zip(items, refs):
+        if n == 0:
+            continue
+        got = y.cpu().numpy().astype(np.float64)
+        if k == 0:
+            assert np.all(got == 0.0)
+            continue
+        rxc, rxs = oracle.mx_from_bf16(xb)
+        wc, wsc = oracle.mx_from_nvfp4(codes, scales)
+        y_ref, s = oracle.mx_gemm(wc, wsc, st, rxc, rxs, nthreads=oracle_threads())
+        assert_within(got, y_ref, s, what=f"w4a4 batch {m}x{n}x{k}")
 
 
 @pytest.mark.parametrize("mat", I.PREFILL_MATRICES, ids=lambda m: m.name)
