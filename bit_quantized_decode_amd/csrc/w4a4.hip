@@ -74,6 +74,17 @@ __device__ __forceinline__ void mx_put(uint8_t* dst, const MxGeom& g, int64_t ro
   dst[g.scale_offset + blk * 64 + lane] = (uint8_t)scale;
 }
 
+// Thread t works on the element of MX tile (rb, ks) = t / 64 that lane t % 64
+// of the matrix instruction holds: row 32 rb + t % 32, 32-k block 2 ks + t % 64
+// / 32.  A wavefront thus writes one tile's kilobyte of codes and 64 scale
+// bytes, each contiguously.
+__device__ __forceinline__ void mx_element(int64_t t, int64_t nks, int64_t& row, int64_t& kb) {
+  const int64_t tile = t >> 6;
+  const int l = (int)(t & 63);
+  row = 32 * (tile / nks) + (l & 31);
+  kb = 2 * (tile % nks) + (l >> 5);
+}
+
 // Weights: canonical NVFP4 (codes [n][k/2], E4M3 scales [n][k/16]) -> MX tiles;
 // one thread per (row, 32-k block) of the padded extent.
 __global__ __launch_bounds__(256) void mx_pack_kernel(const uint8_t* __restrict__ codes,
@@ -81,7 +92,8 @@ __global__ __launch_bounds__(256) void mx_pack_kernel(const uint8_t* __restrict_
                                                       uint8_t* __restrict__ dst) {
   const int64_t kbs = 2 * g.nks, total = g.nrb * 32 * kbs;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t row = t / kbs, kb = t % kbs;
+    int64_t row, kb;
+    mx_element(t, g.nks, row, kb);
     float v[32];
     if (row < g.rows && 32 * kb < g.k) {
       const u32x4 q = *reinterpret_cast<const u32x4*>(codes + row * (g.k / 2) + 16 * kb);
@@ -116,7 +128,8 @@ __global__ __launch_bounds__(256) void mx_quant_act_kernel(const uint16_t* __res
                                                            uint8_t* __restrict__ dst) {
   const int64_t kbs = 2 * g.nks, total = g.nrb * 32 * kbs;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t row = t / kbs, kb = t % kbs;
+    int64_t row, kb;
+    mx_element(t, g.nks, row, kb);
     float v[32];
     if (row < g.rows && 32 * kb < g.k) {
       const u32x4* p = reinterpret_cast<const u32x4*>(x + row * ldx + 32 * kb);
