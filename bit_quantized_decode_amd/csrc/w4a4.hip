@@ -123,33 +123,46 @@ __global__ __launch_bounds__(256) void mx_pack_kernel(const uint8_t* __restrict_
   }
 }
 
-// Activations: bf16 [m][ldx] -> MX tiles.
+// Activations: bf16 [m][ldx] -> MX tiles; four threads per (row, 32-k
+// block), each converting 8 k (one dword of the 16 code bytes), with the
+// block's largest magnitude combined across the four.
 __global__ __launch_bounds__(256) void mx_quant_act_kernel(const uint16_t* __restrict__ x, int64_t ldx, MxGeom g,
                                                            uint8_t* __restrict__ dst) {
-  const int64_t kbs = 2 * g.nks, total = g.nrb * 32 * kbs;
+  const int64_t total = g.nrb * 32 * (2 * g.nks) * 4;  // a multiple of 4: quads are never split
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
+    const int j = (int)(t & 3);
     int64_t row, kb;
-    mx_element(t, g.nks, row, kb);
-    float v[32];
+    mx_element(t >> 2, g.nks, row, kb);
+    float v[8];
     if (row < g.rows && 32 * kb < g.k) {
-      const u32x4* p = reinterpret_cast<const u32x4*>(x + row * ldx + 32 * kb);
+      const u32x4 w = *reinterpret_cast<const u32x4*>(x + row * ldx + 32 * kb + 8 * j);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x4 w = p[j];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[8 * j + 2 * i] = __uint_as_float(w[i] << 16);
-          v[8 * j + 2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-        }
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] = 0.0f;
+      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
     }
-    u32x4 out;
-    uint32_t sc;
-    mx_block(v, out, sc);
-    mx_put(dst, g, row, kb, out, sc);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 4));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 4));
+    uint32_t code = 0u, scale = 0u;
+    if (amax != 0.0f) {
+      int ex = ilogbf(amax) - 2;
+      ex = ex < -127 ? -127 : (ex > 127 ? 127 : ex);
+      scale = (uint32_t)(ex + 127);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        code |= (e2m1_code(ldexpf(fabsf(v[i]), -ex)) | ((__float_as_uint(v[i]) >> 31) << 3)) << (4 * i);
+    }
+    const int64_t blk = (row / 32) * g.nks + kb / 2;
+    const int lane = (int)(row % 32) + 32 * (int)(kb % 2);
+    reinterpret_cast<uint32_t*>(dst + blk * 1024 + lane * 16)[j] = code;
+    if (j == 0) dst[g.scale_offset + blk * 64 + lane] = (uint8_t)scale;
   }
 }
 
@@ -194,7 +207,7 @@ hipError_t launch_mx_unpack(const void* src, int64_t rows, int64_t k, uint8_t* c
 
 hipError_t launch_mx_quant_act(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, void* dst, hipStream_t s) {
   const MxGeom g = mx_geom(m, k);
-  hipLaunchKernelGGL(mx_quant_act_kernel, dim3(grid_of(g.nrb * 32 * 2 * g.nks)), dim3(256), 0, s, x, ldx, g,
+  hipLaunchKernelGGL(mx_quant_act_kernel, dim3(grid_of(g.nrb * 32 * 2 * g.nks * 4)), dim3(256), 0, s, x, ldx, g,
                      static_cast<uint8_t*>(dst));
   return hipGetLastError();
 }
