@@ -202,6 +202,15 @@ __device__ __forceinline__ void stage_frag(uint8_t* buf, int lane, int u, f32x4 
   *reinterpret_cast<f32x4*>(buf + swz(32 * jt + (lane & 31), 2 * e4 + (lane >> 5))) = v;
 }
 
+// Add v to float4 u of a half where stage_frag / stage_half put it (this
+// lane's own slot: no other lane touches it).
+template <int JT>
+__device__ __forceinline__ void add_frag(uint8_t* buf, int lane, int u, f32x4 v) {
+  const int jt = (u >> 2) % JT, e4 = u & 3;
+  f32x4* p = reinterpret_cast<f32x4*>(buf + swz(32 * jt + (lane & 31), 2 * e4 + (lane >> 5)));
+  *p = *p + v;
+}
+
 // Wavefront's half H (accumulator tiles acc[H][*]) into its LDS buffer:
 // activation row 32 jt + lane % 32 at byte 128 row, the 4 columns
 // 8 e4 + 4 (lane / 32) of the half as 16-byte chunk 2 e4 + lane / 32.
@@ -616,25 +625,50 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillBatch b, u
       __syncthreads();
       write_half(1);
     } else {
-      // Cut tile: publish this segment's sums straight from the
-      // accumulators (written through to memory, in accumulator order: float4
-      // u of lane l of wavefront v at ((v * 8 JT + u) * 64 + l) * 16 bytes),
-      // note this workgroup's XCD in the tile's mask, and let the last
-      // contributor to arrive add all contributions in k order.
+      // Cut tile.  Normally each contributor publishes its segment's sums
+      // straight from the accumulators (written through to memory, in
+      // accumulator order: float4 u of lane l of wavefront v at
+      // ((v * 8 JT + u) * 64 + l) * 16 bytes), notes its XCD in the tile's
+      // mask, and the last contributor to arrive adds all contributions in k
+      // order.  The head segment (the tile's first iterations, which ends this
+      // workgroup's share) usually finishes after all the others: if at that
+      // point every other contributor has arrived, the head finishes the tile
+      // itself, keeping the first half of its sums in LDS (staged as the
+      // output is) instead of writing them out and reading them back.
+      const int gtile = pv.tile_base + tile;
+      const unsigned xcc = xcc_id();
+      const int c_first = owner_of(tile_g0, b_total, b_wgs);
+      const int c_last = owner_of(tile_g0 + iters - 1, b_total, b_wgs);
       const int slot = g_begin >= tile_g0 ? 0 : 1;  // this workgroup's first or last segment
       const PartBuf mine = part_buf(partials, (size_t)w * 2 + slot, part_floats<JT>());
       const int frag_off = (wave * 8 * JT * 64 + lane) * 16;
+      __shared__ unsigned s_others_in;
+      bool head_finishes = false;
+      if (ib == 0) {
+        if (threadIdx.x == 0)
+          s_others_in = __hip_atomic_load(counters + gtile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                        (unsigned)(c_last - c_first);
+        __syncthreads();
+        head_finishes = s_others_in != 0u;
+      }
+      bool finisher;
+      if (head_finishes) {
+        stage_half<0, JT>(acc, mybuf, lane);  // the buffers are free: the main loop ended with a barrier
 #pragma unroll
-      for (int u = 0; u < 8 * JT; ++u) store_part(mine, frag_off, u * 1024, frag4<JT>(acc, u));
-      const int gtile = pv.tile_base + tile;
-      const unsigned xcc = xcc_id();
-      if (threadIdx.x == 0)
-        __hip_atomic_fetch_or(counters + kMaskBase + gtile, 1u << xcc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const int c_first = owner_of(tile_g0, b_total, b_wgs);
-      const int c_last = owner_of(tile_g0 + iters - 1, b_total, b_wgs);
-      if (arrive_last(counters + gtile, (unsigned)(c_last - c_first + 1))) {
-        // Every contributor ran on this XCD: their sums are in this XCD's L2
-        // and are read from there; else from memory.
+        for (int u = 4 * JT; u < 8 * JT; ++u) store_part(mine, frag_off, u * 1024, frag4<JT>(acc, u));
+        if (threadIdx.x == 0) __hip_atomic_store(counters + gtile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);  // the second half's sums have landed before they are read back
+        finisher = true;
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8 * JT; ++u) store_part(mine, frag_off, u * 1024, frag4<JT>(acc, u));
+        if (threadIdx.x == 0)
+          __hip_atomic_fetch_or(counters + kMaskBase + gtile, 1u << xcc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        finisher = arrive_last(counters + gtile, (unsigned)(c_last - c_first + 1));
+      }
+      if (finisher) {
+        // Every contributor that published ran on this XCD: their sums are in
+        // this XCD's L2 and are read from there; else from memory.
         const unsigned mask = __builtin_amdgcn_readfirstlane(
             __hip_atomic_load(counters + kMaskBase + gtile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
         __syncthreads();
@@ -649,15 +683,32 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillBatch b, u
         // stages them like its accumulators; the workgroup then writes the
         // half out coalesced.
         // Sums are ((p_first + p_next) + ...) in contributor (k) order; every
-        // contribution, this workgroup's own included, is read from its slot
-        // (the accumulators are dead once published), and with two
+        // contribution is read from its slot (the accumulators are dead once
+        // published) except the head's first half when the head finishes,
+        // which is staged already and has the others added in place; with two
         // contributions both slots' fragments are loaded together.
         auto finish_half = [&](auto hc, auto policy) __attribute__((always_inline)) {
           constexpr int H = decltype(hc)::value;
           constexpr int POL = decltype(policy)::value;
-          __syncthreads();  // the buffers are free
           // A half holds 4 JT float4s per lane, taken G at a time.
           constexpr int G = 4 * JT < 16 ? 4 * JT : 16;
+          if (H == 0 && head_finishes) {
+#pragma unroll
+            for (int q = 0; q < 4 * JT / G; ++q) {
+              for (int c = c_first + 1; c <= c_last; ++c) {
+                const PartBuf src = slot_of(c);
+                f32x4 v[G];
+#pragma unroll
+                for (int t = 0; t < G; ++t) v[t] = load_part<POL>(src, frag_off, (G * q + t) * 1024);
+#pragma unroll
+                for (int t = 0; t < G; ++t) add_frag<JT>(mybuf, lane, G * q + t, v[t]);
+              }
+            }
+            __syncthreads();
+            write_half(H);
+            return;
+          }
+          __syncthreads();  // the buffers are free
 #pragma unroll
           for (int q = 0; q < 4 * JT / G; ++q) {  // float4s u = 4 JT H + G q + [0, G)
             constexpr int U0 = 4 * JT * H;
