@@ -111,6 +111,32 @@ def test_w4a4_batched_matches_oracle(m):
         assert_within(got, y_ref, s, what=f"w4a4 batch {m}x{n}x{k}")
 
 
+def test_w4a4_batched_repeat_is_bit_identical_and_counters_return_to_zero():
+    """The prefill's gate, up and down in one launch, three times: the fix-up
+    order of cut tiles is fixed whichever workgroup finishes a tile (a head
+    segment that ends after the others finishes it from LDS and registers,
+    else the last to arrive from the published sums), and every call leaves
+    the counters zero."""
+    dev = device()
+    items = []
+    for mat in I.PREFILL_MATRICES:
+        codes, scales = I.nvfp4_matrix(I.PREFILL_512, mat.matrix_id, mat.n, mat.k)
+        mx = B.mx_pack(to_dev_u8(codes, dev), to_dev_u8(scales, dev))
+        x = to_dev_bf16(I.activations(I.PREFILL_512, mat.matrix_id, 512, mat.k), dev)
+        items.append((mx, mat.n, mat.k, I.TENSOR_SCALE, x, torch.empty((512, mat.n), dtype=torch.float32, device=dev)))
+    ws = torch.zeros(B.w4a4_batched_workspace_bytes(items, 512), dtype=torch.uint8, device=dev)
+    outs = []
+    for _ in range(3):
+        B.w4a4_batched(items, ws=ws)
+        outs.append([it[5].clone() for it in items])
+    torch.cuda.synchronize()
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    for a, b in zip(outs[0], outs[2]):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert int(torch.count_nonzero(ws[: 1 << 18])) == 0
+
+
 @pytest.mark.parametrize("mat", I.PREFILL_MATRICES, ids=lambda m: m.name)
 def test_w4a4_prefill_full_size(mat):
     """The 512-token prefill's matrices, sampled weight rows x all tokens; also
