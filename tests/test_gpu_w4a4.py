@@ -62,6 +62,27 @@ def test_w4a4_matches_oracle(m, n, k, y_dtype):
     assert_within(got, y_ref, s, extra=extra, what=f"w4a4 {m}x{n}x{k}")
 
 
+def test_w4a4_strided_rows():
+    """x and y as column slices of wider tensors (ldx > k, ldy > n)."""
+    dev = device()
+    m, n, k = 70, 150, 320
+    rng = np.random.default_rng(4242)
+    codes, scales = random_matrix(rng, n, k)
+    xb = wide_x(rng, m, k)
+    mx = B.mx_pack(to_dev_u8(codes, dev), to_dev_u8(scales, dev))
+    xwide = torch.zeros((m, k + 64), dtype=torch.bfloat16, device=dev)
+    xwide[:, 8:8 + k] = to_dev_bf16(xb, dev)
+    ywide = torch.full((m, n + 40), 7.0, dtype=torch.float32, device=dev)
+    B.w4a4_gemm(mx, n, k, I.TENSOR_SCALE, xwide[:, 8:8 + k], y=ywide[:, 16:16 + n])
+    torch.cuda.synchronize()
+    rxc, rxs = oracle.mx_from_bf16(xb)
+    wc, wsc = oracle.mx_from_nvfp4(codes, scales)
+    y_ref, s = oracle.mx_gemm(wc, wsc, I.TENSOR_SCALE, rxc, rxs, nthreads=oracle_threads())
+    got = ywide.cpu().numpy().astype(np.float64)
+    assert_within(got[:, 16:16 + n], y_ref, s, what="w4a4 strided")
+    assert np.all(got[:, :16] == 7.0) and np.all(got[:, 16 + n:] == 7.0)   # nothing written outside y
+
+
 def test_w4a4_workspace_reuse():
     """One workspace through calls of different shapes, each with tiles cut
     between workgroups: every call leaves the counters as it found them."""
