@@ -16,6 +16,11 @@
 // (j = 0..31, low nibble first) -- exactly the instruction's A / B operand for
 // one lane -- and 64 scale bytes, after all codes, at (rb * nks + ks) * 64 + l.
 // Rows past the matrix and k past K are zero.
+//
+// This file holds the conversions into that layout and the entry points; the
+// product itself is the prefill's stream-K kernel with MX operands
+// (prefill.hip): x is quantised into the workspace, problem by problem, and
+// one launch covers up to eight products.
 #include <vector>
 
 #include "device_common.h"
