@@ -227,6 +227,19 @@ def test_w4a4_validation(L):
     assert L.nvfp4_w4a4_batched(arr, 2, 0, 1, None, 0, None) == B.NVFP4_OK      # m = 0
     arr[1].y = arr[0].y
     assert L.nvfp4_w4a4_batched(arr, 2, 300, 1, None, 0, None) == B.NVFP4_ERR_ARG   # shared output
+    # single product: shape, dtype, stride, pointer, alignment and workspace checks before any launch
+    W, X, Y = A, A + 0x1000, A + 0x2000
+    g = L.nvfp4_w4a4_gemm
+    assert g(W, 64, 48, 1.0, X, 4, 48, Y, 64, 1, None, 0, None) == B.NVFP4_ERR_SHAPE      # k % 32
+    assert g(W, 64, 64, 1.0, X, 4, 64, Y, 64, 7, None, 0, None) == B.NVFP4_ERR_DTYPE
+    assert g(W, 64, 64, 1.0, X, 4, 60, Y, 64, 1, None, 0, None) == B.NVFP4_ERR_SHAPE      # ldx < k
+    assert g(W, 64, 64, 1.0, X, 4, 64, Y, 32, 1, None, 0, None) == B.NVFP4_ERR_SHAPE      # ldy < n
+    assert g(None, 64, 64, 1.0, X, 4, 64, Y, 64, 1, None, 0, None) == B.NVFP4_ERR_NULL
+    assert g(W + 8, 64, 64, 1.0, X, 4, 64, Y, 64, 1, None, 0, None) == B.NVFP4_ERR_ALIGN
+    assert g(W, 64, 64, 1.0, X, 4, 64, Y, 64, 1, None, 0, None) == B.NVFP4_ERR_WORKSPACE
+    assert g(W, 64, 64, 1.0, X, 0, 64, Y, 64, 1, None, 0, None) == B.NVFP4_OK              # m = 0
+    assert g(W, 0, 64, 1.0, X, 4, 64, Y, 64, 1, None, 0, None) == B.NVFP4_OK               # n = 0
+    assert g(W, 64, 64, 1.0, X, -1, 64, Y, 64, 1, None, 0, None) == B.NVFP4_ERR_SHAPE
 
 
 def test_expert_cache_validation(L):
