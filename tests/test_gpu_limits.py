@@ -32,6 +32,7 @@ def big():
     k = 1280
     codes, scales = device_matrix(MAX_N, k, 71, dev)
     packed = B.pack(codes, scales)
+    mx = B.mx_pack(codes, scales)
     rows = sample_rows(MAX_N, 256, 72)
     rows = np.union1d(rows, np.arange(MAX_N - 64, MAX_N))   # the whole last row tile
     idx = torch.from_numpy(rows).to(dev)
@@ -39,12 +40,12 @@ def big():
     s_rows = scales.index_select(0, idx).cpu().numpy()
     del codes, scales
     torch.cuda.synchronize()
-    return dev, k, packed, rows, c_rows, s_rows
+    return dev, k, packed, rows, c_rows, s_rows, mx
 
 
 def test_gemv_max_rows(big):
     """Split K in two workgroups per row tile: all 65536 counters in use, left zero afterwards."""
-    dev, k, packed, rows, c_rows, s_rows = big
+    dev, k, packed, rows, c_rows, s_rows, _ = big
     x = I.activations(73, 0, 1, k)[0]
     ws = torch.zeros(B.gemv_workspace_bytes(MAX_N, k), dtype=torch.uint8, device=dev)
     y = B.gemv(packed, MAX_N, k, I.TENSOR_SCALE, to_dev_bf16(x, dev), ws=ws)
@@ -57,7 +58,7 @@ def test_gemv_max_rows(big):
 @pytest.mark.parametrize("m", [32, 64])
 def test_gemm_max_rows(big, m):
     """The skinny path (m = 32) and the prefill path (m = 64) at the row limit, fp32 output."""
-    dev, k, packed, rows, c_rows, s_rows = big
+    dev, k, packed, rows, c_rows, s_rows, _ = big
     x = I.activations(74, m, m, k)
     y = B.gemm(packed, MAX_N, k, I.TENSOR_SCALE, to_dev_bf16(x, dev), y_dtype=torch.float32)
     torch.cuda.synchronize()
@@ -65,3 +66,24 @@ def test_gemm_max_rows(big, m):
     got = y.index_select(1, idx).cpu().numpy().astype(np.float64)
     y_ref, s = oracle.gemm(c_rows, s_rows, I.TENSOR_SCALE, x, nthreads=oracle_threads())
     assert_within(got, y_ref, s, what=f"gemm m={m} at the row limit")
+
+
+def test_w4a4_max_rows(big):
+    """The W4A4 product at the row limit with 300 activation rows: two row slabs
+    of 256, so the launch's 32768 output tiles use every tile counter and XCD
+    mask of the stream-K area; fp32 output, sampled weight rows against the
+    oracle's MX product."""
+    dev, k, packed, rows, c_rows, s_rows, mx = big
+    m = 300
+    x = I.activations(75, m, m, k)
+    ws = torch.zeros(B.w4a4_workspace_bytes(m, k), dtype=torch.uint8, device=dev)
+    y = B.w4a4_gemm(mx, MAX_N, k, I.TENSOR_SCALE, to_dev_bf16(x, dev), y_dtype=torch.float32, ws=ws)
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(rows).to(dev)
+    got = y.index_select(1, idx).cpu().numpy().astype(np.float64)
+    del y
+    wc, wsc = oracle.mx_from_nvfp4(c_rows, s_rows)
+    xc, xs = oracle.mx_from_bf16(x)
+    y_ref, s = oracle.mx_gemm(wc, wsc, I.TENSOR_SCALE, xc, xs, nthreads=oracle_threads())
+    assert_within(got, y_ref, s, what="w4a4 m=300 at the row limit")
+    assert int(ws[:262144].count_nonzero()) == 0
