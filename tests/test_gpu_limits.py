@@ -87,3 +87,29 @@ def test_w4a4_max_rows(big):
     y_ref, s = oracle.mx_gemm(wc, wsc, I.TENSOR_SCALE, xc, xs, nthreads=oracle_threads())
     assert_within(got, y_ref, s, what="w4a4 m=300 at the row limit")
     assert int(ws[:262144].count_nonzero()) == 0
+
+
+def test_activation_rows_beyond_one_launch(big):
+    """513 activation rows at the row limit: three slabs of 256 rows would need
+    49152 tile counters, so the prefill and the W4A4 product each run rows
+    0..511 and then row 512 as a second launch (activation and output offsets
+    of a later launch)."""
+    dev, k, packed, rows, c_rows, s_rows, mx = big
+    m = 513
+    x = I.activations(76, m, m, k)
+    xd = to_dev_bf16(x, dev)
+    idx = torch.from_numpy(rows).to(dev)
+    y = B.gemm(packed, MAX_N, k, I.TENSOR_SCALE, xd, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = y.index_select(1, idx).cpu().numpy().astype(np.float64)
+    del y
+    y_ref, s = oracle.gemm(c_rows, s_rows, I.TENSOR_SCALE, x, nthreads=oracle_threads())
+    assert_within(got, y_ref, s, what="prefill m=513 at the row limit")
+    y = B.w4a4_gemm(mx, MAX_N, k, I.TENSOR_SCALE, xd, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = y.index_select(1, idx).cpu().numpy().astype(np.float64)
+    del y
+    wc, wsc = oracle.mx_from_nvfp4(c_rows, s_rows)
+    xc, xs = oracle.mx_from_bf16(x)
+    y_ref, s = oracle.mx_gemm(wc, wsc, I.TENSOR_SCALE, xc, xs, nthreads=oracle_threads())
+    assert_within(got, y_ref, s, what="w4a4 m=513 at the row limit")
