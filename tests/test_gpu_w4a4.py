@@ -132,6 +132,30 @@ def test_w4a4_batched_matches_oracle(m):
         assert_within(got, y_ref, s, what=f"w4a4 batch {m}x{n}x{k}")
 
 
+@pytest.mark.parametrize("m", [5, 70, 300])
+def test_w4a4_batched_ten_problems(m):
+    """Ten problems (two launches of up to eight), ragged shapes, bf16 output."""
+    dev = device()
+    rng = np.random.default_rng(900 + m)
+    shapes = [(1, 32), (100, 96), (65, 288), (200, 1056), (130, 2336), (64, 256), (7, 4128), (300, 512),
+              (33, 64), (129, 1024)]
+    items, refs = [], []
+    for n, k in shapes:
+        codes, scales = random_matrix(rng, n, k)
+        xb = wide_x(rng, m, k)
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        items.append((B.mx_pack(to_dev_u8(codes, dev), to_dev_u8(scales, dev)), n, k, I.TENSOR_SCALE,
+                      to_dev_bf16(xb, dev), y))
+        refs.append((codes, scales, xb))
+    B.w4a4_batched(items)
+    torch.cuda.synchronize()
+    for (mx, n, k, st, xd, y), (codes, scales, xb) in zip(items, refs):
+        rxc, rxs = oracle.mx_from_bf16(xb)
+        wc, wsc = oracle.mx_from_nvfp4(codes, scales)
+        y_ref, s = oracle.mx_gemm(wc, wsc, st, rxc, rxs, nthreads=oracle_threads())
+        assert_within(bf16_to_f64(y), y_ref, s, extra=ulp_bf16(y_ref), what=f"w4a4 batch of ten m={m} {n}x{k}")
+
+
 def test_w4a4_batched_repeat_is_bit_identical_and_counters_return_to_zero():
     """The prefill's gate, up and down in one launch, three times: the fix-up
     order of cut tiles is fixed whichever workgroup finishes a tile (a head
