@@ -878,6 +878,42 @@ hipError_t launch_prefill_batch(const Problem* p, int count, int64_t m, bool y_b
   return hipSuccess;
 }
 
+// Workgroup count for an MX launch.  Its iterations are cheap next to the
+// fix-up of a tile cut between workgroups (measured: one cut costs about as
+// much as 40 iterations), so fewer, longer shares can win when their
+// boundaries fall on tile boundaries -- e.g. 204 shares of 160 iterations over
+// gate, up and down at 512 tokens cut no gate or up tile (~10 % faster than 256
+// shares, which cut nearly every tile).  Candidates: 256, and every count in
+// [192, 256] whose share is a whole number of one problem's tiles; each is
+// scored as its share length plus 32 iterations per cut boundary per workgroup.
+int64_t mx_share_count(const PrefillBatch& b, int nq) {
+  constexpr int64_t kCutCost = 32, kLow = 192;
+  const int64_t total = b.total;
+  auto cuts = [&](int64_t wgs) {
+    int64_t n = 0;
+    for (int64_t w = 1; w < wgs; ++w) {
+      const int64_t g = w * total / wgs;
+      int p = 0;
+      for (int i = 1; i < nq; ++i)
+        if (g >= b.iter_begin[i]) p = i;
+      if ((g - b.iter_begin[p]) % b.iters[p] != 0) ++n;
+    }
+    return n;
+  };
+  auto score = [&](int64_t wgs) { return (total + wgs - 1) / wgs + (2 * kCutCost * cuts(wgs)) / wgs; };
+  int64_t best = kPreWgs, best_score = score(kPreWgs);
+  for (int i = 0; i < nq; ++i)
+    for (int64_t j = 1; j <= 64; ++j) {
+      const int64_t len = j * b.iters[i];
+      if (total % len != 0) continue;
+      const int64_t wgs = total / len;
+      if (wgs < kLow || wgs >= kPreWgs) continue;
+      const int64_t sc = score(wgs);
+      if (sc < best_score) best = wgs, best_score = sc;
+    }
+  return best;
+}
+
 size_t w4a4_streamk_bytes() { return kCounterBytes + (size_t)2 * kPreWgs * part_bytes(8); }
 
 hipError_t launch_w4a4_batch(const MxProblem* p, int count, int64_t m, bool y_bf16, void* ws, hipStream_t s) {
@@ -939,6 +975,7 @@ hipError_t launch_w4a4_batch(const MxProblem* p, int count, int64_t m, bool y_bf
       b.total = it;
       int64_t wgs = it / kMinShare;
       wgs = wgs < 1 ? 1 : (wgs > kPreWgs ? kPreWgs : wgs);
+      if (wgs == kPreWgs) wgs = mx_share_count(b, nq);
       b.wgs = (int)wgs;
       if (jt == 8) launch_one<8, true, true>(b, (unsigned)wgs, counters, partials, s);
       else launch_one<4, true, true>(b, (unsigned)wgs, counters, partials, s);
