@@ -286,6 +286,7 @@ def test_moe_matches_torch_float64_chain(top_k):
     assert np.array_equal(ids, tids.numpy())
     assert np.allclose(g, gt.numpy(), rtol=1e-14)
     yref = torch.zeros(t, hidden, dtype=torch.float64)
+    ybref = torch.zeros(t, hidden, dtype=torch.float64)
     for ti in range(t):
         for j in range(top_k):
             ex = int(tids[ti, j])
@@ -294,7 +295,39 @@ def test_moe_matches_torch_float64_chain(top_k):
             wd = torch.from_numpy(decode_independent(w.down_codes[ex], w.down_scales[ex], w.down_st[ex]))
             h = torch.nn.functional.silu(wg @ xt[ti]) * (wu @ xt[ti])
             yref[ti] += gt[ti, j] * (wd @ h)
+            ybref[ti] += gt[ti, j] * (wd.abs() @ h.abs())
+    # ybound is the magnitude sum the end-to-end bound scales with: sum_j g_j |Wd| |h_j|
+    assert np.allclose(yb, ybref.numpy(), rtol=1e-12, atol=0)
+    assert np.all(yb >= np.abs(y) * (1 - 1e-12))
     assert np.all(np.abs(y - yref.numpy()) <= 1e-12 * yb + 1e-300)
+
+
+def test_moe_ybound_closed_form_on_signed_and_scaled_weights():
+    """ybound on a hand-built layer: one expert, h known in closed form.
+
+    Gate codes all 0 except one weight, so G = w*x exactly; up weights give U;
+    down weights of alternating sign make |Wd h| differ from |Wd| |h|, so a
+    bound computed from the signed sum (a dropped abs) fails here."""
+    hidden, inter, t = 32, 16, 1
+    gc = np.zeros((1, inter, hidden // 2), np.uint8)
+    uc = np.zeros((1, inter, hidden // 2), np.uint8)
+    gc[0, :, 0] = 2                               # G[i] = 1.0 * x[0]  (code 2 = 1.0 at k = 0)
+    uc[0, :, 0] = 4                               # U[i] = 2.0 * x[0]  (code 4 = 2.0)
+    gs = np.full((1, inter, hidden // 16), 0x38, np.uint8)   # E4M3 1.0
+    us = gs.copy()
+    dc = np.zeros((1, hidden, inter // 2), np.uint8)
+    dc[0, :, :] = (10 << 4) | 2                   # codes 2 (+1.0) and 10 (-1.0) alternate along i
+    ds = np.full((1, hidden, inter // 16), 0x40, np.uint8)   # E4M3 2.0
+    one = np.ones(1, np.float32)
+    xv = np.zeros((t, hidden), np.float32)
+    xv[0, 0] = 1.5
+    x = I.bf16_round(xv)
+    logits = np.zeros((t, 1), np.float32)
+    ids, g, y, yb = oracle.moe((gc, gs, one), (uc, us, one), (dc, ds, one), x, logits, 1)
+    hval = (1.5 / (1.0 + math.exp(-1.5))) * 3.0   # silu(1.5) * (2 * 1.5)
+    # d[o] = sum_i 2 * (+-1) * h = 0 (inter even); |d| bound = sum_i 2 * h = 2 * inter * h
+    assert np.all(np.abs(y) <= 1e-15)
+    assert np.allclose(yb, 2.0 * inter * hval, rtol=1e-15, atol=0)
 
 
 def test_moe_single_expert_reduces_to_dense_chain():

@@ -91,3 +91,118 @@ def test_zero_blocks():
     c, s = oracle.mx_from_bf16(x)
     assert s[0, 0] == 0 and s[0, 1] == 0 and s[1, 0] == 0 and not c[0].any() and not c[1, :16].any()
     assert s[1, 1] == 125                                      # 1.5: exponent 0 - 2
+
+
+# Maps of an E2M1 magnitude code (0..7) to the code of half its value, where
+# half of it is on the grid: 0->0, 1.0->0.5, 2->1, 3->1.5, 4->2, 6->3.
+HALF_CODE = {0: 0, 2: 1, 4: 2, 5: 3, 6: 4, 7: 5}
+
+
+def test_mx_scales_vary_by_row_and_block():
+    """MX-representable operands whose power-of-two scales differ per row and per
+    32-block, and per 16-half inside a weight block.
+
+    Weights: in each 32-block, one 16-half has E4M3 scale 2^a (a byte from
+    0x08..0x48, mantissa 0) and a magnitude-6 code; the other half either shares
+    that byte or has scale 2^(a-1) with codes whose halves are on the grid.  So
+    the MX scale is 2^a, E8M0 byte 127 + a, the first half's codes are
+    unchanged and the other half's codes are those of its values / 2^a.
+    Activations: E2M1 values times 2^e with e drawn per (row, block) and a 4 or
+    6 in every block, so the E8M0 byte is 127 + e and the codes are the grid codes.
+    A requantiser that drops the E4M3 scale or reads another 16-half's, or an MX
+    product that reads a scale at the wrong row or block, gives other bytes or
+    another product.  The product then equals the exact NVFP4 one bit for bit
+    (s_t = 1, so every partial sum is exact in fp64)."""
+    rng = np.random.default_rng(17)
+    n, k, m = 24, 256, 7
+    nb = k // 32
+    codes = rng.integers(0, 16, size=(n, k)).astype(np.uint8)
+    scales = np.zeros((n, k // 16), np.uint8)
+    want_mc = np.zeros((n, k), np.uint8)
+    want_ms = np.zeros((n, nb), np.uint8)
+    for r in range(n):
+        for b in range(nb):
+            ebyte = int(rng.integers(1, 10))              # E4M3 exponent field: 2^(ebyte - 7), 2^-6 .. 2^2
+            a = ebyte - 7
+            top = int(rng.integers(0, 2))                 # which 16-half holds the block's largest value
+            lo = int(rng.integers(0, 3))                  # 0: both halves share 2^a; else the other has 2^(a-1)
+            half = [32 * b, 32 * b + 16]
+            big, other = half[top], half[1 - top]
+            codes[r, big + int(rng.integers(0, 16))] = 7 | (8 if rng.integers(0, 2) else 0)
+            scales[r, big // 16] = ebyte << 3
+            want_mc[r, big:big + 16] = codes[r, big:big + 16]
+            if lo == 0 or ebyte == 1:
+                scales[r, other // 16] = ebyte << 3
+                want_mc[r, other:other + 16] = codes[r, other:other + 16]
+            else:
+                mags = rng.choice(np.array(list(HALF_CODE), np.uint8), size=16)
+                signs = rng.integers(0, 2, size=16).astype(np.uint8) << 3
+                codes[r, other:other + 16] = mags | signs
+                scales[r, other // 16] = (ebyte - 1) << 3
+                want_mc[r, other:other + 16] = np.array([HALF_CODE[int(c)] for c in mags], np.uint8) | signs
+            want_ms[r, b] = 127 + a
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    want_packed = (want_mc[:, 0::2] | (want_mc[:, 1::2] << 4)).astype(np.uint8)
+
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.0, -0.5, -1, -1.5, -2, -3, -4, -6], np.float64)
+    xcode = rng.integers(0, 16, size=(m, k)).astype(np.uint8)
+    xexp = rng.integers(-6, 7, size=(m, nb))
+    for r in range(m):
+        for b in range(nb):
+            xcode[r, 32 * b + int(rng.integers(0, 32))] = int(rng.choice([6, 7, 14, 15]))
+    xv = grid[xcode] * np.exp2(np.repeat(xexp, 32, axis=1))
+    xb = bf16_bits(xv.astype(np.float32))
+    want_xc = (xcode[:, 0::2] | (xcode[:, 1::2] << 4)).astype(np.uint8)
+
+    mc, ms = oracle.mx_from_nvfp4(packed, scales)
+    xc, xs = oracle.mx_from_bf16(xb)
+    assert np.array_equal(ms, want_ms)
+    assert np.array_equal(mc, want_packed)
+    assert np.array_equal(xs, (127 + xexp).astype(np.uint8))
+    assert np.array_equal(xc, want_xc)
+    one = np.float32(1.0)
+    y, s = oracle.mx_gemm(mc, ms, one, xc, xs)
+    ye, se = oracle.gemm(packed, scales, one, xb)
+    assert np.array_equal(y, ye) and np.array_equal(s, se)
+    # A row subset reads the same rows' scales.
+    rows = np.array([n - 1, 3, 3, 0], np.int64)
+    yr, sr = oracle.mx_gemm(mc, ms, one, xc, xs, rows=rows)
+    assert np.array_equal(yr, y[:, rows]) and np.array_equal(sr, s[:, rows])
+
+
+def test_mx_product_is_s_t_times_the_unscaled_sum():
+    """The per-tensor scale multiplies the exact fp64 sum once (s_t after accumulation)."""
+    rng = np.random.default_rng(19)
+    n, k, m = 9, 96, 3
+    wc = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    ws = rng.integers(110, 140, size=(n, k // 32), dtype=np.uint8)
+    xc = rng.integers(0, 256, size=(m, k // 2), dtype=np.uint8)
+    xs = rng.integers(110, 140, size=(m, k // 32), dtype=np.uint8)
+    y1, s1 = oracle.mx_gemm(wc, ws, np.float32(1.0), xc, xs)
+    st = I.TENSOR_SCALE
+    y2, s2 = oracle.mx_gemm(wc, ws, st, xc, xs)
+    assert np.array_equal(y2, float(st) * y1) and np.array_equal(s2, float(st) * s1)
+    # and the unscaled sum is the plain definition over decoded operands
+    def dec(c, s):
+        codes = np.stack([c & 15, c >> 4], axis=-1).reshape(c.shape[0], -1)
+        mag = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float64)[codes & 7]
+        val = np.where(codes & 8, -mag, mag)
+        return val * np.exp2(np.repeat(s.astype(np.float64) - 127, 32, axis=1))
+    W, X = dec(wc, ws), dec(xc, xs)
+    assert np.allclose(y1, X @ W.T, rtol=0, atol=1e-12 * (np.abs(X) @ np.abs(W).T).max())
+    assert np.allclose(s1, np.abs(X) @ np.abs(W).T, rtol=1e-15)
+
+
+def test_lone_subnormal_blocks_use_the_clamped_scale():
+    """A block holding one bf16 subnormal: the scale exponent clamps to -127
+    (byte 0), so the element's code is the E2M1 value nearest v / 2^-127."""
+    cases = [(2.0 ** -128, 1), (3 * 2.0 ** -128, 3), (2.0 ** -127, 2), (2.0 ** -130, 0), (-(2.0 ** -129), 8),      # -0.25: a tie, to the even code (-0)
+             (5 * 2.0 ** -128, 4)]                              # 2.5 ties to the even code 4 (2.0)
+    x = np.zeros((len(cases), 32), np.float32)
+    for i, (v, _) in enumerate(cases):
+        x[i, 17] = v
+    c, s = oracle.mx_from_bf16(bf16_bits(x))
+    assert np.all(s[:, 0] == 0)
+    for i, (_, code) in enumerate(cases):
+        assert (c[i, 8] >> 4) == code, (cases[i], c[i, 8] >> 4)
+        assert not np.delete(c[i], 8).any() and (c[i, 8] & 15) == 0
