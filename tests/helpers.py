@@ -83,3 +83,51 @@ def random_matrix(rng, n, k):
     codes = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
     scales = I.e4m3_round(np.exp2(rng.uniform(-6, 2, size=(n, k // 16))))
     return codes, scales
+
+
+# Largest |silu'(z)| over all z (about 1.0998, near z = 2.4).
+SILU_SLOPE = 1.1
+# Relative error of the fp32 silu(G) * U the expert kernel evaluates before
+# rounding h to bf16: expf within 1 ulp, then an add, a correctly rounded
+# division and a multiply (about 5 * 2^-24), taken with margin.
+SILU_FP32_REL = 2.0 ** -20
+# Relative tolerance of the GPU's fp32 routing weights against the fp64 ones.
+G_REL = 1e-6
+
+
+def moe_end_to_end_extra(w, x, ids_ref, g_ref, ybound, nthreads=None):
+    """What the fp64 chain's y may differ from a correct GPU layer's y by,
+    beyond TOL * ybound, per output [t][hidden].
+
+    The GPU layer rounds h to bf16 after an fp32 silu of fp32 gate and up sums,
+    so its h differs from the fp64 chain's h by at most, per element,
+      dh = P + ulp_bf16(|h| + P) / 2,
+      P  = 1.1 * eG * (|U| + eU) + |silu(G)| * eU + 2^-20 * |h|,
+    where eG = TOL * S_G and eU = TOL * S_U are the gate and up stages' own
+    bounds, 1.1 bounds |silu'| and 2^-20 the fp32 evaluation.  That moves each
+    down output by at most |Wd| dh (plus TOL of it, inside the down stage's
+    bound), and the routing weights' tolerance G_REL moves y by G_REL of the
+    bound's magnitude sum.  So:
+      extra[t] = G_REL * (1 + TOL) * ybound[t] + (1 + TOL) * (1 + G_REL) * sum_j g_j |Wd_j| dh_j.
+    """
+    import oracle
+    t, hidden = x.shape
+    top_k = ids_ref.shape[1]
+    extra = G_REL * (1 + TOL) * np.asarray(ybound, np.float64).copy()
+    wd_abs = {}
+    for ti in range(t):
+        xs = np.ascontiguousarray(x[ti:ti + 1])
+        for j in range(top_k):
+            ex = int(ids_ref[ti, j])
+            gy, gs = oracle.gemm(w.gate_codes[ex], w.gate_scales[ex], w.gate_st[ex], xs, nthreads=nthreads)
+            uy, us = oracle.gemm(w.up_codes[ex], w.up_scales[ex], w.up_st[ex], xs, nthreads=nthreads)
+            G, U = gy[0], uy[0]
+            eG, eU = TOL * gs[0], TOL * us[0]
+            sG = oracle.silu(G)
+            h = sG * U
+            p = SILU_SLOPE * eG * (np.abs(U) + eU) + np.abs(sG) * eU + SILU_FP32_REL * np.abs(h)
+            dh = p + 0.5 * ulp_bf16(np.abs(h) + p)
+            if ex not in wd_abs:
+                wd_abs[ex] = np.abs(oracle.dequant(w.down_codes[ex], w.down_scales[ex], w.down_st[ex]))
+            extra[ti] += (1 + TOL) * (1 + G_REL) * g_ref[ti, j] * (wd_abs[ex] @ dh)
+    return extra

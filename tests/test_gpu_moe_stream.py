@@ -1,6 +1,7 @@
-"""GPU: routed experts streamed from pinned host memory (f3) against the same
-layer with the experts device-resident -- bit-identical outputs -- and the
-cache's bookkeeping (hits, least-recently-used eviction, the slot limit)."""
+"""GPU: routed experts streamed from pinned host memory (f3) against the
+oracle (every stage and the whole layer, as for the resident layer), against
+the same layer with the experts device-resident (bit-identical outputs), and
+the cache's bookkeeping (hits, least-recently-used eviction, the slot limit)."""
 import numpy as np
 import pytest
 import torch
@@ -8,6 +9,7 @@ import torch
 from bit_quantized_decode_amd import binding as B
 from bit_quantized_decode_amd import inputs as I
 from helpers import device, to_dev_bf16, to_dev_u8
+from moe_checks import check_moe
 
 pytestmark = pytest.mark.gpu
 
@@ -31,22 +33,22 @@ def setup():
     w = I.moe_weights(77, shape)
     (pg, sg), (pu, su), (pd, sd) = pools(w, dev)
     st = [torch.from_numpy(v).to(dev) for v in (w.gate_st, w.up_st, w.down_st)]
-    return dev, shape, (pg, pu, pd, sg, su, sd), st
+    return dev, shape, (pg, pu, pd, sg, su, sd), st, w
 
 
-def call(dev, shape, x, logits, wts, st, stream_obj=None):
+def call(dev, shape, x, logits, wts, st, stream_obj=None, debug=False):
     pg, pu, pd, sg, su, sd = wts
     args = (to_dev_bf16(x, dev), torch.from_numpy(logits).to(dev), shape.top_k)
     if stream_obj is None:
-        o = B.moe_grouped(*args, pg, pu, pd, sg, su, sd, *st, shape.inter)
+        o = B.moe_grouped(*args, pg, pu, pd, sg, su, sd, *st, shape.inter, debug=debug)
     else:
-        o = B.moe_grouped(*args, stream_obj, None, None, None, None, None, *st, shape.inter)
+        o = B.moe_grouped(*args, stream_obj, None, None, None, None, None, *st, shape.inter, debug=debug)
     torch.cuda.synchronize()
     return {k: v.clone() for k, v in o.items()}
 
 
 def test_streamed_equals_resident_over_calls(setup):
-    dev, shape, wts, st = setup
+    dev, shape, wts, st, w = setup
     pg, pu, pd, sg, su, sd = wts
     es = B.ExpertStream(pg, pu, pd, sg, su, sd, shape.experts, 16, dev)
     seen = set()
@@ -54,7 +56,9 @@ def test_streamed_equals_resident_over_calls(setup):
         x = I.activations(78, r, shape.tokens, shape.hidden)
         logits = I.router_logits(79 + r, shape.tokens, shape.experts)
         ref = call(dev, shape, x, logits, wts, st)
-        got = call(dev, shape, x, logits, wts, st, es)
+        got = call(dev, shape, x, logits, wts, st, es, debug=True)
+        # The streamed layer against the oracle: routing, grouping, every stage, end to end.
+        check_moe(w, x, logits, shape.top_k, o=got)
         for key in ("y", "topk_ids", "topk_weights", "expert_counts", "expert_offsets", "perm"):
             assert torch.equal(got[key].view(torch.int32) if got[key].dtype == torch.float32 else got[key],
                                ref[key].view(torch.int32) if ref[key].dtype == torch.float32 else ref[key]), (r, key)
@@ -73,7 +77,7 @@ def test_streamed_equals_resident_over_calls(setup):
 
 
 def test_lru_eviction_and_slot_limit(setup):
-    dev, shape, wts, st = setup
+    dev, shape, wts, st, w = setup
     pg, pu, pd, sg, su, sd = wts
     # Logits that route every token to experts {0, 1, 2}, then to {3, 4, 5}, then {0, 1, 2} again.
     def routed_to(ids):
@@ -89,8 +93,9 @@ def test_lru_eviction_and_slot_limit(setup):
     assert sorted(es.expert_in.tolist()) == [2, 3, 4, 5] or sorted(es.expert_in.tolist()) == [0, 3, 4, 5] \
         or sorted(es.expert_in.tolist()) == [1, 3, 4, 5]
     ref = call(dev, shape, x, routed_to([0, 1, 2]), wts, st)
-    got = call(dev, shape, x, routed_to([0, 1, 2]), wts, st, es)
+    got = call(dev, shape, x, routed_to([0, 1, 2]), wts, st, es, debug=True)
     assert es.stats()["fetched"] == 2                          # one of them survived
+    check_moe(w, x, routed_to([0, 1, 2]), shape.top_k, o=got)  # refilled slots against the oracle
     assert torch.equal(got["y"].view(torch.int32), ref["y"].view(torch.int32))
     # More routed experts than slots: refused after routing.
     lg = I.router_logits(81, shape.tokens, shape.experts)
