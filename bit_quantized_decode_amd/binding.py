@@ -30,7 +30,7 @@ EXPORTED = (
     "nvfp4_gemm_batched", "nvfp4_moe_workspace_bytes", "nvfp4_moe_grouped", "nvfp4_quantize_workspace_bytes",
     "nvfp4_quantize", "nvfp4_expert_cache_reset", "nvfp4_moe_streamed", "nvfp4_mx_packed_bytes", "nvfp4_mx_pack",
     "nvfp4_mx_unpack", "nvfp4_w4a4_workspace_bytes", "nvfp4_w4a4_gemm", "nvfp4_w4a4_batched_workspace_bytes",
-    "nvfp4_w4a4_batched",
+    "nvfp4_w4a4_batched", "nvfp4_gemv_batched_noalloc",
 )
 
 
@@ -106,6 +106,7 @@ def lib():
         "nvfp4_gemm": (I, [P, i64, i64, ctypes.c_float, P, i64, i64, P, i64, I, P, sz, P]),
         "nvfp4_gemv_batched_workspace_bytes": (I, [ctypes.POINTER(Problem), I, ctypes.POINTER(sz)]),
         "nvfp4_gemv_batched": (I, [ctypes.POINTER(Problem), I, P, sz, P]),
+        "nvfp4_gemv_batched_noalloc": (I, [ctypes.POINTER(Problem), I, P]),
         "nvfp4_gemm_batched_workspace_bytes": (I, [ctypes.POINTER(Problem), I, i64, ctypes.POINTER(sz)]),
         "nvfp4_gemm_batched": (I, [ctypes.POINTER(Problem), I, i64, I, P, sz, P]),
         "nvfp4_moe_workspace_bytes": (I, [ctypes.POINTER(MoeArgs), ctypes.POINTER(sz)]),
@@ -359,6 +360,13 @@ def gemv_batched(items, ws=None, stream=None):
     if ws is None and items:
         ws = workspace(need.value, items[0][4].device)
     check(L.nvfp4_gemv_batched(arr, len(items), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def gemv_batched_noalloc(items, stream=None):
+    """nvfp4_gemv_batched_noalloc: the batched GEMV with the library's static
+    device scratch instead of a workspace (same items as gemv_batched)."""
+    arr = problems(items)
+    check(lib().nvfp4_gemv_batched_noalloc(arr, len(items), _stream(stream)))
 
 
 def gemv_batched_prepared(items, ws=None, stream=None):

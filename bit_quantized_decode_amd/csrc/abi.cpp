@@ -1,6 +1,8 @@
 // The C ABI of libnvfp4.so (declared in include/nvfp4.h): argument
 // validation, status codes and dispatch to the kernel launchers.  Nothing here
-// allocates, frees or synchronises, and no exception leaves this file.
+// allocates or frees device memory; the one synchronisation is
+// nvfp4_moe_streamed's read-back of the expert counts.  No exception leaves
+// this file.
 #include <hip/hip_runtime_api.h>
 
 #include <cstdarg>
@@ -413,6 +415,26 @@ int nvfp4_gemv_batched(const nvfp4_problem* problems, int count, void* workspace
     return fail(NVFP4_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, workspace ? workspace_bytes : 0);
   if (need > 0 && !aligned16(workspace)) return fail(NVFP4_ERR_ALIGN, "workspace must be 16-byte aligned");
   return hip_status(nvfp4::launch_gemv_batch(pr.data(), count, workspace, (hipStream_t)stream), "gemv batch launch");
+  NVFP4_GUARD_END
+}
+
+int nvfp4_gemv_batched_noalloc(const nvfp4_problem* problems, int count, void* stream) {
+  NVFP4_GUARD_BEGIN
+  if (count > nvfp4::kNoallocMaxProblems)
+    return fail(NVFP4_ERR_ARG, "count=%d above the %d problems this call takes", count, nvfp4::kNoallocMaxProblems);
+  nvfp4::Problem pr[nvfp4::kNoallocMaxProblems];
+  NVFP4_TRY(check_batch(problems, count, -1, NVFP4_F32, true, pr));
+  if (count <= 0) return ok();
+  const size_t need = nvfp4::gemv_batch_workspace_bytes(pr, count);
+  if (need > nvfp4::kStaticScratchBytes)
+    return fail(NVFP4_ERR_WORKSPACE, "the batch needs %zu bytes of scratch; the library's static scratch holds %zu",
+                need, nvfp4::kStaticScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = nvfp4::static_scratch((hipStream_t)stream, &ws);
+    if (e != hipSuccess) return hip_status(e, "static scratch set-up");
+  }
+  return hip_status(nvfp4::launch_gemv_batch(pr, count, ws, (hipStream_t)stream), "gemv batch launch");
   NVFP4_GUARD_END
 }
 

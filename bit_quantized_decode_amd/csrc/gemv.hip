@@ -22,8 +22,18 @@
 // the tile's blocks, 1 for the k-half merge, 3 in the wavefront merge, one
 // per workgroup of the row tile (K/1024) and 1 for s_t: for K <= 32768 below
 // 70 * 2^-24 * sum|w x| = 4.2e-6 * sum|w x|.
+#include <mutex>
+
 #include "device_common.h"
 #include "launchers.h"
+
+// Scratch of nvfp4_gemv_batched_noalloc (callers that cannot allocate): the
+// split-K counters and partial sums of one batched GEMV call, in a device
+// array of the library itself.  Each device holds its own copy for the life of
+// the process.  Host code reaches it only through the address that
+// hipGetSymbolAddress returns on that device (static_scratch below); the
+// array's name is not a device address on the host.
+static __device__ __align__(256) uint8_t scratch[nvfp4::kStaticScratchBytes];
 
 namespace nvfp4 {
 namespace {
@@ -402,6 +412,33 @@ hipError_t launch_gemv_rows_batch(const Problem* p, int count, int64_t m, bool y
       hipLaunchKernelGGL(gemv_rows_kernel<2>, dim3((unsigned)wgs), dim3(256), 0, s, b, cnt, partial);
   }
   return hipGetLastError();
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+}  // namespace
+
+hipError_t static_scratch(hipStream_t s, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    // The counters must start at zero (every call leaves them so); the array
+    // is zero when the code object loads, and this fill, ordered before the
+    // first call's launch, makes that explicit.
+    e = launch_fill_zero(p, kCounterBytes, s);
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_gemv(const void* packed, const Geometry& g, float st, const uint16_t* x, float* y, void* ws,

@@ -64,6 +64,13 @@ constexpr int64_t kGemvRowsMax = 2;
 size_t gemv_rows_batch_workspace_bytes(const Problem* p, int count, int64_t m);
 hipError_t launch_gemv_rows_batch(const Problem* p, int count, int64_t m, bool y_bf16, void* ws, hipStream_t s);
 hipError_t launch_gemv_batch(const Problem* p, int count, void* ws, hipStream_t s);
+// The library's own scratch for the GEMV batch (nvfp4_gemv_batched_noalloc):
+// a device array of kStaticScratchBytes per device; static_scratch() returns
+// its address on the current device, setting it up on first use (its counter
+// area zeroed on stream s).  No allocation anywhere.
+constexpr size_t kStaticScratchBytes = kCounterBytes + ((size_t)8 << 20);
+constexpr int kNoallocMaxProblems = 64;
+hipError_t static_scratch(hipStream_t s, void** out);
 size_t skinny_batch_workspace_bytes(const Problem* p, int count);
 hipError_t launch_skinny_batch(const Problem* p, int count, int64_t m, bool y_bf16, void* ws, hipStream_t s);
 size_t prefill_batch_workspace_bytes(const Problem* p, int count, int64_t m);

@@ -20,7 +20,8 @@
  *
  * ---- Conventions for every call ---------------------------------------------
  *  - Pointers are DEVICE memory unless marked (host).  The caller owns all
- *    memory; the library never allocates, frees or synchronises.
+ *    memory; the library never allocates or frees it, and synchronises only
+ *    in nvfp4_moe_streamed (one read-back of the expert counts).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued on
  *    it and runs asynchronously; results are ready after the caller
  *    synchronises with the stream.
@@ -35,7 +36,9 @@
  *    HIP error text.  Faults during execution surface at the caller's next
  *    synchronisation.
  *  - No C++ exception crosses this boundary.  The library keeps no mutable
- *    global state apart from the thread-local error text.
+ *    global state apart from the thread-local error text and, once
+ *    nvfp4_gemv_batched_noalloc has run on a device, that device's address of
+ *    the library's static scratch array.
  *  - Workspaces: calls that split a reduction across workgroups take a caller
  *    workspace of at least the size the matching *_workspace_bytes() returns.
  *    For nvfp4_gemv / nvfp4_gemm its first 262144 bytes are counters that must
@@ -223,6 +226,19 @@ int nvfp4_gemv_batched_workspace_bytes(const nvfp4_problem* problems /* host */,
                                        size_t* bytes /* host */);
 int nvfp4_gemv_batched(const nvfp4_problem* problems /* host */, int count, void* workspace,
                        size_t workspace_bytes, void* stream);
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops that forbid allocation): nvfp4_gemv_batched without
+ * a workspace argument.  Its split-K counters and partial sums live in a
+ * static device array of the library, 8 MiB + 256 KiB on each GPU the library
+ * runs on, held until the process ends; the call allocates nothing.  A batch
+ * whose nvfp4_gemv_batched_workspace_bytes() exceeds that returns
+ * NVFP4_ERR_WORKSPACE; count must be <= 64 (NVFP4_ERR_ARG).  Results are
+ * bit-identical to nvfp4_gemv_batched.  Every call on a GPU shares that GPU's
+ * array: calls that may overlap on one GPU (other streams, other threads) race
+ * and must be serialised by the caller.  The first call on a device also
+ * enqueues, on `stream`, a fill of the array's counters with zeros; every call
+ * leaves them zero.  Other validation and statuses as nvfp4_gemv_batched. */
+int nvfp4_gemv_batched_noalloc(const nvfp4_problem* problems /* host */, int count, void* stream);
 /* All problems of a batch share m and y_dtype. */
 int nvfp4_gemm_batched_workspace_bytes(const nvfp4_problem* problems /* host */, int count, int64_t m,
                                        size_t* bytes /* host */);

@@ -28,7 +28,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 27, names
+    assert len(names) == 28, names
     assert set(names) == set(B.EXPORTED)
     for name in names:
         assert hasattr(L, name), name
@@ -197,6 +197,31 @@ def test_batched_validation(L):
     big[0].ldx, big[0].ldy = 17408, 5120
     assert L.nvfp4_gemm_batched_workspace_bytes(big, 1, 32, ctypes.byref(sz)) == B.NVFP4_OK and sz.value > 0
     assert L.nvfp4_gemm_batched(big, 1, 32, 1, None, 0, None) == B.NVFP4_ERR_WORKSPACE
+
+
+def test_gemv_noalloc_validation(L):
+    """The static-scratch GEMV batch refuses, before any HIP call, batches its
+    scratch cannot hold, more than 64 problems, and what nvfp4_gemv_batched refuses."""
+    A = 0x10000
+    arr = (B.Problem * 65)()
+    for i in range(65):
+        arr[i].packed, arr[i].n, arr[i].k, arr[i].tensor_scale = A, 64, 2048, 1.0
+        arr[i].x, arr[i].y = A, A + 0x1000 * (i + 1)
+    assert L.nvfp4_gemv_batched_noalloc(arr, 65, None) == B.NVFP4_ERR_ARG
+    assert L.nvfp4_gemv_batched_noalloc(arr, 0, None) == B.NVFP4_OK
+    arr[0].n = 1 << 20                                  # 2 k-groups x 2^20 rows x 4 B = 8 MiB of partials
+    arr[1].n = 64
+    assert L.nvfp4_gemv_batched_noalloc(arr, 2, None) == B.NVFP4_ERR_WORKSPACE
+    assert b"static scratch" in L.nvfp4_last_error()
+    arr[0].n = 64
+    arr[1].k = 40
+    assert L.nvfp4_gemv_batched_noalloc(arr, 2, None) == B.NVFP4_ERR_SHAPE
+    arr[1].k = 2048
+    arr[1].y = arr[0].y
+    assert L.nvfp4_gemv_batched_noalloc(arr, 2, None) == B.NVFP4_ERR_ARG     # shared output
+    arr[1].y = A + 0x9000
+    arr[1].x = A + 8
+    assert L.nvfp4_gemv_batched_noalloc(arr, 2, None) == B.NVFP4_ERR_ALIGN
 
 
 def test_w4a4_validation(L):
