@@ -5,6 +5,7 @@
 // this file.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -49,10 +50,16 @@ int check_shape(int64_t n, int64_t k) {
   return NVFP4_OK;
 }
 
-int check_rows(int64_t n) {
+// Products: n up to the split-K counters' row limit, and k up to the length
+// over which every kernel's fp32 accumulation provably stays within
+// 1e-5 * sum |w x| (refuse rather than run wrong).
+int check_product(int64_t n, int64_t k) {
   if (n > nvfp4::kMaxSplitRows)
     return fail(NVFP4_ERR_SHAPE, "n=%lld above the %lld rows a product call supports", (long long)n,
                 (long long)nvfp4::kMaxSplitRows);
+  if (k > nvfp4::kMaxProductK)
+    return fail(NVFP4_ERR_SHAPE, "k=%lld above the %lld a product call accepts (the accumulation bound's range)",
+                (long long)k, (long long)nvfp4::kMaxProductK);
   return NVFP4_OK;
 }
 
@@ -127,7 +134,7 @@ int nvfp4_gemv_workspace_bytes(int64_t n, int64_t k, size_t* bytes) {
   NVFP4_GUARD_BEGIN
   if (!bytes) return fail(NVFP4_ERR_NULL, "bytes is NULL");
   NVFP4_TRY(check_shape(n, k));
-  NVFP4_TRY(check_rows(n));
+  NVFP4_TRY(check_product(n, k));
   *bytes = nvfp4::gemv_workspace_bytes(nvfp4::geometry(n, k));
   return ok();
   NVFP4_GUARD_END
@@ -183,7 +190,7 @@ int nvfp4_w4a4_gemm(const void* mx_packed, int64_t n, int64_t k, float tensor_sc
                     void* stream) {
   NVFP4_GUARD_BEGIN
   NVFP4_TRY(check_mx_shape(n, k));
-  NVFP4_TRY(check_rows(n));
+  NVFP4_TRY(check_product(n, k));
   if (m < 0 || m > (int64_t(1) << 24)) return fail(NVFP4_ERR_SHAPE, "m=%lld out of range", (long long)m);
   if (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16) return fail(NVFP4_ERR_DTYPE, "unknown y_dtype %d", y_dtype);
   if (m == 0 || n == 0) return ok();
@@ -237,7 +244,7 @@ int nvfp4_gemv(const void* packed, int64_t n, int64_t k, float tensor_scale, con
                void* workspace, size_t workspace_bytes, void* stream) {
   NVFP4_GUARD_BEGIN
   NVFP4_TRY(check_shape(n, k));
-  NVFP4_TRY(check_rows(n));
+  NVFP4_TRY(check_product(n, k));
   if (n == 0) return ok();
   if (!y || (k > 0 && (!packed || !x))) return fail(NVFP4_ERR_NULL, "packed, x and y must be non-NULL");
   if (!aligned16(y) || (k > 0 && (!aligned16(packed) || !aligned16(x))))
@@ -255,7 +262,7 @@ int nvfp4_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, size_t* bytes) {
   NVFP4_GUARD_BEGIN
   if (!bytes) return fail(NVFP4_ERR_NULL, "bytes is NULL");
   NVFP4_TRY(check_shape(n, k));
-  NVFP4_TRY(check_rows(n));
+  NVFP4_TRY(check_product(n, k));
   if (m < 0 || m > kMaxDim) return fail(NVFP4_ERR_SHAPE, "m=%lld out of range", (long long)m);
   const nvfp4::Geometry g = nvfp4::geometry(n, k);
   if (m <= nvfp4::kGemvRowsMax) {
@@ -273,7 +280,7 @@ int nvfp4_gemm(const void* packed, int64_t n, int64_t k, float tensor_scale, con
                void* stream) {
   NVFP4_GUARD_BEGIN
   NVFP4_TRY(check_shape(n, k));
-  NVFP4_TRY(check_rows(n));
+  NVFP4_TRY(check_product(n, k));
   if (m < 0 || m > kMaxDim) return fail(NVFP4_ERR_SHAPE, "m=%lld out of range", (long long)m);
   if (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16) return fail(NVFP4_ERR_DTYPE, "unknown y_dtype %d", y_dtype);
   if (m == 0 || n == 0) return ok();
@@ -316,7 +323,7 @@ static int check_batch(const nvfp4_problem* pr, int count, int64_t gemm_m, int y
   for (int i = 0; i < count; ++i) {
     const nvfp4_problem& q = pr[i];
     NVFP4_TRY(check_shape(q.n, q.k));
-    NVFP4_TRY(check_rows(q.n));
+    NVFP4_TRY(check_product(q.n, q.k));
     if (i % nvfp4::kMaxBatch == 0) tiles = 0;
     tiles += (q.n + 63) / 64;
     if (tiles > nvfp4::kCounterSlots)
@@ -344,8 +351,10 @@ static int check_moe(const nvfp4_moe_args* a, bool need_buffers) {
     return fail(NVFP4_ERR_SHAPE, "tokens must be >= 0; experts, hidden and inter > 0");
   if (a->hidden % 16 != 0 || a->inter % 16 != 0)
     return fail(NVFP4_ERR_SHAPE, "hidden=%lld and inter=%lld must be multiples of 16", (long long)a->hidden, (long long)a->inter);
-  if (a->tokens > kMaxDim || a->hidden > kMaxDim || a->inter > kMaxDim)
-    return fail(NVFP4_ERR_SHAPE, "size above 2^30");
+  if (a->tokens > kMaxDim) return fail(NVFP4_ERR_SHAPE, "tokens above 2^30");
+  if (a->hidden > nvfp4::kMaxProductK || a->inter > nvfp4::kMaxProductK)
+    return fail(NVFP4_ERR_SHAPE, "hidden=%lld and inter=%lld must be at most %lld (the accumulation bound's range)",
+                (long long)a->hidden, (long long)a->inter, (long long)nvfp4::kMaxProductK);
   if (a->experts > nvfp4::moe_max_experts())
     return fail(NVFP4_ERR_ARG, "experts=%lld above the supported %lld", (long long)a->experts, (long long)nvfp4::moe_max_experts());
   if (a->top_k < 1 || a->top_k > a->experts || a->top_k > 64)
@@ -593,12 +602,18 @@ int nvfp4_moe_streamed(const nvfp4_moe_args* a, nvfp4_expert_cache* c, void* str
   NVFP4_TRY(hip_status(hipMemcpyAsync(c->host_counts, a->expert_counts, (size_t)a->experts * 4, hipMemcpyDeviceToHost, s),
                        "expert counts read-back"));
   NVFP4_TRY(hip_status(hipStreamSynchronize(s), "expert counts read-back"));
-  const uint64_t now = ++c->clock;
+  // The cache's new state is planned on copies and committed only once every
+  // launch of the call has been enqueued: a failure leaves no expert marked
+  // resident whose bytes never arrived.
+  const uint64_t now = c->clock + 1;
+  std::vector<int32_t> slot_of(c->slot_of, c->slot_of + a->experts);
+  std::vector<int32_t> expert_in(c->expert_in, c->expert_in + c->slots);
+  std::vector<uint64_t> last_use(c->last_use, c->last_use + c->slots);
   int64_t active = 0;
   for (int64_t e = 0; e < a->experts; ++e)
     if (c->host_counts[e] > 0) {
       ++active;
-      if (c->slot_of[e] >= 0) c->last_use[c->slot_of[e]] = now;  // a hit: keep it this call
+      if (slot_of[e] >= 0) last_use[slot_of[e]] = now;  // a hit: keep it this call
     }
   c->last_active = active;
   c->last_fetched = 0;
@@ -620,26 +635,30 @@ int nvfp4_moe_streamed(const nvfp4_moe_args* a, nvfp4_expert_cache* c, void* str
   std::vector<const void*> csrc;
   std::vector<void*> cdst;
   std::vector<size_t> cbytes;
+  std::vector<int64_t> victims;
   uint8_t* dg = static_cast<uint8_t*>(c->dev_gate);
   uint8_t* du = static_cast<uint8_t*>(c->dev_up);
   uint8_t* dd = static_cast<uint8_t*>(c->dev_down);
+  int64_t fetched = 0;
+  size_t fetched_bytes = 0;
   for (int64_t e = 0; e < a->experts; ++e) {
-    if (c->host_counts[e] <= 0 || c->slot_of[e] >= 0) continue;
+    if (c->host_counts[e] <= 0 || slot_of[e] >= 0) continue;
     // A miss: a free slot, else the least recently used slot not routed to in this call.
     int64_t v = -1;
     for (int64_t q = 0; q < c->slots; ++q)
-      if (c->expert_in[q] < 0) {
+      if (expert_in[q] < 0) {
         v = q;
         break;
       }
     if (v < 0)
       for (int64_t q = 0; q < c->slots; ++q)
-        if (c->last_use[q] < now && (v < 0 || c->last_use[q] < c->last_use[v])) v = q;
+        if (last_use[q] < now && (v < 0 || last_use[q] < last_use[v])) v = q;
     if (v < 0) return fail(NVFP4_ERR_ARG, "no free cache slot");  // cannot happen when active <= slots
-    if (c->expert_in[v] >= 0) c->slot_of[c->expert_in[v]] = -1;
-    c->expert_in[v] = (int32_t)e;
-    c->slot_of[e] = (int32_t)v;
-    c->last_use[v] = now;
+    if (expert_in[v] >= 0) slot_of[expert_in[v]] = -1;
+    expert_in[v] = (int32_t)e;
+    slot_of[e] = (int32_t)v;
+    last_use[v] = now;
+    victims.push_back(v);
     csrc.push_back(hg + e * c->stride_gate);
     cdst.push_back(dg + v * c->stride_gate);
     cbytes.push_back(gu);
@@ -649,16 +668,40 @@ int nvfp4_moe_streamed(const nvfp4_moe_args* a, nvfp4_expert_cache* c, void* str
     csrc.push_back(hd + e * c->stride_down);
     cdst.push_back(dd + v * c->stride_down);
     cbytes.push_back(dn);
-    ++c->last_fetched;
-    c->last_bytes += 2 * gu + dn;
+    ++fetched;
+    fetched_bytes += 2 * gu + dn;
   }
-  if (!csrc.empty())
-    NVFP4_TRY(hip_status(nvfp4::launch_expert_copies(csrc.data(), cdst.data(), cbytes.data(), (int)csrc.size(), s),
-                         "expert copy launch"));
+  // After a failure once copies may have been enqueued, the slots they write
+  // hold nothing usable: they are emptied in the cache.
+  auto drop_victims = [&]() {
+    for (int64_t v : victims) {
+      if (c->expert_in[v] >= 0) c->slot_of[c->expert_in[v]] = -1;
+      c->expert_in[v] = -1;
+      c->last_use[v] = 0;
+    }
+  };
+  if (!csrc.empty()) {
+    const hipError_t e = nvfp4::launch_expert_copies(csrc.data(), cdst.data(), cbytes.data(), (int)csrc.size(), s);
+    if (e != hipSuccess) {
+      drop_victims();
+      return hip_status(e, "expert copy launch");
+    }
+  }
   // The slot table (entries of experts not routed to are never read).
-  for (int64_t e = 0; e < a->experts; ++e) c->host_slot_stage[e] = c->slot_of[e] < 0 ? 0 : c->slot_of[e];
-  NVFP4_TRY(hip_status(hipMemcpyAsync(c->dev_slot_of, c->host_slot_stage, (size_t)a->experts * 4, hipMemcpyHostToDevice, s),
-                       "slot table copy"));
+  for (int64_t e = 0; e < a->experts; ++e) c->host_slot_stage[e] = slot_of[e] < 0 ? 0 : slot_of[e];
+  const hipError_t ec =
+      hipMemcpyAsync(c->dev_slot_of, c->host_slot_stage, (size_t)a->experts * 4, hipMemcpyHostToDevice, s);
+  if (ec != hipSuccess) {
+    drop_victims();
+    return hip_status(ec, "slot table copy");
+  }
+  // Every copy is enqueued: commit the cache's new state.
+  c->clock = now;
+  std::copy(slot_of.begin(), slot_of.end(), c->slot_of);
+  std::copy(expert_in.begin(), expert_in.end(), c->expert_in);
+  std::copy(last_use.begin(), last_use.end(), c->last_use);
+  c->last_fetched = fetched;
+  c->last_bytes = fetched_bytes;
   l.slot_table = c->dev_slot_of;
   return hip_status(nvfp4::launch_moe_experts(l, s), "moe expert launch");
   NVFP4_GUARD_END

@@ -17,11 +17,13 @@
 //  - the two k halves meet with one lane-half exchange, the four wavefronts
 //    in LDS, and the workgroups of one row tile through the workspace, summed
 //    in a fixed order by whichever arrives last (no floating-point atomics).
-// Rounding: a result passes at most 8 roundings in a half-block partial (4
-// dot2, each measured below 2.5 roundings' worth), 1 for the scale, 16 over
-// the tile's blocks, 1 for the k-half merge, 3 in the wavefront merge, one
-// per workgroup of the row tile (K/1024) and 1 for s_t: for K <= 32768 below
-// 70 * 2^-24 * sum|w x| = 4.2e-6 * sum|w x|.
+// Error (first order, u = 2^-24, S = sum|w x|): a half-block partial is a
+// chain of 4 dot2, each measured to err by at most 3 u of its inputs'
+// magnitudes (12 u S); the scale enters by one fma per half-block, 16 of
+// them per lane and tile (16 u S); then the k-half merge (1), the wavefront
+// merge (3), one add per workgroup of the row tile (K / 1024) and s_t (1):
+// at most (33 + K / 1024) u S, i.e. 65 u S = 3.9e-6 S for K <= 32768, the
+// longest k the products accept.
 #include <mutex>
 
 #include "device_common.h"

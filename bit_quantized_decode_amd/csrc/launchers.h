@@ -32,6 +32,9 @@ inline size_t packed_bytes(const Geometry& g) { return (size_t)g.nrt * (size_t)g
 constexpr int64_t kCounterSlots = 65536;
 constexpr size_t kCounterBytes = (size_t)kCounterSlots * 4;
 constexpr int64_t kMaxSplitRows = kCounterSlots * 64;
+// The longest k (and MoE hidden / inter) the products accept: the range over
+// which the kernels' fp32 accumulation error is proven below 1e-5 sum|w x|.
+constexpr int64_t kMaxProductK = 32768;
 
 // Split-K plan shared by the GEMV and the skinny GEMM: `groups` workgroups per
 // row tile, 4 wavefronts each, so the K tiles are cut into 4*groups parts.

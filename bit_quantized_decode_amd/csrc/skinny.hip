@@ -183,12 +183,15 @@ __global__ void zero_rows_kernel(void* __restrict__ y, int64_t m, int64_t n, int
 
 // K parts per problem for a batch: aim at about 2048 wavefronts over the whole
 // batch (two per SIMD), i.e. `tpw` k tiles per wavefront, with at most 12 parts
-// per row group (bounding the last workgroup's reduction) and none empty.
+// per row group (bounding the last workgroup's reduction) and none empty --
+// but at least one part per 64 k tiles, so that no wavefront's running sum
+// chains more than 64 tile sums (the accumulation bound).
 int skinny_groups(const Geometry& g, int64_t batch_units) {
   int64_t tpw = (batch_units + 2047) / 2048;
   if (tpw < 2) tpw = 2;
   int64_t groups = (g.nkt + tpw - 1) / tpw;
   if (groups > 12) groups = 12;
+  if (groups < (g.nkt + 63) / 64) groups = (g.nkt + 63) / 64;
   if (groups > g.nkt) groups = g.nkt;
   if (groups < 1) groups = 1;
   return (int)groups;

@@ -98,6 +98,21 @@ def test_shape_and_pointer_validation(L):
     assert L.nvfp4_gemv(A, big, 1280, 1.0, A, A, A, 1 << 40, None) == B.NVFP4_ERR_SHAPE
     assert L.nvfp4_gemm(A, big, 1280, 1.0, A, 32, 1280, A, big, 1, A, 1 << 40, None) == B.NVFP4_ERR_SHAPE
     assert L.nvfp4_gemm(A, big, 256, 1.0, A, 64, 256, A, big, 1, A, 1 << 40, None) == B.NVFP4_ERR_SHAPE
+    # k up to 32768, where the accumulation bound is proven; one block past it is refused.
+    sz = ctypes.c_size_t()
+    assert L.nvfp4_gemv_workspace_bytes(64, 32768, ctypes.byref(sz)) == B.NVFP4_OK
+    assert L.nvfp4_gemv_workspace_bytes(64, 32784, ctypes.byref(sz)) == B.NVFP4_ERR_SHAPE
+    assert L.nvfp4_gemv(A, 64, 32784, 1.0, A, A, A, 1 << 40, None) == B.NVFP4_ERR_SHAPE
+    for m in (2, 32, 64):
+        assert L.nvfp4_gemm_workspace_bytes(m, 64, 32768, ctypes.byref(sz)) == B.NVFP4_OK
+        assert L.nvfp4_gemm(A, 64, 32784, 1.0, A, m, 32784, A, 64, 1, A, 1 << 40, None) == B.NVFP4_ERR_SHAPE
+    assert L.nvfp4_w4a4_gemm(A, 64, 32800, 1.0, A, 64, 32800, A, 64, 1, A, 1 << 40, None) == B.NVFP4_ERR_SHAPE
+    arr = (B.Problem * 1)()
+    arr[0].packed, arr[0].n, arr[0].k, arr[0].x, arr[0].y, arr[0].ldx, arr[0].ldy = A, 64, 32784, A, A, 32784, 64
+    assert L.nvfp4_gemv_batched(arr, 1, A, 1 << 40, None) == B.NVFP4_ERR_SHAPE
+    assert L.nvfp4_gemm_batched(arr, 1, 32, 1, A, 1 << 40, None) == B.NVFP4_ERR_SHAPE
+    # packing and quantising are not products: no such limit
+    assert L.nvfp4_packed_bytes(64, 65536, ctypes.byref(sz)) == B.NVFP4_OK
 
 
 def test_quantize_validation(L):
@@ -139,6 +154,8 @@ def moe_template(**over):
     (dict(top_k=65, experts=2048), B.NVFP4_ERR_ARG),
     (dict(hidden=2040), B.NVFP4_ERR_SHAPE),
     (dict(inter=-16), B.NVFP4_ERR_SHAPE),
+    (dict(hidden=32784), B.NVFP4_ERR_SHAPE),     # past the products' k limit (gate / up)
+    (dict(inter=32784), B.NVFP4_ERR_SHAPE),      # (down)
     (dict(tokens=-1), B.NVFP4_ERR_SHAPE),
     (dict(stride_down=589_808), B.NVFP4_ERR_ARG),
     (dict(stride_gate=589_832), B.NVFP4_ERR_ALIGN),
@@ -289,3 +306,32 @@ def test_expert_cache_validation(L):
     c.dev_gate = c.dev_up = c.dev_down = 0x20000
     c.stride_gate = c.stride_up = c.stride_down = 589_824
     assert L.nvfp4_moe_streamed(ctypes.byref(a), ctypes.byref(c), None) == B.NVFP4_ERR_ARG
+
+
+def test_failed_streamed_call_leaves_the_cache_unchanged(L):
+    """A streamed call whose first launch fails (here: no GPU) returns
+    NVFP4_ERR_HIP and leaves the cache exactly as it was: the cache's new
+    state is committed only after every copy of the call is enqueued.  Runs
+    only where no GPU is visible (it would otherwise launch on fake pointers)."""
+    import numpy as np
+    import torch
+    if torch.cuda.device_count() != 0:
+        pytest.skip("a GPU is visible: this call would launch kernels on placeholder pointers")
+    c = B.ExpertCache()
+    c.experts, c.slots = 512, 4
+    slot_of = np.full(512, -1, np.int32)
+    expert_in = np.array([7, -1, 300, 2], np.int32)
+    last_use = np.array([5, 0, 9, 3], np.uint64)
+    slot_of[[7, 300, 2]] = [0, 2, 3]
+    c.slot_of, c.expert_in, c.last_use = slot_of.ctypes.data, expert_in.ctypes.data, last_use.ctypes.data
+    c.clock = 9
+    c.dev_gate = c.dev_up = c.dev_down = 0x20000
+    c.stride_gate = c.stride_up = c.stride_down = 589_824
+    c.host_gate = c.host_up = c.host_down = 0x40000
+    c.dev_slot_of, c.host_counts, c.host_slot_stage = 0x50000, 0x60000, 0x70000
+    a = moe_template(w_gate=0x20000, w_up=0x20000, w_down=0x20000, stride_gate=589_824, stride_up=589_824,
+                     stride_down=589_824)
+    before = (slot_of.copy(), expert_in.copy(), last_use.copy())
+    assert L.nvfp4_moe_streamed(ctypes.byref(a), ctypes.byref(c), None) == B.NVFP4_ERR_HIP
+    assert np.array_equal(slot_of, before[0]) and np.array_equal(expert_in, before[1])
+    assert np.array_equal(last_use, before[2]) and c.clock == 9
