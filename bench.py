@@ -9,16 +9,23 @@ synthetic workload:
   moe         32 tokens through a 512-expert, top-10 MoE layer (hidden 2048, expert
               width 512): route, group, gate/up + SwiGLU, down, scatter
   prefill     a 512-token prompt through gate, up (5120->17408) and down (17408->5120)
+  gemv_1k     one 1024 x 1024 GEMV at batch 1 (latency-bound: reported in us and GB/s)
 The headline `value` is the batch-1 layer's weight-stream rate in GB/s
 (algorithmic bytes: NVFP4 weights + x + y).  Weights are rotated over several
 device copies so that no copy is re-read before > 1 GiB of other traffic:
-the 256 MB Infinity Cache cannot serve repeats.
+the 256 MB Infinity Cache cannot serve repeats.  After the timed steps the
+ceiling probes (libnvfp4_probes.so) measure what this machine sustains for a
+streaming read in the weights' tile unit and for the bf16 and FP4 matrix
+instructions with random operands; every row's fraction of nominal peak is
+reported next to its fraction of that measured ceiling.
 
 Prints ONE JSON line on stdout; details go to stderr.
 """
 import argparse
+import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -88,12 +95,13 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target length of the oracle sample")
-    p.add_argument("--rows", default="decode_b1,decode_b32,moe,prefill",
+    p.add_argument("--no-probes", action="store_true", help="skip the ceiling probes after the timed steps")
+    p.add_argument("--rows", default="decode_b1,decode_b32,moe,prefill,gemv_1k",
                    help="rows to run; optional, not default: quantize (the NVFP4 quantiser over the layer), "
                         "decode_m2 .. decode_m8 (the layer at decode widths 2..8), head_b1 (the output head, batch 1), "
                         "moe_stream (the MoE layer with experts streamed from host memory), prefill_w4a4 (the prefill "
                         "products as W4A4 on the FP4 matrix cores)")
-    p.add_argument("--order", default="prefill,moe,decode_b32,decode_b1",
+    p.add_argument("--order", default="prefill,moe,decode_b32,gemv_1k,decode_b1",
                    help="row order within a step (the batch-1 GEMV last: see the note at the plan)")
     p.add_argument("--graphs", action="store_true", help="replay per-row HIP graphs instead of direct launches")
     return p.parse_args()
@@ -126,8 +134,11 @@ def main():
     layer = I.DENSE_LAYER
     dense_copies = 4
     packed = [[None] * len(layer) for _ in range(dense_copies)]
+    b1_inputs = hashlib.sha256()   # the batch-1 layer's codes, scales and x, as the oracle baseline also hashes them
     for j, mat in enumerate(layer):
         c, s = I.nvfp4_matrix(I.DECODE_B1, mat.matrix_id, mat.n, mat.k)
+        for a_ in (c, s, I.activations(I.DECODE_B1, mat.matrix_id, 1, mat.k)):
+            b1_inputs.update(np.ascontiguousarray(a_).tobytes())
         p0 = B.pack(u8(c), u8(s))
         for cp in range(dense_copies):
             packed[cp][j] = p0 if cp == 0 else p0.clone()
@@ -166,13 +177,29 @@ def main():
                                                    shape.inter), dev, kind="moe")
         del w
 
-    moe_calls = []
+    # The row routes a different batch of 32 tokens each step: 16 seeded
+    # routings (other tokens and router noise, the same Zipf expert
+    # popularity) over the two weight pools, 32 prepared calls in turn.
+    moe_routings = 16
+    moe_calls, moe_call_bytes, moe_call_active = [], [], []
     if "moe" in rows:
-        for cp in range(2):
-            pg_, pu_, pd_ = moe_pools[cp]
-            moe_calls.append(B.moe_grouped_prepared(moe_x, moe_logits, shape.top_k, pg_, pu_, pd_, stride_gu,
-                                                    stride_gu, stride_d, sts[0], sts[1], sts[2], shape.inter,
-                                                    y_dtype=torch.float32, ws=moe_ws, outputs=moe_out)[0])
+        per_expert = 3 * B.packed_bytes(shape.inter, shape.hidden)
+        fixed = (2 * shape.tokens * shape.hidden + 4 * shape.tokens * shape.experts + 4 * shape.tokens * shape.hidden
+                 + 8 * shape.tokens * shape.top_k)
+        for r in range(moe_routings):
+            xr = moe_x if r == 0 else bf16(I.activations(I.MOE_32T, r, shape.tokens, shape.hidden))
+            lr = moe_logits if r == 0 else torch.from_numpy(
+                I.router_logits(I.MOE_32T, shape.tokens, shape.experts, shape.zipf_s, batch=r)).to(dev)
+            for cp in range(2):
+                pg_, pu_, pd_ = moe_pools[cp]
+                call, o_ = B.moe_grouped_prepared(xr, lr, shape.top_k, pg_, pu_, pd_, stride_gu, stride_gu, stride_d,
+                                                  sts[0], sts[1], sts[2], shape.inter, y_dtype=torch.float32,
+                                                  ws=moe_ws, outputs=moe_out)
+                moe_calls.append(call)
+            torch.cuda.synchronize()
+            active = int((moe_out["expert_counts"].cpu() > 0).sum())
+            moe_call_active += [active, active]
+            moe_call_bytes += [active * per_expert + fixed] * 2
 
     def run_moe(cp):
         moe_calls[cp]()
@@ -260,6 +287,21 @@ def main():
         extra_rows["head_b1"] = ([B.gemv_batched_prepared([(head_packed, I.HEAD.n, I.HEAD.k, I.TENSOR_SCALE, xh, yh)],
                                                           ws=ws_split)], 1, [yh], hbytes, 2.0 * I.HEAD.n * I.HEAD.k)
 
+    # ---- the single 1024 x 1024 GEMV (batch 1), one launch per step; 1800
+    # copies of its 589,824 packed bytes (1.06 GB) so that no copy is read
+    # twice within 1800 steps ----------------------------------------------
+    g1k_copies, g1k_calls = 1800, []
+    g1k_bytes = B.packed_bytes(1024, 1024) + 2 * 1024 + 4 * 1024
+    if "gemv_1k" in rows:
+        c, s_ = I.nvfp4_matrix(I.GEMV_1K, 0, 1024, 1024)
+        g1k_p0 = B.pack(u8(c), u8(s_))
+        g1k_x = bf16(I.activations(I.GEMV_1K, 0, 1, 1024)[0])
+        g1k_y = torch.empty(1024, dtype=torch.float32, device=dev)
+        g1k_ws = B.workspace(B.gemv_workspace_bytes(1024, 1024), dev)
+        for cp in range(g1k_copies):
+            pcp = g1k_p0 if cp == 0 else g1k_p0.clone()
+            g1k_calls.append(B.gemv_batched_prepared([(pcp, 1024, 1024, I.TENSOR_SCALE, g1k_x, g1k_y)], ws=g1k_ws))
+
     def pre_items(cp):
         return [(pre_packed[cp][j], mat.n, mat.k, I.TENSOR_SCALE, pre_x[j], pre_y[j]) for j, mat in enumerate(pre)]
 
@@ -318,7 +360,9 @@ def main():
     # that a decode loop does not have.
     plan_all = {
         "prefill": ("prefill", row_pre, pre_copies, lambda i: i % pre_copies, pre_y),
-        "moe": ("moe", run_moe, 2, lambda i: i % 2, None),
+        "moe": ("moe", run_moe, 2 * moe_routings, lambda i: i % (2 * moe_routings), None),
+        "gemv_1k": ("gemv_1k", lambda cp: g1k_calls[cp](), g1k_copies, lambda i: i % g1k_copies,
+                    [g1k_y] if g1k_calls else None),
         "decode_b32": ("decode_b32", row_b32, dense_copies, lambda i: (2 * i + 1) % dense_copies, y32),
         "decode_b1": ("decode_b1", row_b1, dense_copies, lambda i: (2 * i) % dense_copies, y1),
         "quantize": ("quantize", row_q, 1, lambda i: 0, [c for c, _, _ in q_out]),
@@ -399,10 +443,14 @@ def main():
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
     ms_per_step = total_ms / args.steps
-    seg = {}
+    seg, seg_med = {}, {}
     for name in all_marks[0]:
-        seg[name] = sum(hev.elapsed_ms(m[name][0], m[name][1]) for m in all_marks) / args.steps
+        per = [hev.elapsed_ms(m[name][0], m[name][1]) for m in all_marks]
+        seg[name] = sum(per) / args.steps
+        seg_med[name] = statistics.median(per)
     hev.close()
+    picks = {name: [pick(args.warmup + i) for i in range(args.steps)] for name, _, _, pick, _ in plan}
+    ceil = {} if args.no_probes else probe_ceilings(dev, layer_weight_bytes=b1_weight_bytes)
     gemv_launches = args.steps if "decode_b1" in seg else 0   # one batched launch per step
     gemv_ms = seg.get("decode_b1", 0.0) * args.steps
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step; segments (ms): "
@@ -410,37 +458,57 @@ def main():
 
     # ---- per-row results --------------------------------------------------
     result_rows = {}
+    read_ceiling = ceil.get("hbm_read_GB/s")
+
+    def hbm_row(gbs):
+        d = {"frac_hbm": gbs / HBM_PEAK_GBS}
+        if read_ceiling:
+            d["frac_probe_read"] = gbs / read_ceiling
+        return d
+
     if "decode_b1" in seg:
         s = seg["decode_b1"] * 1e-3
         result_rows["decode_b1"] = {"GB/s": b1_bytes / s / 1e9, "weight_GB/s": b1_weight_bytes / s / 1e9,
-                                    "us": s * 1e6, "frac_hbm": b1_bytes / s / 1e9 / HBM_PEAK_GBS,
-                                    "equiv_tok_s": b1_bytes / s / MODEL_27B_BYTES_PER_TOKEN}
+                                    "us": s * 1e6, "us_median": seg_med["decode_b1"] * 1e3,
+                                    **hbm_row(b1_bytes / s / 1e9),
+                                    "equiv_tok_s": b1_bytes / s / MODEL_27B_BYTES_PER_TOKEN,
+                                    "inputs_sha256": b1_inputs.hexdigest()}
     if "decode_b32" in seg:
         s = seg["decode_b32"] * 1e-3
         result_rows["decode_b32"] = {"GB/s": b32_bytes / s / 1e9, "TFLOP/s": b32_flops / s / 1e12, "us": s * 1e6,
-                                     "frac_hbm": b32_bytes / s / 1e9 / HBM_PEAK_GBS,
+                                     "us_median": seg_med["decode_b32"] * 1e3, **hbm_row(b32_bytes / s / 1e9),
                                      "equiv_tok_s": 32 * b32_bytes / s / MODEL_27B_BYTES_PER_TOKEN}
+    if "gemv_1k" in seg:
+        s = seg["gemv_1k"] * 1e-3
+        result_rows["gemv_1k"] = {"us": s * 1e6, "us_median": seg_med["gemv_1k"] * 1e3, "GB/s": g1k_bytes / s / 1e9,
+                                  "algorithmic_bytes": g1k_bytes, **hbm_row(g1k_bytes / s / 1e9),
+                                  "note": "latency-bound: 0.6 MB per launch; the 75 % bar applies to the layer"}
     if "moe" in seg:
         s = seg["moe"] * 1e-3
+        moe_bytes = sum(moe_call_bytes[cp] for cp in picks["moe"]) / args.steps
+        active = sum(moe_call_active[cp] for cp in picks["moe"]) / args.steps
         counts = moe_out["expert_counts"].cpu().numpy()
-        active = int((counts > 0).sum())
-        per_expert = 3 * B.packed_bytes(shape.inter, shape.hidden)
-        moe_bytes = (active * per_expert + 2 * shape.tokens * shape.hidden + 4 * shape.tokens * shape.experts
-                     + 4 * shape.tokens * shape.hidden + 8 * shape.tokens * shape.top_k)
-        result_rows["moe"] = {"GB/s": moe_bytes / s / 1e9, "us": s * 1e6, "active_experts": active,
-                              "algorithmic_bytes": moe_bytes, "frac_hbm": moe_bytes / s / 1e9 / HBM_PEAK_GBS,
-                              "layer_tok_s": shape.tokens / s, "max_tokens_per_expert": int(counts.max())}
+        result_rows["moe"] = {"GB/s": moe_bytes / s / 1e9, "us": s * 1e6, "us_median": seg_med["moe"] * 1e3,
+                              "routings": moe_routings, "active_experts_mean": active,
+                              "algorithmic_bytes_mean": moe_bytes, **hbm_row(moe_bytes / s / 1e9),
+                              "layer_tok_s": shape.tokens / s, "max_tokens_per_expert_last": int(counts.max())}
+    bf16_ceiling = ceil.get("mfma_bf16_TFLOP/s")
     if "prefill" in seg:
         s = seg["prefill"] * 1e-3
-        result_rows["prefill"] = {"TFLOP/s": pre_flops / s / 1e12, "us": s * 1e6,
-                                  "frac_mfma_bf16": pre_flops / s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        tf = pre_flops / s / 1e12
+        result_rows["prefill"] = {"TFLOP/s": tf, "us": s * 1e6, "us_median": seg_med["prefill"] * 1e3,
+                                  "frac_mfma_bf16": tf / MFMA_BF16_PEAK_TFLOPS,
+                                  **({"frac_probe_mfma_bf16": tf / bf16_ceiling} if bf16_ceiling else {}),
                                   "GB/s": pre_bytes / s / 1e9, "equiv_tok_s": pre_flops / s / (2 * 27e9)}
 
     if "prefill_w4a4" in seg:
         s = seg["prefill_w4a4"] * 1e-3
-        result_rows["prefill_w4a4"] = {"TFLOP/s": pre_flops / s / 1e12, "us": s * 1e6,
-                                       "frac_mfma_fp4": pre_flops / s / 1e12 / 10100.0,
-                                       "frac_mfma_bf16": pre_flops / s / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+        tf = pre_flops / s / 1e12
+        fp4_ceiling = ceil.get("mfma_fp4_TFLOP/s")
+        result_rows["prefill_w4a4"] = {"TFLOP/s": tf, "us": s * 1e6, "us_median": seg_med["prefill_w4a4"] * 1e3,
+                                       "frac_mfma_fp4": tf / 10100.0,
+                                       **({"frac_probe_mfma_fp4": tf / fp4_ceiling} if fp4_ceiling else {}),
+                                       "frac_mfma_bf16": tf / MFMA_BF16_PEAK_TFLOPS}
     if "moe_stream" in seg:
         s = seg["moe_stream"] * 1e-3
         st_timed = stream_state["stats"][-args.steps:]
@@ -454,11 +522,11 @@ def main():
     for r, (_, _, _, nbytes, flops) in extra_rows.items():
         s = seg[r] * 1e-3
         result_rows[r] = {"GB/s": nbytes / s / 1e9, "TFLOP/s": flops / s / 1e12, "us": s * 1e6,
-                          "algorithmic_bytes": nbytes, "frac_hbm": nbytes / s / 1e9 / HBM_PEAK_GBS}
+                          "us_median": seg_med[r] * 1e3, "algorithmic_bytes": nbytes, **hbm_row(nbytes / s / 1e9)}
     if "quantize" in seg:
         s = seg["quantize"] * 1e-3
-        result_rows["quantize"] = {"GB/s": q_bytes / s / 1e9, "us": s * 1e6, "algorithmic_bytes": q_bytes,
-                                   "frac_hbm": q_bytes / s / 1e9 / HBM_PEAK_GBS,
+        result_rows["quantize"] = {"GB/s": q_bytes / s / 1e9, "us": s * 1e6, "us_median": seg_med["quantize"] * 1e3,
+                                   "algorithmic_bytes": q_bytes, **hbm_row(q_bytes / s / 1e9),
                                    "weights_per_s": sum(m.n * m.k for m in layer) / s}
 
     roofline = None
@@ -469,7 +537,11 @@ def main():
         roofline = {"kernel": "gemv_kernel", "bound": "hbm", "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": gemv_traffic(), "avg_launch_us": round(avg_launch_s * 1e6, 3),
+                    "median_launch_us": round(seg_med["decode_b1"] * 1e3, 3),
                     "bytes_per_launch": int(bytes_per_launch)}
+        if read_ceiling:
+            roofline["probe_ceiling"] = round(read_ceiling, 1)
+            roofline["frac_probe"] = round(achieved / read_ceiling, 4)
 
     cpu = None
     if not args.no_cpu_baseline and "decode_b1" in rows:
@@ -491,6 +563,7 @@ def main():
         "rows": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                  for k, v in result_rows.items()},
         "roofline": roofline,
+        "ceilings": {k: round(v, 2) for k, v in ceil.items()},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -517,9 +590,76 @@ def gemv_traffic():
     return int(float(fields["traffic_bytes_per_launch"]))
 
 
+def probe_ceilings(dev, layer_weight_bytes):
+    """What this machine sustains, measured by libnvfp4_probes.so after the timed
+    steps (median of timed launches, HIP events on the launch stream):
+    a streaming read of the layer's packed-weight bytes in 9216-byte tiles
+    (four rotating copies, so no copy is re-read from the 256 MB MALL), and the
+    bf16 and FP4 matrix instructions with random operands."""
+    import ctypes
+
+    import torch
+    path = os.path.join(ROOT, "bit_quantized_decode_amd", "libnvfp4_probes.so")
+    if not os.path.exists(path):
+        log("ceiling probes skipped: libnvfp4_probes.so is not built")
+        return {}
+    L = ctypes.CDLL(path)
+    P, i64, u32, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint, ctypes.c_int
+    L.probe_hbm_read.argtypes = [P, i64, u32, P, P]
+    L.probe_mfma_bf16.argtypes = [P, I32, I32, u32, P, P]
+    L.probe_mfma_fp4.argtypes = [P, I32, I32, u32, P, P]
+    magic = 0x9E3779B9
+    stream = torch.cuda.current_stream().cuda_stream
+    hev = HipTimingEvents()
+
+    def timed(fn, reps):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        marks = []
+        for i in range(reps):
+            a, b = hev.new(), hev.new()
+            hev.record(a, stream)
+            fn(i)
+            hev.record(b, stream)
+            marks.append((a, b))
+        torch.cuda.synchronize()
+        return statistics.median(hev.elapsed_ms(a, b) for a, b in marks) * 1e-3
+
+    nbytes = layer_weight_bytes
+    bufs = [torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=dev) for _ in range(4)]
+    sink = torch.zeros(256 * 4096, dtype=torch.int32, device=dev)
+
+    def read(i):
+        if L.probe_hbm_read(bufs[i % 4].data_ptr(), nbytes, magic, sink.data_ptr(), stream) != 0:
+            raise RuntimeError("probe_hbm_read refused its arguments or failed to launch")
+    t_read = timed(read, 20)
+    del bufs
+    # Launch shapes that gave each instruction its best sustained rate on
+    # this box (a sweep of 256..2048 workgroups): bf16 2048 x 128
+    # iterations, FP4 256 x 1024; operands N(0,1) bf16 / random FP4 codes.
+    rnd_bf16 = torch.randn(256 * 6 * 1024 // 2, device=dev).to(torch.bfloat16)
+    rnd_fp4 = torch.randint(0, 256, (256 * 6 * 1024,), dtype=torch.uint8, device=dev)
+
+    def mfma(fn, buf, wgs, iters):
+        def run(i):
+            if fn(buf.data_ptr(), wgs, iters, magic, sink.data_ptr(), stream) != 0:
+                raise RuntimeError("matrix-core probe refused its arguments or failed to launch")
+        return run
+    t_bf16 = timed(mfma(L.probe_mfma_bf16, rnd_bf16, 2048, 128), 10)
+    t_fp4 = timed(mfma(L.probe_mfma_fp4, rnd_fp4, 256, 1024), 10)
+    hev.close()
+    flops = 2048 * 4 * 16 * 128 * 32768          # the same for both launches, in units of a bf16 instruction
+    out = {"hbm_read_GB/s": nbytes / t_read / 1e9, "hbm_read_us": t_read * 1e6,
+           "mfma_bf16_TFLOP/s": flops / t_bf16 / 1e12, "mfma_fp4_TFLOP/s": 4 * flops / t_fp4 / 1e12}
+    log("ceilings: " + ", ".join(f"{k}={v:.1f}" for k, v in out.items()))
+    return out
+
+
 def cpu_baseline(target_s):
     """The oracle, untuned, on this host's cores: the batch-1 layer's five GEMVs, repeated
-    until about `target_s` seconds of work, reported in the same unit (GB/s)."""
+    until about `target_s` seconds of work, reported in the same unit (GB/s); then, on
+    one thread, one pass of the layer and the 1024 x 1024 GEMV repeated for about a second."""
     import numpy as np
 
     import oracle
@@ -528,9 +668,22 @@ def cpu_baseline(target_s):
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     mats = [(m, *I.nvfp4_matrix(I.DECODE_B1, m.matrix_id, m.n, m.k)) for m in I.DENSE_LAYER]
     xs = [I.activations(I.DECODE_B1, m.matrix_id, 1, m.k) for m in I.DENSE_LAYER]
+    h = hashlib.sha256()
+    for (m, c, s), x in zip(mats, xs):
+        for a_ in (c, s, x[0]):
+            h.update(np.ascontiguousarray(a_).tobytes())
     layer_bytes = sum(m.n * m.k * 9 // 16 + 2 * m.k + 4 * m.n for m in I.DENSE_LAYER)
+    layer_flops = 2 * sum(m.n * m.k for m in I.DENSE_LAYER)
     oracle.gemm(mats[4][1], mats[4][2], I.TENSOR_SCALE, xs[4], nthreads=cores)  # warm-up
     reps, t0 = 0, time.time()
     while True:
@@ -540,10 +693,30 @@ def cpu_baseline(target_s):
         if time.time() - t0 >= target_s or reps >= 200:
             break
     dt = time.time() - t0
-    log(f"cpu baseline: {reps} passes of the layer in {dt:.1f}s on {cores} threads")
+    # One thread: one pass of the layer, and the 1024 x 1024 GEMV for about a second.
+    t1 = time.time()
+    for (m, c, s), x in zip(mats, xs):
+        oracle.gemm(c, s, I.TENSOR_SCALE, x, nthreads=1)
+    dt1 = time.time() - t1
+    c0, s0 = I.nvfp4_matrix(I.GEMV_1K, 0, 1024, 1024)
+    x0 = I.activations(I.GEMV_1K, 0, 1, 1024)
+    oracle.gemm(c0, s0, I.TENSOR_SCALE, x0, nthreads=1)
+    r0, t2 = 0, time.time()
+    while time.time() - t2 < 1.0:
+        oracle.gemm(c0, s0, I.TENSOR_SCALE, x0, nthreads=1)
+        r0 += 1
+    dt0 = (time.time() - t2) / r0
+    log(f"cpu baseline ({model}): {reps} passes of the layer in {dt:.1f}s on {cores} threads; one thread: "
+        f"layer {dt1:.2f}s, 1024x1024 GEMV {dt0 * 1e3:.2f} ms")
     return {"value": round(reps * layer_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"{reps} full passes of the batch-1 layer (5 GEMVs, 330,301,440 weights) in fp64, "
-                      f"{dt:.1f} s wall"}
+                      f"{dt:.1f} s wall; then one pass on one thread and the 1024 x 1024 GEMV on one thread",
+            "cpu_model": model, "gflops_fp64": round(reps * layer_flops / dt / 1e9, 3),
+            "single_thread": {"layer_b1_s": round(dt1, 3), "layer_b1_GB/s": round(layer_bytes / dt1 / 1e9, 4),
+                              "layer_b1_gflops_fp64": round(layer_flops / dt1 / 1e9, 3),
+                              "gemv_1k_ms": round(dt0 * 1e3, 3),
+                              "gemv_1k_gflops_fp64": round(2 * 1024 * 1024 / dt0 / 1e9, 3)},
+            "inputs_sha256": h.hexdigest()}
 
 
 if __name__ == "__main__":
