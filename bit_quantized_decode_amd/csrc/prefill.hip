@@ -246,15 +246,17 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillBatch b, u
   const int lane = tid & 63;
 
   // Share of this workgroup.  Dispatch places workgroup b on XCD b % 8; give
-  // each XCD a contiguous run of shares.
+  // each XCD a contiguous run of shares: XCD x runs the q + (x < r) shares
+  // from x q + min(x, r) on (q = wgs / 8, r = wgs % 8), a bijection for any
+  // workgroup count.
   // Scalars used inside the lambdas below are copied out of the argument
   // struct: a lambda capturing the struct itself would take its address and
   // force a copy of it into scratch memory.
   const int b_wgs = b.wgs, b_count = b.count;
   const int64_t b_total = b.total, b_m = b.m;
   const bool b_ybf16 = b.y_bf16 != 0;
-  int w = (int)blockIdx.x;
-  if ((b_wgs & 7) == 0) w = (int)(blockIdx.x & 7) * (b_wgs >> 3) + (int)(blockIdx.x >> 3);
+  const int xcd = (int)(blockIdx.x & 7), xq = b_wgs >> 3, xr = b_wgs & 7;
+  const int w = xcd * xq + (xcd < xr ? xcd : xr) + (int)(blockIdx.x >> 3);
   const int64_t g_begin = share_begin(w, b_total, b_wgs);
   const int64_t g_end = share_begin(w + 1, b_total, b_wgs);
 

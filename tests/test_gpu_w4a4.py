@@ -156,19 +156,71 @@ def test_w4a4_batched_ten_problems(m):
         assert_within(bf16_to_f64(y), y_ref, s, extra=ulp_bf16(y_ref), what=f"w4a4 batch of ten m={m} {n}x{k}")
 
 
+def mx_share_count(shapes, m):
+    """The workgroup count the W4A4 launch picks for one batch (the library's
+    rule, restated: 256, or a count in [192, 256) whose share is a whole
+    number of one problem's tiles, scored by share length plus 32 iterations
+    per cut boundary per workgroup); also returns how many share boundaries
+    cut a tile.  shapes: [(n, k)] of the batch's problems."""
+    bm = 256 if m > 128 else 128
+    mtiles = (m + bm - 1) // bm
+    probs, total = [], 0
+    for n, k in shapes:
+        ntn = ((((n + 31) // 32) + 1) // 2 + 3) // 4
+        probs.append((total, (k + 63) // 64))
+        total += ntn * mtiles * ((k + 63) // 64)
+    wgs = min(max(total // 8, 1), 256)
+    if wgs < 256:
+        return wgs, None
+
+    def cuts(w):
+        c = 0
+        for i in range(1, w):
+            g = i * total // w
+            p = max(j for j, (b, _) in enumerate(probs) if j == 0 or g >= b)
+            c += (g - probs[p][0]) % probs[p][1] != 0
+        return c
+
+    def score(w):
+        return (total + w - 1) // w + (64 * cuts(w)) // w
+    best, bs = 256, score(256)
+    for _, iters in probs:
+        for j in range(1, 65):
+            if total % (j * iters):
+                continue
+            w = total // (j * iters)
+            if 192 <= w < 256 and score(w) < bs:
+                best, bs = w, score(w)
+    return best, cuts(best)
+
+
+def check_batch_sampled(items, refs, m, rows_per, seed):
+    for (mx, n, k, st, xd, y), (codes, scales, xb) in zip(items, refs):
+        rows = sample_rows(n, rows_per, seed + n)
+        rxc, rxs = oracle.mx_from_bf16(xb)
+        wc, wsc = oracle.mx_from_nvfp4(codes, scales)
+        y_ref, s = oracle.mx_gemm(wc, wsc, st, rxc, rxs, rows=rows, nthreads=oracle_threads())
+        assert_within(y.cpu().numpy().astype(np.float64)[:, rows], y_ref, s, what=f"w4a4 batch m={m} {n}x{k}")
+
+
 def test_w4a4_batched_repeat_is_bit_identical_and_counters_return_to_zero():
     """The prefill's gate, up and down in one launch, three times: the fix-up
     order of cut tiles is fixed whichever workgroup finishes a tile (a head
     segment that ends after the others finishes it from LDS and registers,
     else the last to arrive from the published sums), and every call leaves
-    the counters zero."""
+    the counters zero.  This batch runs on 204 workgroups (no gate or up tile
+    cut, the down tiles cut; 204 is not a multiple of the 8 XCDs), and each
+    output is checked against the oracle on sampled rows."""
     dev = device()
-    items = []
+    assert mx_share_count([(m.n, m.k) for m in I.PREFILL_MATRICES], 512) == (204, 64)
+    items, refs = [], []
     for mat in I.PREFILL_MATRICES:
         codes, scales = I.nvfp4_matrix(I.PREFILL_512, mat.matrix_id, mat.n, mat.k)
+        xb = I.activations(I.PREFILL_512, mat.matrix_id, 512, mat.k)
         mx = B.mx_pack(to_dev_u8(codes, dev), to_dev_u8(scales, dev))
-        x = to_dev_bf16(I.activations(I.PREFILL_512, mat.matrix_id, 512, mat.k), dev)
-        items.append((mx, mat.n, mat.k, I.TENSOR_SCALE, x, torch.empty((512, mat.n), dtype=torch.float32, device=dev)))
+        items.append((mx, mat.n, mat.k, I.TENSOR_SCALE, to_dev_bf16(xb, dev),
+                      torch.empty((512, mat.n), dtype=torch.float32, device=dev)))
+        refs.append((codes, scales, xb))
     ws = torch.zeros(B.w4a4_batched_workspace_bytes(items, 512), dtype=torch.uint8, device=dev)
     outs = []
     for _ in range(3):
@@ -180,6 +232,48 @@ def test_w4a4_batched_repeat_is_bit_identical_and_counters_return_to_zero():
     for a, b in zip(outs[0], outs[2]):
         assert torch.equal(a.view(torch.int32), b.view(torch.int32))
     assert int(torch.count_nonzero(ws[: 1 << 18])) == 0
+    check_batch_sampled(items, refs, 512, 48, 610)
+
+
+def test_w4a4_batched_fewer_shares_with_cut_tiles():
+    """A batch for which the launch takes 208 workgroups (a share is four
+    tiles of the first problem) and cuts 160 tile boundaries of the others."""
+    dev = device()
+    shapes, m = [(1024, 1024), (1024, 1024), (4096, 6144)], 300
+    assert mx_share_count(shapes, m) == (208, 160)
+    rng = np.random.default_rng(208)
+    items, refs = [], []
+    for n, k in shapes:
+        codes, scales = random_matrix(rng, n, k)
+        xb = I.bf16_round(rng.standard_normal((m, k)).astype(np.float32))
+        mx = B.mx_pack(to_dev_u8(codes, dev), to_dev_u8(scales, dev))
+        items.append((mx, n, k, I.TENSOR_SCALE, to_dev_bf16(xb, dev), torch.empty((m, n), dtype=torch.float32, device=dev)))
+        refs.append((codes, scales, xb))
+    B.w4a4_batched(items)
+    torch.cuda.synchronize()
+    check_batch_sampled(items, refs, m, 64, 620)
+
+
+def test_w4a4_same_sign_long_k():
+    """Every MX product >= 0 (weight codes 0-7, activations |N(0,1)|): the
+    partial sums only grow, the worst case for the fp32 accumulation chains;
+    the prefill's longest k (17408) at 512 rows, fp32 out."""
+    dev = device()
+    m, n, k = 512, 1024, 17408
+    rng = np.random.default_rng(17408)
+    c = rng.integers(0, 8, size=(n, k)).astype(np.uint8)
+    codes = (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+    scales = I.e4m3_round(np.exp2(rng.uniform(-6, 2, size=(n, k // 16))))
+    xb = I.bf16_round(np.abs(rng.standard_normal((m, k))).astype(np.float32))
+    mx = B.mx_pack(to_dev_u8(codes, dev), to_dev_u8(scales, dev))
+    y = B.w4a4_gemm(mx, n, k, I.TENSOR_SCALE, to_dev_bf16(xb, dev), y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = sample_rows(n, 48, 630)
+    wc, wsc = oracle.mx_from_nvfp4(codes, scales)
+    xc, xs = oracle.mx_from_bf16(xb)
+    y_ref, s = oracle.mx_gemm(wc, wsc, I.TENSOR_SCALE, xc, xs, rows=rows, nthreads=oracle_threads())
+    worst = assert_within(y.cpu().numpy().astype(np.float64)[:, rows], y_ref, s, what="w4a4 same sign")
+    print(f"same-sign W4A4, k={k}: worst error {worst:.3g} of sum|w' x'|")
 
 
 @pytest.mark.parametrize("mat", I.PREFILL_MATRICES, ids=lambda m: m.name)
