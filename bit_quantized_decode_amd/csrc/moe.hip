@@ -569,13 +569,15 @@ struct MoeWs {
 MoeWs carve(void* ws, int64_t tokens, int64_t experts, int64_t top_k, int64_t hidden, int64_t inter, size_t* total) {
   uint8_t* p = static_cast<uint8_t*>(ws);
   size_t off = 0;
+  // (ws == nullptr: only the total is wanted; no pointer arithmetic on it.)
+  auto at = [&](size_t o) { return p ? p + o : nullptr; };
   MoeWs w;
   const int64_t f = tokens * top_k;
-  w.pos = reinterpret_cast<int32_t*>(p + off); off = align256(off + (size_t)f * 4);
-  w.h = reinterpret_cast<uint16_t*>(p + off); off = align256(off + (size_t)f * inter * 2);
-  w.d = reinterpret_cast<float*>(p + off); off = align256(off + (size_t)f * hidden * 4);
-  w.chunks = reinterpret_cast<int32_t*>(p + off); off = align256(off + (size_t)max_chunks(tokens, experts, top_k) * kChunkInts * 4);
-  w.n_chunks = reinterpret_cast<int32_t*>(p + off); off = align256(off + 16);
+  w.pos = reinterpret_cast<int32_t*>(at(off)); off = align256(off + (size_t)f * 4);
+  w.h = reinterpret_cast<uint16_t*>(at(off)); off = align256(off + (size_t)f * inter * 2);
+  w.d = reinterpret_cast<float*>(at(off)); off = align256(off + (size_t)f * hidden * 4);
+  w.chunks = reinterpret_cast<int32_t*>(at(off)); off = align256(off + (size_t)max_chunks(tokens, experts, top_k) * kChunkInts * 4);
+  w.n_chunks = reinterpret_cast<int32_t*>(at(off)); off = align256(off + 16);
   if (total) *total = off;
   return w;
 }
