@@ -1,4 +1,4 @@
-// a2: NVFP4 GEMV, one bf16 activation vector -> fp32 outputs.
+// NVFP4 GEMV: one bf16 activation vector -> fp32 outputs.
 //
 // y[j] = s_t * sum_k e2m1(c[j][k]) * e4m3(sigma[j][k/16]) * x[k]
 //

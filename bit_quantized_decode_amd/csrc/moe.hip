@@ -1,4 +1,4 @@
-// a4-a8: the top-k routed mixture-of-experts layer on NVFP4 experts.
+// The top-k routed mixture-of-experts layer on NVFP4 experts.
 //
 // Each token is routed to `top_k` of `experts` experts and only the routed
 // experts' weights are read (CHImp-Alpha-v1.0 model card, "How it fits on one
@@ -341,7 +341,7 @@ __device__ __forceinline__ void store_partials(float* red, int wave, int lane, c
   }
 }
 
-// a6: gate/up.  Workgroup (chunk, row tile rt): wavefronts 0-3 take the gate
+// Gate/up.  Workgroup (chunk, row tile rt): wavefronts 0-3 take the gate
 // matrix's tile rt at k slots 0-3, wavefronts 4-7 the up matrix's; then
 // h = bf16(silu(s_g Wg x) * (s_u Wu x)) for the tile's 64 rows.
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void gate_up_kernel(
@@ -406,7 +406,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
   }
 }
 
-// a7: down.  Workgroup (chunk, row tiles 4 q .. 4 q + 3): wavefront w takes
+// Down.  Workgroup (chunk, row tiles 4 q .. 4 q + 3): wavefront w takes
 // row tile 4 q + w / 2 at k slot w % 2; d = s_d Wd h (fp32) for those rows.
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void down_kernel(
     const uint16_t* __restrict__ hin, const int32_t* __restrict__ chunks, const int32_t* __restrict__ n_chunks,

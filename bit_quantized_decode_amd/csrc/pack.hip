@@ -1,4 +1,4 @@
-// a1: repack canonical NVFP4 codes/scales into the tile layout (and back).
+// Repack canonical NVFP4 codes/scales into the tile layout (and back).
 // A pure byte permutation into the tile layout described in device_common.h,
 // zero past the matrix edge.
 #include "device_common.h"

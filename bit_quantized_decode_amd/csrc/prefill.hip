@@ -1,4 +1,4 @@
-// a9: NVFP4 x bf16 GEMM for many activation rows (prompt prefill).
+// NVFP4 x bf16 GEMM for many activation rows (prompt prefill).
 //
 // y[i][j] = s_t * sum_k W[j][k] * x[i][k]
 //

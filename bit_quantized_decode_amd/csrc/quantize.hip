@@ -1,4 +1,4 @@
-// f1: the NVFP4 quantiser -- fp32 or bf16 weights to canonical codes [n][k/2],
+// The NVFP4 quantiser -- fp32 or bf16 weights to canonical codes [n][k/2],
 // E4M3 block scales [n][k/16] and one fp32 per-tensor scale; the step before
 // the repack (the imp README, "How does it work?", converts weights to NVFP4
 // once and then computes on them).

@@ -1,4 +1,4 @@
-// a3: NVFP4 x bf16 GEMM for up to 32 activation rows (a decode batch).
+// NVFP4 x bf16 GEMM for up to 32 activation rows (a decode batch).
 //
 // y[i][j] = s_t * sum_k W[j][k] * x[i][k],   i < m <= 32.
 //

@@ -1,5 +1,5 @@
-// The skinny-product core shared by the decode-batch GEMM (a3) and the
-// mixture-of-experts expert GEMMs (a6, a7): a workgroup of four wavefronts
+// The skinny-product core shared by the decode-batch GEMM and the
+// mixture-of-experts expert GEMMs (gate/up, down): a workgroup of four wavefronts
 // multiplies four 64-row NVFP4 tiles (one per wavefront, possibly of different
 // matrices), over a common range of 256-k tiles, by the same <= 32 bf16
 // activation rows, on the bf16 matrix cores.

@@ -1,4 +1,4 @@
-// f4: W4A4 prefill -- both operands in the OCP MX FP4 format (32 k elements
+// W4A4 prefill -- both operands in the OCP MX FP4 format (32 k elements
 // per E8M0 power-of-two scale) on gfx950's scaled FP4 matrix instruction
 // v_mfma_scale_f32_32x32x64_f8f6f4, the native-FP4 design point of the pages'
 // prefill (imp README, "How does it work?").  An approximation of the NVFP4

@@ -88,7 +88,7 @@ const char* nvfp4_status_str(int status);
 /* Thread-local text describing this thread's last failed call ("" if none). */
 const char* nvfp4_last_error(void);
 
-/* ---- a1: offline repack -------------------------------------------------------
+/* ---- offline repack -------------------------------------------------------
  * The packed buffer is the only form the product kernels read.  Its layout is
  * private to the library (a gfx950 tile layout); only nvfp4_packed_bytes() and
  * nvfp4_unpack() expose it.  It holds exactly the NVFP4 information (0.5625
@@ -112,7 +112,7 @@ int nvfp4_pack(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k
 int nvfp4_unpack(const void* packed, int64_t n, int64_t k, uint8_t* codes, uint8_t* scales,
                  void* stream);
 
-/* ---- f1: quantiser (the step before nvfp4_pack) ---------------------------------
+/* ---- quantiser (the step before nvfp4_pack) ---------------------------------
  * Encodes an [n][k] weight matrix, fp32 or bf16 (w_dtype), rows ldw elements
  * apart, as canonical NVFP4: codes [n][k/2], scales [n][k/16] (the layouts
  * nvfp4_pack() reads) and one fp32 per-tensor scale written to *tensor_scale
@@ -136,7 +136,7 @@ int nvfp4_quantize(const void* w, int w_dtype, int64_t n, int64_t k, int64_t ldw
                    uint8_t* scales, float* tensor_scale, void* workspace, size_t workspace_bytes,
                    void* stream);
 
-/* ---- a2: GEMV, one activation vector ----------------------------------------
+/* ---- GEMV, one activation vector ----------------------------------------
  * y[j] = s_t * sum_k e2m1(c[j][k]) * e4m3(sigma[j][k/16]) * x[k],   j < n.
  * x: bf16 bit patterns [k];  y: float32 [n].
  * The memory-bound decode product: the Ignis README ("The decode round")
@@ -149,7 +149,7 @@ int nvfp4_gemv(const void* packed, int64_t n, int64_t k, float tensor_scale,
                const uint16_t* x, float* y, void* workspace, size_t workspace_bytes,
                void* stream);
 
-/* ---- a3 / a9: GEMM, m activation rows -----------------------------------------
+/* ---- GEMM, m activation rows -----------------------------------------
  * y[i][j] = s_t * sum_k W[j][k] * x[i][k],   i < m, j < n.
  * x: bf16 bit patterns, row i at x + i*ldx (ldx >= k, ldx % 8 == 0);
  * y: y_dtype, row i at y + i*ldy elements (ldy >= n).
@@ -167,7 +167,7 @@ int nvfp4_gemm(const void* packed, int64_t n, int64_t k, float tensor_scale,
                void* y, int64_t ldy, int y_dtype,
                void* workspace, size_t workspace_bytes, void* stream);
 
-/* ---- f4: W4A4 prefill on the FP4 matrix cores (an approximation) -------------
+/* ---- W4A4 prefill on the FP4 matrix cores (an approximation) -------------
  * The pages' prefill runs native FP4 on weights and activations (imp README,
  * "How does it work?").  gfx950's FP4 matrix instruction takes the OCP MX
  * format: E2M1 values with one power-of-two (E8M0) scale per 32 k.  Both
@@ -244,7 +244,7 @@ int nvfp4_gemm_batched_workspace_bytes(const nvfp4_problem* problems /* host */,
                                        size_t* bytes /* host */);
 int nvfp4_gemm_batched(const nvfp4_problem* problems /* host */, int count, int64_t m, int y_dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
-/* W4A4 batch (the f4 rule above for each problem; `packed` holds the MX
+/* W4A4 batch (the W4A4 rule above for each problem; `packed` holds the MX
  * tiles of nvfp4_mx_pack): one stream-K launch per eight problems, so that
  * the split tiles' fix-up is shared like the gemm batch's.  The workspace holds
  * the schedule's counters and partial sums (zero before the first use, left
@@ -257,7 +257,7 @@ int nvfp4_w4a4_batched_workspace_bytes(const nvfp4_problem* problems /* host */,
 int nvfp4_w4a4_batched(const nvfp4_problem* problems /* host */, int count, int64_t m, int y_dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
 
-/* ---- a4-a8: top-k routed mixture-of-experts layer ----------------------------
+/* ---- top-k routed mixture-of-experts layer ----------------------------
  * Per token t (CHImp-Alpha-v1.0 model card, "How it fits on one GPU": each
  * token is routed to 10 of 512 experts and only those experts' weights are read):
  *   ids[t][0..top_k)  the top_k experts by router logit, descending, equal
@@ -310,7 +310,7 @@ typedef struct nvfp4_moe_args {
 int nvfp4_moe_workspace_bytes(const nvfp4_moe_args* args /* host */, size_t* bytes /* host */);
 int nvfp4_moe_grouped(const nvfp4_moe_args* args /* host */, void* stream);
 
-/* ---- f3: routed experts streamed from host memory --------------------------
+/* ---- routed experts streamed from host memory --------------------------
  * The imp README runs mixture-of-experts models larger than the card with the
  * experts in host RAM ("Will it fit?"); only the routed experts' weights are
  * needed per token (CHImp-Alpha-v1.0 model card, "How it fits on one GPU").

@@ -49,7 +49,7 @@ def check_moe(w, x, logits, top_k, y_dtype=torch.float32, end_to_end=True, o=Non
         o = run_moe(w, x, logits, top_k, dev, y_dtype=y_dtype)
     nt = oracle_threads()
 
-    # a4 / a5: routing and grouping, bit-exact.
+    # Routing and grouping, bit-exact.
     ids_ref, g_ref = oracle.route(logits, top_k)
     counts_ref, offsets_ref, perm_ref, pos_ref = oracle.group(ids_ref, e)
     ids = o["topk_ids"].cpu().numpy()
@@ -60,7 +60,7 @@ def check_moe(w, x, logits, top_k, y_dtype=torch.float32, end_to_end=True, o=Non
     g = o["topk_weights"].cpu().numpy().astype(np.float64)
     assert np.allclose(g, g_ref, rtol=1e-6, atol=0)
 
-    # a6: gate / up per expert, fed the same activation rows.
+    # Gate / up per expert, fed the same activation rows.
     gate = o["dbg_gate"].cpu().numpy().astype(np.float64)
     up = o["dbg_up"].cpu().numpy().astype(np.float64)
     h = o["dbg_h"]
@@ -78,7 +78,7 @@ def check_moe(w, x, logits, top_k, y_dtype=torch.float32, end_to_end=True, o=Non
         uy, us = oracle.gemm(w.up_codes[ex], w.up_scales[ex], w.up_st[ex], xs, nthreads=nt)
         assert_within(gate[p0:p1], gy, gs, what=f"gate expert {ex}")
         assert_within(up[p0:p1], uy, us, what=f"up expert {ex}")
-        # a7: down, fed the GPU's own h.
+        # Down, fed the GPU's own h.
         dy, ds = oracle.gemm(w.down_codes[ex], w.down_scales[ex], w.down_st[ex],
                              np.ascontiguousarray(h_bits[p0:p1]), nthreads=nt)
         assert_within(down[p0:p1], dy, ds, what=f"down expert {ex}")
@@ -88,7 +88,7 @@ def check_moe(w, x, logits, top_k, y_dtype=torch.float32, end_to_end=True, o=Non
     hz = oracle.silu(gate) * up
     assert np.all(np.abs(h_f64 - hz) <= ulp_bf16(hz) + 1e-300)
 
-    # a8: scatter with the GPU's g over the oracle's d (of the GPU's h).
+    # Scatter with the GPU's g over the oracle's d (of the GPU's h).
     pos = pos_ref.reshape(t, top_k)
     y_ref_stage = np.einsum("tj,tjo->to", g, d_ref_gpu_h[pos])
     bound_stage = np.einsum("tj,tjo->to", g, s_down[pos])

@@ -1,4 +1,4 @@
-"""GPU parity: the decode-batch skinny GEMM (a3, m <= 32) and the prefill GEMM (a9, m > 32)."""
+"""GPU parity: the decode-batch skinny GEMM (m <= 32) and the prefill GEMM (m > 32)."""
 import numpy as np
 import pytest
 import torch

@@ -1,4 +1,4 @@
-"""GPU parity: the routed expert layer (a4-a8) against the CPU oracle.
+"""GPU parity: the routed expert layer against the CPU oracle.
 
 Integer outputs (ids, counts, offsets, perm) must be bit-exact.  Each GEMM
 stage is checked against the oracle fed that stage's GPU input; the whole

@@ -1,4 +1,4 @@
-"""GPU: routed experts streamed from pinned host memory (f3) against the
+"""GPU: routed experts streamed from pinned host memory against the
 oracle (every stage and the whole layer, as for the resident layer), against
 the same layer with the experts device-resident (bit-identical outputs), and
 the cache's bookkeeping (hits, least-recently-used eviction, the slot limit)."""

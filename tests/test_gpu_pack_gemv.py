@@ -1,4 +1,4 @@
-"""GPU parity: offline repack (a1) and the batch-1 GEMV (a2) against the CPU oracle."""
+"""GPU parity: offline repack and the batch-1 GEMV against the CPU oracle."""
 import numpy as np
 import pytest
 import torch

@@ -1,4 +1,4 @@
-"""GPU parity: the NVFP4 quantiser (f1) against the CPU oracle, bit-exact.
+"""GPU parity: the NVFP4 quantiser against the CPU oracle, bit-exact.
 
 Codes, block scales and the tensor scale are integer decisions (taken in fp32
 on both sides), so every byte must match.

@@ -1,4 +1,4 @@
-"""GPU parity for the W4A4 product (f4): both operands in the OCP MX FP4 format
+"""GPU parity for the W4A4 product: both operands in the OCP MX FP4 format
 on the FP4 matrix instruction, against the oracle's MX product.  The MX
 operands themselves (weights requantised from NVFP4, activations quantised per
 call) must match the oracle bit for bit; the products within 1e-5 of
