@@ -6,7 +6,9 @@
 // streaming at the card's bandwidth).  Mapping on gfx950:
 //  - one wavefront per (64-row tile, 256-k tile), issuing all ten of its
 //    16-byte loads per lane at once; the grid holds every tile of the matrix,
-//    so the whole weight stream is requested from the start;
+//    so the whole weight stream is requested from the start; the loads are
+//    non-temporal (each weight is read once: measured, the layer runs ~6 %
+//    faster than with ordinary loads);
 //  - in the tile layout lane l carries rows l%32 and 32 + l%32 at k half
 //    l/32 of every 16-k step, so it needs only 16 of each chunk's 32
 //    activations; a workgroup is four wavefronts on four consecutive k tiles
@@ -110,10 +112,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvBatch b, unsigned* 
   u32x4 q[8], sa = {0u, 0u, 0u, 0u}, sb = {0u, 0u, 0u, 0u};
   if (has_tile) {
     const uint8_t* t = packed + ((size_t)rt * nkt + kt) * kTileBytes;
-    sa = load16(t + kScaleOffset + 32 * (lane & 31));
-    sb = load16(t + kScaleOffset + 32 * (lane & 31) + 16);
+    sa = load16_stream(t + kScaleOffset + 32 * (lane & 31));
+    sb = load16_stream(t + kScaleOffset + 32 * (lane & 31) + 16);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) q[c] = load16(t + c * 1024 + lane * 16);
+    for (int c = 0; c < 8; ++c) q[c] = load16_stream(t + c * 1024 + lane * 16);
   }
   // Stage the workgroup's 1024 activations (128 x 16 bytes).
   if (threadIdx.x < kGemvWaves * kTileK / 8) {
@@ -230,10 +232,10 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(const GemvRowsBatch b, u
   u32x4 q[8], sa = {0u, 0u, 0u, 0u}, sb = {0u, 0u, 0u, 0u};
   if (has_tile) {
     const uint8_t* t = packed + ((size_t)rt * nkt + kt) * kTileBytes;
-    sa = load16(t + kScaleOffset + 32 * (lane & 31));
-    sb = load16(t + kScaleOffset + 32 * (lane & 31) + 16);
+    sa = load16_stream(t + kScaleOffset + 32 * (lane & 31));
+    sb = load16_stream(t + kScaleOffset + 32 * (lane & 31) + 16);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) q[c] = load16(t + c * 1024 + lane * 16);
+    for (int c = 0; c < 8; ++c) q[c] = load16_stream(t + c * 1024 + lane * 16);
   }
   for (int i = threadIdx.x; i < M * (kGemvWaves * kTileK / 8); i += 256) {
     const int r = i / (kGemvWaves * kTileK / 8), c = i % (kGemvWaves * kTileK / 8);

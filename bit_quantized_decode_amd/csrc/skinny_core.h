@@ -45,10 +45,10 @@ struct WTile {
 };
 
 __device__ __forceinline__ void load_wtile(const uint8_t* tile, int lane, WTile& r) {
-  r.sa = load16(tile + kScaleOffset + 32 * (lane & 31));
-  r.sb = load16(tile + kScaleOffset + 32 * (lane & 31) + 16);
+  r.sa = load16_stream(tile + kScaleOffset + 32 * (lane & 31));
+  r.sb = load16_stream(tile + kScaleOffset + 32 * (lane & 31) + 16);
 #pragma unroll
-  for (int c = 0; c < 8; ++c) r.q[c] = load16(tile + c * 1024 + lane * 16);
+  for (int c = 0; c < 8; ++c) r.q[c] = load16_stream(tile + c * 1024 + lane * 16);
 }
 
 // One 32-k chunk C of a tile: four MFMAs into the two tile accumulators.  The
@@ -164,10 +164,10 @@ __device__ __forceinline__ void skinny_stream(const uint8_t* wrow, int kt0, int 
   const uint32_t lane_code = lane * 16, lane_scale = kScaleOffset + 32 * (lane & 31);
   auto load_w = [&](int i, WTile& w) __attribute__((always_inline)) {
     const uint8_t* t = wrow + (size_t)tile_of(i) * kTileBytes;
-    w.sa = load16(t + lane_scale);
-    w.sb = load16(t + lane_scale + 16);
+    w.sa = load16_stream(t + lane_scale);
+    w.sb = load16_stream(t + lane_scale + 16);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) w.q[c] = load16(t + c * 1024 + lane_code);
+    for (int c = 0; c < 8; ++c) w.q[c] = load16_stream(t + c * 1024 + lane_code);
   };
   const int br = lane & 31, bh = lane >> 5;
   const uint32_t abase_a = 512 * br + 16 * (bh ^ (br & 3));
@@ -182,12 +182,12 @@ __device__ __forceinline__ void skinny_stream(const uint8_t* wrow, int kt0, int 
 #define NVFP4_SK_CHUNK(C)                                 \
   load_bops<C>(buf, abase_a, abase_b, sw, xa, xb);        \
   chunk_mfma<C>(w.q[C], w.sa, w.sb, xa, xb, ta, tb);      \
-  w.q[C] = load16(t + C * 1024 + lane_code);
+  w.q[C] = load16_stream(t + C * 1024 + lane_code);
     NVFP4_SK_CHUNK(0) NVFP4_SK_CHUNK(1) NVFP4_SK_CHUNK(2) NVFP4_SK_CHUNK(3)
     NVFP4_SK_CHUNK(4) NVFP4_SK_CHUNK(5) NVFP4_SK_CHUNK(6) NVFP4_SK_CHUNK(7)
 #undef NVFP4_SK_CHUNK
-    w.sa = load16(t + lane_scale);
-    w.sb = load16(t + lane_scale + 16);
+    w.sa = load16_stream(t + lane_scale);
+    w.sb = load16_stream(t + lane_scale + 16);
     acc_a += ta;
     acc_b += tb;
   };
