@@ -20,6 +20,13 @@
 // what fits at once) that walk the work list; its actual length is read on
 // the device.  A chunk's record holds everything a GEMM workgroup needs, so
 // its weight loads wait on one load only.
+// A small batch (tokens * top_k <= 1024 routed rows over at most 1024
+// experts, the decode case) skips launch 2: every gate/up workgroup groups
+// the routed rows itself in its LDS before its first item -- a few
+// microseconds of integer work in parallel on every CU instead of a
+// dependent one-workgroup launch -- and workgroup 0 writes the grouping
+// outputs and the work-list headers that launches 4 and 5 read.  The result
+// is the same stable grouping, bit for bit.
 #include <atomic>
 
 #include "device_common.h"
@@ -33,6 +40,10 @@ constexpr int kMaxExperts = 2048;
 constexpr int kMaxTopK = 64;
 constexpr int kChunkRows = 32;               // activation rows per expert-GEMM workgroup
 constexpr int kChunkInts = 4 + kChunkRows;   // one work-list record
+// Batches the gate/up workgroups group in their own LDS.
+constexpr int kLocalFlat = 1024;
+constexpr int kLocalExperts = 1024;
+constexpr int kLocalChunks = kLocalExperts + kLocalFlat / kChunkRows;  // bound on the work-list length
 
 // Routing key of one logit: larger logit first, then the smaller expert id
 // (-0 counts as +0); unsigned 64-bit order = (logit desc, id asc).
@@ -279,6 +290,127 @@ __global__ __launch_bounds__(1024) void group_kernel(const int32_t* __restrict__
   group_body(ids, total, experts, top_k, counts, offsets, perm, pos, chunks, n_chunks);
 }
 
+// ---- grouping inside the expert-GEMM workgroups (small batches) ----------
+// What a gate/up workgroup keeps of the grouping for its items: the expert
+// offsets, the stable permutation, and per work-list chunk its expert and
+// its index among that expert's chunks.
+struct LocalGroups {
+  int off[kLocalExperts + 1];
+  int perm[kLocalFlat];
+  uint32_t chunk[kLocalChunks];  // expert << 16 | chunk index within the expert
+  int nch;
+};
+
+// Two exclusive scans at once over n <= 1024 entries by a 512-thread
+// workgroup (thread t owns entries 2t, 2t+1): out_a of in_a, and out_b of
+// the 32-row chunk counts ceil(in_a / 32).  out_a[n] and out_b[n] receive the
+// totals.  s_red: 32 ints of scratch.
+__device__ __forceinline__ void scan_counts_512(const int* in_a, int* out_a, int* out_b, int n, int* s_red) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int a0 = 2 * tid < n ? in_a[2 * tid] : 0;
+  const int a1 = 2 * tid + 1 < n ? in_a[2 * tid + 1] : 0;
+  const int b0 = (a0 + kChunkRows - 1) / kChunkRows, b1 = (a1 + kChunkRows - 1) / kChunkRows;
+  const int ia = wave_inclusive_sum(a0 + a1), ib = wave_inclusive_sum(b0 + b1);
+  if (lane == 63) {
+    s_red[wave] = ia;
+    s_red[8 + wave] = ib;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    // Lanes 0-7 scan the eight wavefront totals of a, lanes 16-23 those of b.
+    const int v = (lane & 15) < 8 && lane < 32 ? s_red[(lane >> 4) * 8 + (lane & 7)] : 0;
+    const int inc = wave_inclusive_sum(v);  // rows of 16: lanes 16-31 continue lanes 0-15's sum
+    const int tot_a = __builtin_amdgcn_readlane(inc, 15);
+    const int base = lane >= 16 && lane < 32 ? tot_a : 0;
+    if (lane < 8) s_red[16 + lane] = inc - v;
+    if (lane >= 16 && lane < 24) s_red[24 + (lane & 7)] = inc - base - v;
+    if (lane == 7) s_red[32] = inc;
+    if (lane == 23) s_red[33] = inc - base;
+  }
+  __syncthreads();
+  const int ea = s_red[16 + wave] + ia - (a0 + a1), eb = s_red[24 + wave] + ib - (b0 + b1);
+  if (2 * tid < n) {
+    out_a[2 * tid] = ea;
+    out_b[2 * tid] = eb;
+  }
+  if (2 * tid + 1 < n) {
+    out_a[2 * tid + 1] = ea + a0;
+    out_b[2 * tid + 1] = eb + b0;
+  }
+  if (tid == 0) {
+    out_a[n] = s_red[32];
+    out_b[n] = s_red[33];
+  }
+  __syncthreads();
+}
+
+// The stable grouping of `flat` routed rows (flat <= kLocalFlat, experts <=
+// kLocalExperts) by a 512-thread workgroup, into `lg`.  `tmp` is scratch of at
+// least (2 kLocalFlat + 3 kLocalExperts + 65) ints.  Each row is placed in
+// its expert's segment by an LDS atomic (any order), then ranked by the
+// number of that segment's rows with a smaller flat index, so the
+// permutation is the stable sort by expert whatever the atomics' order.
+// With `write` the grouping outputs and the work-list headers (expert, first
+// row slot, rows) also go to memory.
+__device__ void group_local(const int32_t* __restrict__ ids, int flat, int experts, int* tmp, LocalGroups& lg,
+                            bool write, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                            int32_t* __restrict__ perm, int32_t* __restrict__ pos, int32_t* __restrict__ chunks,
+                            int32_t* __restrict__ n_chunks) {
+  int* s_ids = tmp;                     // [kLocalFlat]
+  int* s_unord = s_ids + kLocalFlat;    // [kLocalFlat] rows placed by atomics
+  int* s_cnt = s_unord + kLocalFlat;    // [kLocalExperts]
+  int* s_run = s_cnt + kLocalExperts;   // [kLocalExperts]
+  int* s_chb = s_run + kLocalExperts;   // [kLocalExperts + 1] first chunk of each expert
+  int* s_red = s_chb + kLocalExperts + 1;
+  const int tid = threadIdx.x;
+  for (int f = tid; f < flat; f += 512) s_ids[f] = ids[f];
+  for (int e = tid; e < experts; e += 512) s_cnt[e] = s_run[e] = 0;
+  __syncthreads();
+  for (int f = tid; f < flat; f += 512) atomicAdd(&s_cnt[s_ids[f]], 1);
+  __syncthreads();
+  scan_counts_512(s_cnt, lg.off, s_chb, experts, s_red);
+  for (int f = tid; f < flat; f += 512) {
+    const int e = s_ids[f];
+    s_unord[lg.off[e] + atomicAdd(&s_run[e], 1)] = f;
+  }
+  __syncthreads();
+  for (int f = tid; f < flat; f += 512) {
+    const int e = s_ids[f], b = lg.off[e], n = s_cnt[e];
+    int r = 0;
+    for (int q = 0; q < n; ++q) r += s_unord[b + q] < f ? 1 : 0;
+    lg.perm[b + r] = f;
+  }
+  for (int e = tid; e < experts; e += 512)
+    for (int c = 0, c0 = s_chb[e]; c0 + c < s_chb[e + 1]; ++c) lg.chunk[c0 + c] = ((uint32_t)e << 16) | (uint32_t)c;
+  if (tid == 0) lg.nch = s_chb[experts];
+  __syncthreads();
+  if (write) {
+    for (int e = tid; e < experts; e += 512) {
+      counts[e] = s_cnt[e];
+      offsets[e] = lg.off[e];
+    }
+    if (tid == 0) {
+      offsets[experts] = flat;
+      *n_chunks = lg.nch;
+    }
+    for (int p = tid; p < flat; p += 512) {
+      perm[p] = lg.perm[p];
+      pos[lg.perm[p]] = p;
+    }
+    for (int j = tid; j < lg.nch; j += 512) {
+      const int e = (int)(lg.chunk[j] >> 16), c = (int)(lg.chunk[j] & 0xffffu);
+      const int p0 = lg.off[e] + c * kChunkRows;
+      const int rows = lg.off[e] + s_cnt[e] - p0 < kChunkRows ? lg.off[e] + s_cnt[e] - p0 : kChunkRows;
+      int32_t* r = chunks + (size_t)j * kChunkInts;
+      r[0] = e;
+      r[1] = p0;
+      r[2] = rows;
+      r[3] = 0;
+    }
+  }
+  __syncthreads();  // the scratch is free again
+}
+
 // ---- expert GEMMs --------------------------------------------------------
 // One workgroup of 8 wavefronts per (work-list chunk, output rows); each
 // wavefront multiplies one 64-row weight tile by one 256-k activation tile
@@ -290,6 +422,7 @@ __global__ __launch_bounds__(1024) void group_kernel(const int32_t* __restrict__
 // which the dequantisation needs to keep a SIMD busy.
 constexpr int kExpertWaves = 8;
 constexpr int kExpertLds = 64 * 1024;  // 4 activation tiles, later 8 wavefronts' partial sums
+static_assert(kExpertWaves * 64 == 512, "group_local and scan_counts_512 assume 512 threads");
 
 // This wavefront's share of staging k tiles t0 .. t0 + KS - 1 of a chunk:
 // activation rows 4 w .. 4 w + 3 of each (row 4 w + 2 j + lane / 32 from
@@ -344,35 +477,68 @@ __device__ __forceinline__ void store_partials(float* red, int wave, int lane, c
 // Gate/up.  Workgroup (chunk, row tile rt): wavefronts 0-3 take the gate
 // matrix's tile rt at k slots 0-3, wavefronts 4-7 the up matrix's; then
 // h = bf16(silu(s_g Wg x) * (s_u Wu x)) for the tile's 64 rows.
+// LOCAL: the workgroup first groups the routed rows (`ids`) itself; the work
+// list then lives in its LDS, and workgroup 0 writes the grouping outputs.
+struct LocalArgs {
+  const int32_t* ids;
+  int flat, experts, top_k;
+  int32_t *counts, *offsets, *perm, *pos;
+};
+
+template <bool LOCAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void gate_up_kernel(
-    const uint16_t* __restrict__ x, const int32_t* __restrict__ chunks, const int32_t* __restrict__ n_chunks,
+    const uint16_t* __restrict__ x, int32_t* __restrict__ chunks, int32_t* __restrict__ n_chunks,
     int max_chunks, int hidden, int inter, const uint8_t* __restrict__ w_gate, const uint8_t* __restrict__ w_up,
     size_t stride_gate, size_t stride_up, const int32_t* __restrict__ slot_table,
     const float* __restrict__ scale_gate, const float* __restrict__ scale_up, uint16_t* __restrict__ h,
-    float* __restrict__ dbg_gate, float* __restrict__ dbg_up) {
+    float* __restrict__ dbg_gate, float* __restrict__ dbg_up, const LocalArgs la) {
   constexpr int KS = 4;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kExpertLds];
+  __shared__ LocalGroups lg;  // LOCAL only (otherwise unused, and not allocated)
   const int nrt = (inter + 63) / 64;
   const int nkt = (hidden + 255) / 256;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int slot = wave % KS;
-  const int nch = *n_chunks;
+  int nch;
+  if constexpr (LOCAL) {
+    group_local(la.ids, la.flat, la.experts, reinterpret_cast<int*>(lds), lg, blockIdx.x == 0, la.counts,
+                la.offsets, la.perm, la.pos, chunks, n_chunks);
+    nch = lg.nch;
+  } else {
+    nch = *n_chunks;
+  }
   for (int64_t item = blockIdx.x;; item += gridDim.x) {
     const int64_t jq = item / nrt;
     const int jc = jq < max_chunks ? (int)jq : max_chunks;  // max_chunks: past the list
     const int rt = (int)(item % nrt);
-    // The record's loads do not wait for the count: its index is clamped
-    // into the list's allocation.
-    const int32_t* rec = chunks + (size_t)(jc < max_chunks ? jc : max_chunks - 1) * kChunkInts;
-    const int e = rec[0], p0 = rec[1], rows = rec[2];
-    if (jc >= nch) break;
+    int e, p0, rows;
+    const uint16_t* xrow[2];
+    if constexpr (LOCAL) {
+      if (jc >= nch) break;
+      const uint32_t ci = lg.chunk[jc];
+      e = (int)(ci >> 16);
+      p0 = lg.off[e] + (int)(ci & 0xffffu) * kChunkRows;
+      rows = lg.off[e + 1] - p0 < kChunkRows ? lg.off[e + 1] - p0 : kChunkRows;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = 4 * wave + 2 * j + (lane >> 5);
+        xrow[j] = x + (int64_t)(lg.perm[p0 + (r < rows ? r : rows - 1)] / la.top_k) * hidden;
+      }
+    } else {
+      // The record's loads do not wait for the count: its index is clamped
+      // into the list's allocation.
+      const int32_t* rec = chunks + (size_t)(jc < max_chunks ? jc : max_chunks - 1) * kChunkInts;
+      e = rec[0];
+      p0 = rec[1];
+      rows = rec[2];
+      if (jc >= nch) break;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) xrow[j] = x + (int64_t)rec[4 + 4 * wave + 2 * j + (lane >> 5)] * hidden;
+    }
     const int es = slot_table ? slot_table[e] : e;  // where expert e's matrices sit in the pools
     const uint8_t* wrow =
         (wave >= KS ? w_up + es * stride_up : w_gate + es * stride_gate) + (size_t)rt * nkt * kTileBytes;
-    const uint16_t* xrow[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) xrow[j] = x + (int64_t)rec[4 + 4 * wave + 2 * j + (lane >> 5)] * hidden;
     f32x16 acc_a = {}, acc_b = {};
     expert_rounds<KS>(wrow, nkt, hidden, slot, xrow, wave, lane, lds, acc_a, acc_b);
     float* red = reinterpret_cast<float*>(lds);
@@ -613,25 +779,14 @@ size_t moe_workspace_bytes(int64_t tokens, int64_t experts, int64_t top_k, int64
   return total;
 }
 
-hipError_t launch_moe_routing(const MoeLaunch& a, hipStream_t s) {
-  if (a.tokens == 0) return hipSuccess;
-  MoeWs w = carve(a.ws, a.tokens, a.experts, a.top_k, a.hidden, a.inter, nullptr);
-  const int64_t flat = a.tokens * a.top_k;
-  hipError_t err = hipSuccess;
-#define NVFP4_R(NPL)                                                                                        \
-  hipLaunchKernelGGL(route_kernel<NPL>, dim3((unsigned)a.tokens), dim3(64), 0, s, a.logits, a.tokens, (int)a.experts, \
-                     (int)a.top_k, a.ids, a.g)
-  if (a.experts <= 512) NVFP4_R(8);
-  else if (a.experts <= 1024) NVFP4_R(16);
-  else NVFP4_R(32);
-#undef NVFP4_R
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(1024), 0, s, a.ids, (int)flat, (int)a.experts, (int)a.top_k,
-                     a.counts, a.offsets, a.perm, w.pos, w.chunks, w.n_chunks);
-  return hipGetLastError();
+namespace {
+// Whether the gate/up workgroups group the batch themselves.
+bool local_grouping(const MoeLaunch& a) {
+  return a.slot_table == nullptr && a.tokens * a.top_k <= kLocalFlat && a.experts <= kLocalExperts;
 }
 
-hipError_t launch_moe_experts(const MoeLaunch& a, hipStream_t s) {
+// Expert GEMMs and scatter; with `local`, gate/up also groups the routed rows.
+hipError_t launch_experts(const MoeLaunch& a, bool local, hipStream_t s) {
   if (a.tokens == 0) return hipSuccess;
   MoeWs w = carve(a.ws, a.tokens, a.experts, a.top_k, a.hidden, a.inter, nullptr);
   const int64_t flat = a.tokens * a.top_k;
@@ -643,10 +798,16 @@ hipError_t launch_moe_experts(const MoeLaunch& a, hipStream_t s) {
   const int64_t resident = 2 * (int64_t)cu_count();
   const int64_t nrt_i = (a.inter + 63) / 64;
   const int64_t gu_items = mch * nrt_i;
-  hipLaunchKernelGGL(gate_up_kernel, dim3((unsigned)(gu_items < resident ? gu_items : resident)),
-                     dim3(64 * kExpertWaves), 0, s, a.x, w.chunks, w.n_chunks, (int)mch, (int)a.hidden, (int)a.inter,
-                     a.w_gate, a.w_up, a.stride_gate, a.stride_up, a.slot_table, a.scale_gate, a.scale_up, w.h,
-                     a.dbg_gate, a.dbg_up);
+  const dim3 gu_grid((unsigned)(gu_items < resident ? gu_items : resident));
+  const LocalArgs la{a.ids, (int)flat, (int)a.experts, (int)a.top_k, a.counts, a.offsets, a.perm, w.pos};
+  if (local)
+    hipLaunchKernelGGL(gate_up_kernel<true>, gu_grid, dim3(64 * kExpertWaves), 0, s, a.x, w.chunks, w.n_chunks,
+                       (int)mch, (int)a.hidden, (int)a.inter, a.w_gate, a.w_up, a.stride_gate, a.stride_up,
+                       a.slot_table, a.scale_gate, a.scale_up, w.h, a.dbg_gate, a.dbg_up, la);
+  else
+    hipLaunchKernelGGL(gate_up_kernel<false>, gu_grid, dim3(64 * kExpertWaves), 0, s, a.x, w.chunks, w.n_chunks,
+                       (int)mch, (int)a.hidden, (int)a.inter, a.w_gate, a.w_up, a.stride_gate, a.stride_up,
+                       a.slot_table, a.scale_gate, a.scale_up, w.h, a.dbg_gate, a.dbg_up, la);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const int64_t grp_h = ((a.hidden + 63) / 64 + 3) / 4;
   const int64_t dn_items = mch * grp_h;
@@ -665,9 +826,39 @@ hipError_t launch_moe_experts(const MoeLaunch& a, hipStream_t s) {
   return err;
 }
 
+hipError_t launch_route(const MoeLaunch& a, hipStream_t s) {
+#define NVFP4_R(NPL)                                                                                        \
+  hipLaunchKernelGGL(route_kernel<NPL>, dim3((unsigned)a.tokens), dim3(64), 0, s, a.logits, a.tokens, (int)a.experts, \
+                     (int)a.top_k, a.ids, a.g)
+  if (a.experts <= 512) NVFP4_R(8);
+  else if (a.experts <= 1024) NVFP4_R(16);
+  else NVFP4_R(32);
+#undef NVFP4_R
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_moe_routing(const MoeLaunch& a, hipStream_t s) {
+  if (a.tokens == 0) return hipSuccess;
+  MoeWs w = carve(a.ws, a.tokens, a.experts, a.top_k, a.hidden, a.inter, nullptr);
+  const int64_t flat = a.tokens * a.top_k;
+  hipError_t err = launch_route(a, s);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(1024), 0, s, a.ids, (int)flat, (int)a.experts, (int)a.top_k,
+                     a.counts, a.offsets, a.perm, w.pos, w.chunks, w.n_chunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_experts(const MoeLaunch& a, hipStream_t s) { return launch_experts(a, false, s); }
+
 hipError_t launch_moe(const MoeLaunch& a, hipStream_t s) {
+  if (a.tokens == 0) return hipSuccess;
+  if (local_grouping(a)) {
+    const hipError_t err = launch_route(a, s);
+    return err != hipSuccess ? err : launch_experts(a, true, s);
+  }
   const hipError_t err = launch_moe_routing(a, s);
-  return err != hipSuccess ? err : launch_moe_experts(a, s);
+  return err != hipSuccess ? err : launch_experts(a, false, s);
 }
 
 }  // namespace nvfp4

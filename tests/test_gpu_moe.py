@@ -24,8 +24,10 @@ def small_weights(seed, e, hidden, inter):
     (7, 6, 3, 272, 48),      # ragged against the 256-k and 64-row tiles
     (40, 12, 4, 512, 96),    # an expert can receive more than 32 rows
     (3, 64, 1, 128, 32),
-    (130, 16, 8, 128, 32),   # tokens * top_k > 1024: separate routing and grouping launches
-    (4, 1100, 2, 128, 32),   # more than 1024 experts: separate launches, 32 logits per lane
+    (128, 16, 8, 128, 32),   # tokens * top_k == 1024: still grouped inside the gate/up workgroups
+    (130, 16, 8, 128, 32),   # tokens * top_k > 1024: the grouping launch
+    (4, 1024, 3, 128, 32),   # 1024 experts: grouped inside the gate/up workgroups, 16 logits per lane
+    (4, 1100, 2, 128, 32),   # more than 1024 experts: the grouping launch, 32 logits per lane
     (1536, 6, 4, 1024, 384),  # more work-list items than the persistent expert-GEMM grids hold
     (3, 2048, 64, 128, 32),   # the largest expert count and top-k the layer takes
     (1, 1, 1, 16, 16),        # one token, one expert, the smallest hidden and inter
