@@ -7,7 +7,8 @@ synthetic workload:
               down 17408->5120, QKV 5120->7168, O 5120->5120), fp32 outputs
   decode_b32  the same layer's weights at 32 decode tokens: five skinny GEMMs, bf16 outputs
   moe         32 tokens through a 512-expert, top-10 MoE layer (hidden 2048, expert
-              width 512): route, group, gate/up + SwiGLU, down, scatter
+              width 512): route; gate/up + SwiGLU, each workgroup grouping the
+              routed rows first; down; scatter
   prefill     a 512-token prompt through gate, up (5120->17408) and down (17408->5120)
   gemv_1k     one 1024 x 1024 GEMV at batch 1 (latency-bound: reported in us and GB/s)
 The headline `value` is the batch-1 layer's weight-stream rate in GB/s

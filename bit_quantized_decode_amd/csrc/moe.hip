@@ -544,8 +544,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
     float* red = reinterpret_cast<float*>(lds);
     store_partials(red, wave, lane, acc_a, acc_b);
     __syncthreads();
-    // Thread t: accumulator elements i0 + 8 q (i0 = t / 64) of lane t % 64, gate and up.
-    const int l = threadIdx.x & 63, i0 = threadIdx.x >> 6;
+    // Thread t: accumulator elements i0 + 8 q (i0 = t / 64) of lane t % 64,
+    // gate and up.  (t is opaque here, so that the addresses derived from it
+    // are formed per item instead of being kept, spilled, across the rounds.)
+    int t = (int)threadIdx.x;
+    asm volatile("" : "+v"(t));
+    const int l = t & 63, i0 = t >> 6;
     const int slots = nkt < KS ? nkt : KS;
     const float sg = scale_gate[e], su = scale_up[e];
     const int tok = l & 31;
