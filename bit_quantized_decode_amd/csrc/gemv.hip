@@ -92,7 +92,7 @@ struct GemvBatch {
 
 __global__ __launch_bounds__(256) void gemv_kernel(const GemvBatch b, unsigned* __restrict__ counters,
                                                    float* __restrict__ partial_all) {
-  __shared__ u32x4 xs[kGemvWaves * kTileK / 8];  // 4 k tiles of x as bf16 pairs, zero past K
+  __shared__ u32x4 xs[2 * kGemvWaves * kTileK / 8];  // 4 k tiles of x as bf16 pairs, zero past K (+ an unread half)
   __shared__ float red[kGemvWaves][64];
   int p = 0;
   while (p + 1 < b.count && (int)blockIdx.x >= b.wg_begin[p + 1]) ++p;
@@ -108,21 +108,26 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvBatch b, unsigned* 
   const int kt = grp * kGemvWaves + wave;
   const bool has_tile = kt < nkt;
 
-  // This wavefront's tile: all ten loads issued before anything waits.
-  u32x4 q[8], sa = {0u, 0u, 0u, 0u}, sb = {0u, 0u, 0u, 0u};
-  if (has_tile) {
-    const uint8_t* t = packed + ((size_t)rt * nkt + kt) * kTileBytes;
+  // The workgroup's 1024 activations (128 x 16 bytes) load first, so that
+  // they reach the LDS (and the barrier) while the weights are still on the
+  // way, and each chunk's arithmetic starts as its weights land.  Every
+  // thread loads and stores (the last 128 repeat the first 128's loads into
+  // an unread half of the buffer), and wavefronts past the last k tile load
+  // that tile and drop it: no load or store sits under a branch, so the load
+  // stays first and every wait counts exactly the loads it needs.
+  const int64_t kk = (int64_t)grp * kGemvWaves * kTileK + 8 * (int64_t)(threadIdx.x & 127);
+  const u32x4 xv = x16[(kk < k ? kk : 0) >> 3];
+  u32x4 q[8], sa, sb;
+  {
+    const uint8_t* t = packed + ((size_t)rt * nkt + (has_tile ? kt : nkt - 1)) * kTileBytes;
     sa = load16_stream(t + kScaleOffset + 32 * (lane & 31));
     sb = load16_stream(t + kScaleOffset + 32 * (lane & 31) + 16);
 #pragma unroll
     for (int c = 0; c < 8; ++c) q[c] = load16_stream(t + c * 1024 + lane * 16);
   }
-  // Stage the workgroup's 1024 activations (128 x 16 bytes).
-  if (threadIdx.x < kGemvWaves * kTileK / 8) {
-    const int64_t kk = (int64_t)grp * kGemvWaves * kTileK + 8 * (int64_t)threadIdx.x;
-    xs[threadIdx.x] = kk < k ? x16[kk >> 3] : u32x4{0u, 0u, 0u, 0u};
-  }
-  __syncthreads();
+  xs[threadIdx.x] = kk < k ? xv : u32x4{0u, 0u, 0u, 0u};
+  wait_vmcnt_lgkm0<63>();  // this thread's LDS store is done (the weight loads are not waited for)
+  barrier_only();
 
   float acc_a = 0.0f, acc_b = 0.0f;
   if (has_tile) {
