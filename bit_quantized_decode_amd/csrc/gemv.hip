@@ -187,7 +187,7 @@ struct GemvRowsBatch {
 };
 
 template <int C, int M>
-__device__ __forceinline__ void chunk_rows(u32x4 q, const u32x4 (&xs)[M][kGemvWaves * kTileK / 8], int xi, u32x4 sa,
+__device__ __forceinline__ void chunk_rows(u32x4 q, const u32x4 (&xs)[2][kGemvWaves * kTileK / 8], int xi, u32x4 sa,
                                            u32x4 sb, float (&acc_a)[M], float (&acc_b)[M]) {
   bf16x2 w[4][4];
 #pragma unroll
@@ -218,7 +218,8 @@ __device__ __forceinline__ void chunk_rows(u32x4 q, const u32x4 (&xs)[M][kGemvWa
 template <int M>
 __global__ __launch_bounds__(256) void gemv_rows_kernel(const GemvRowsBatch b, unsigned* __restrict__ counters,
                                                         float* __restrict__ partial_all) {
-  __shared__ u32x4 xs[M][kGemvWaves * kTileK / 8];  // M rows' 4 k tiles of x, zero past K
+  // M rows' 4 k tiles of x, zero past K (and, for M = 1, an unread half)
+  __shared__ u32x4 xs[2][kGemvWaves * kTileK / 8];
   __shared__ float red[M][kGemvWaves][64];
   int p = 0;
   while (p + 1 < b.count && (int)blockIdx.x >= b.wg_begin[p + 1]) ++p;
@@ -234,20 +235,22 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(const GemvRowsBatch b, u
   const int kt = grp * kGemvWaves + wave;
   const bool has_tile = kt < nkt;
 
-  u32x4 q[8], sa = {0u, 0u, 0u, 0u}, sb = {0u, 0u, 0u, 0u};
-  if (has_tile) {
-    const uint8_t* t = packed + ((size_t)rt * nkt + kt) * kTileBytes;
+  // As in gemv_kernel: the activations load first and no load or store sits
+  // under a branch.  Thread t loads chunk t % 128 of row (t / 128) % M.
+  const int xr = M == 1 ? 0 : (int)(threadIdx.x >> 7), xc = (int)threadIdx.x & 127;
+  const int64_t kk = (int64_t)grp * kGemvWaves * kTileK + 8 * (int64_t)xc;
+  const u32x4 xv = *reinterpret_cast<const u32x4*>(x + xr * ldx + (kk < k ? kk : 0));
+  u32x4 q[8], sa, sb;
+  {
+    const uint8_t* t = packed + ((size_t)rt * nkt + (has_tile ? kt : nkt - 1)) * kTileBytes;
     sa = load16_stream(t + kScaleOffset + 32 * (lane & 31));
     sb = load16_stream(t + kScaleOffset + 32 * (lane & 31) + 16);
 #pragma unroll
     for (int c = 0; c < 8; ++c) q[c] = load16_stream(t + c * 1024 + lane * 16);
   }
-  for (int i = threadIdx.x; i < M * (kGemvWaves * kTileK / 8); i += 256) {
-    const int r = i / (kGemvWaves * kTileK / 8), c = i % (kGemvWaves * kTileK / 8);
-    const int64_t kk = (int64_t)grp * kGemvWaves * kTileK + 8 * (int64_t)c;
-    xs[r][c] = kk < k ? *reinterpret_cast<const u32x4*>(x + r * ldx + kk) : u32x4{0u, 0u, 0u, 0u};
-  }
-  __syncthreads();
+  xs[threadIdx.x >> 7][xc] = kk < k ? xv : u32x4{0u, 0u, 0u, 0u};
+  wait_vmcnt_lgkm0<63>();  // this thread's LDS store is done (the weight loads are not waited for)
+  barrier_only();
 
   float acc_a[M], acc_b[M];
 #pragma unroll
