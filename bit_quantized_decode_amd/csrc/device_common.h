@@ -150,19 +150,20 @@ __device__ __forceinline__ float load_coherent(const float* p) {
 }
 
 // sum_{i < count} p[i * stride], added in index order.  The loads are issued
-// in batches of eight so that their memory latencies overlap; padding lanes of
-// a batch re-read the last element and are not added.
+// in batches of sixteen so that their memory latencies overlap (one round trip
+// for up to 16 parts); padding lanes of a batch re-read the last element and
+// are not added.
 __device__ __forceinline__ float sum_coherent(const float* p, size_t stride, int count) {
   float s = 0.0f;
-  for (int i = 0; i < count; i += 8) {
-    float v[8];
+  for (int i = 0; i < count; i += 16) {
+    float v[16];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 16; ++j) {
       const int idx = i + j < count ? i + j : count - 1;
       v[j] = load_coherent(p + (size_t)idx * stride);
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) s = (i + j < count) ? s + v[j] : s;
+    for (int j = 0; j < 16; ++j) s = (i + j < count) ? s + v[j] : s;
   }
   return s;
 }
