@@ -140,9 +140,17 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lt, int ex
     s_val[lane] = ex;
   }
   __builtin_amdgcn_wave_barrier();
+  // Lane 0 adds them in order, sixteen LDS reads per round issued together.
   float sum = 0.0f;
   if (lane == 0)
-    for (int j = 0; j < top_k; ++j) sum += s_val[j];
+    for (int j0 = 0; j0 < top_k; j0 += 16) {
+      float v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = s_val[j0 + u < top_k ? j0 + u : top_k - 1];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (j0 + u < top_k) sum += v[u];
+    }
   sum = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(sum), 0));
   if (lane < top_k) {
     ids_out[lane] = win_id;
@@ -377,7 +385,13 @@ __device__ void group_local(const int32_t* __restrict__ ids, int flat, int exper
   for (int f = tid; f < flat; f += 512) {
     const int e = s_ids[f], b = lg.off[e], n = s_cnt[e];
     int r = 0;
-    for (int q = 0; q < n; ++q) r += s_unord[b + q] < f ? 1 : 0;
+    for (int q0 = 0; q0 < n; q0 += 8) {  // eight LDS reads per round, issued together
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = s_unord[b + (q0 + u < n ? q0 + u : n - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) r += (q0 + u < n && v[u] < f) ? 1 : 0;
+    }
     lg.perm[b + r] = f;
   }
   for (int e = tid; e < experts; e += 512)
@@ -558,9 +572,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
       for (int q = 0; q < 4; ++q) {
         const int i = i0 + 8 * q;
         float g = 0.0f, u = 0.0f;
-        for (int sl = 0; sl < slots; ++sl) {
-          g += red[(32 * sl + i) * 64 + l];
-          u += red[(32 * (KS + sl) + i) * 64 + l];
+#pragma unroll
+        for (int sl = 0; sl < KS; ++sl) {  // all slots' reads issued together (clamped), added in slot order
+          const int sc = sl < slots ? sl : slots - 1;
+          const float gs = red[(32 * sc + i) * 64 + l], us = red[(32 * (KS + sc) + i) * 64 + l];
+          if (sl < slots) {
+            g += gs;
+            u += us;
+          }
         }
         const int row = rt * 64 + acc_row(i >> 4, i & 15, l);
         if (row < inter) {
@@ -629,7 +648,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void d
           for (int c = 0; c < 4; ++c) {
             const int i = 16 * hh + 4 * e4 + c;
             float acc = 0.0f;
-            for (int sl = 0; sl < slots; ++sl) acc += red[(32 * (wave + sl) + i) * 64 + lane];
+#pragma unroll
+            for (int sl = 0; sl < KS; ++sl) {  // reads issued together (clamped), added in slot order
+              const float v = red[(32 * (wave + (sl < slots ? sl : slots - 1)) + i) * 64 + lane];
+              if (sl < slots) acc += v;
+            }
             v[c] = acc * sd;
           }
           const int row = rt * 64 + acc_row(hh, 4 * e4, lane);
@@ -653,10 +676,26 @@ __global__ __launch_bounds__(256) void scatter_kernel(const float* __restrict__ 
   if (i >= tokens * hidden) return;
   const int64_t t = i / hidden;
   const int o = (int)(i % hidden);
+  // Sixteen selections per round: their positions and weights load together,
+  // then their d values together, so a round costs two memory round trips
+  // whatever top_k is (a plain loop waits twice per selection).  The sum is
+  // still taken in j order; padding entries re-read the last selection and
+  // are not added.
   float acc = 0.0f;
-  for (int j = 0; j < top_k; ++j) {
-    const int64_t f = t * top_k + j;
-    acc = fmaf(g[f], d[(int64_t)pos[f] * hidden + o], acc);
+  for (int j0 = 0; j0 < top_k; j0 += 16) {
+    int pj[16];
+    float gj[16], dj[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int64_t f = t * top_k + (j0 + u < top_k ? j0 + u : top_k - 1);
+      pj[u] = pos[f];
+      gj[u] = g[f];
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) dj[u] = d[(int64_t)pj[u] * hidden + o];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (j0 + u < top_k) acc = fmaf(gj[u], dj[u], acc);
   }
   if (y_bf16) static_cast<uint16_t*>(y)[i] = to_bf16(acc);
   else static_cast<float*>(y)[i] = acc;
