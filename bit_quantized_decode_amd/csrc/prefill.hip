@@ -355,15 +355,19 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillBatch b, u
       const int last = ie - 1;
       auto clampi = [&](int it) __attribute__((always_inline)) { return it < last ? it : last; };
       MxA w0, w1, w2, w3;
+      // Prologue in the steady state's issue order: the first iteration waits
+      // only for its own operands, not for the whole pipeline fill.
       load_a(ib, w0);
-      load_a(clampi(ib + 1), w1);
-      load_a(clampi(ib + 2), w2);
-      load_a(clampi(ib + 3), w3);
       dma_mx(ib, NVFP4_XBUF(0));
+      load_a(clampi(ib + 1), w1);
       dma_mx(clampi(ib + 1), NVFP4_XBUF(1));
+      load_a(clampi(ib + 2), w2);
       dma_mx(clampi(ib + 2), NVFP4_XBUF(2));
-      wait_vmcnt<0>();
+      load_a(clampi(ib + 3), w3);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<kVmAfter>();
       barrier_only();
+      __builtin_amdgcn_sched_barrier(0);
 #define NVFP4_MX_STEP(S, WC)                                                                                  \
   {                                                                                                           \
     const int it = i + (S);                                                                                   \
@@ -470,18 +474,24 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillBatch b, u
       const int last = ie - 1;
       auto clampi = [&](int it) __attribute__((always_inline)) { return it < last ? it : last; };
       WStage w0, w1, w2, w3;
+      // Prologue in the steady state's issue order (weights of it, then its
+      // activations), so that the first iteration waits only for its own
+      // operands -- after them 4 + JT + 4 + JT + 4 memory instructions are
+      // issued, as before every later iteration -- instead of the whole
+      // pipeline fill.  Each later step clears the tail of the activations it
+      // waits for (zero_tail), so only the first buffer's is cleared here.
       load_w(ib, w0);
-      load_w(clampi(ib + 1), w1);
-      load_w(clampi(ib + 2), w2);
-      load_w(clampi(ib + 3), w3);
       dma_x(ib, NVFP4_XBUF(0));
+      load_w(clampi(ib + 1), w1);
       dma_x(clampi(ib + 1), NVFP4_XBUF(1));
+      load_w(clampi(ib + 2), w2);
       dma_x(clampi(ib + 2), NVFP4_XBUF(2));
-      wait_vmcnt<0>();
+      load_w(clampi(ib + 3), w3);
+      __builtin_amdgcn_sched_barrier(0);  // no operand work is hoisted above the wait (it would wait for every load)
+      wait_vmcnt<kVmAfterX>();
       zero_tail(ib, NVFP4_XBUF(0));
-      zero_tail(clampi(ib + 1), NVFP4_XBUF(1));
-      zero_tail(clampi(ib + 2), NVFP4_XBUF(2));
       barrier_only();
+      __builtin_amdgcn_sched_barrier(0);
       AOps ac, an;
       bf16x8 bc[JT], bn[JT];
       load_b<0, JT>(NVFP4_XBUF(0), lane, bc);
