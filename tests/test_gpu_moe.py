@@ -29,6 +29,7 @@ def small_weights(seed, e, hidden, inter):
     (4, 1024, 3, 128, 32),   # 1024 experts: grouped inside the gate/up workgroups, 16 logits per lane
     (4, 1100, 2, 128, 32),   # more than 1024 experts: the grouping launch, 32 logits per lane
     (1536, 6, 4, 1024, 384),  # more work-list items than the persistent expert-GEMM grids hold
+    (9, 10, 3, 1296, 608),    # several k rounds in both expert GEMMs, slots left without a tile in the last
     (3, 2048, 64, 128, 32),   # the largest expert count and top-k the layer takes
     (1, 1, 1, 16, 16),        # one token, one expert, the smallest hidden and inter
     (2, 3, 3, 48, 16),        # top_k == experts: every token reaches every expert
